@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated INT8 linear layer on one MI355X.
+
+One step = one int8_linear call over the whole input (rotate+quantize kernel,
+then the INT8 MFMA GEMM with the fused dequantizing epilogue), inputs already
+resident in HBM.  The reported value is 2*M*N*K / step time in TOP/s (INT8
+ops; the rotation and quantization are inside the timed step).
+
+Prints ONE JSON line.  Besides the headline it carries:
+  roofline      the GEMM kernel (dominant) against the dense INT8 MFMA peak,
+                its duration measured with HIP events on the launch stream;
+  kernels       both kernels' average durations, TOP/s or GB/s and fractions;
+  cpu_baseline  the plain C oracle timed on the host cores over a bounded
+                sample of the same workload (the leading rows), and the GPU
+                output of those rows compared with it.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload 3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published (8 TB/s)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "quantized_diffusion_amd", "csrc", "gemm_i8.hip")
+# The pages' single-call figure for M32700/K5376/N16128 on an RTX 5090 D v2
+# (SGLang PR "Tune Kitchen INT8 row splitting for SM120", Benchmark table):
+# 10.5752 ms.  Context only, another machine.
+PAGE_MS = {3: 10.5752, 2: 2.7743}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(workload_name: str):
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_hash") != kernel_hash(GEMM_SRC) or d.get("workload") != workload_name:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, n, torch):
+    """Average duration (ms) of fn() measured with events around each launch on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / n
+
+
+def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float):
+    """Time the oracle on the leading rows of the same workload; check those rows."""
+    import numpy as np
+
+    import oracle
+    O = oracle.default()
+    wq = wq_dev.cpu().numpy()
+    sw = sw_dev.cpu().numpy()
+
+    def run(rows):
+        x = x_dev[:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        y = O.linear(x, wq, sw, b_bits)
+        return time.perf_counter() - t0, y
+
+    t_small, _ = run(16)
+    rows = int(min(w.M, max(16, 16 * budget_s / max(t_small, 1e-3))))
+    rows = min(rows, 8192)
+    t, y_or = run(rows)
+    y_gpu = y_dev[:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    same = y_gpu == y_or
+    g = (y_gpu.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = (y_or.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    exp = ((y_or >> 7) & 0xFF).astype(np.int64)
+    ulp = np.ldexp(1.0, np.where(exp == 0, -126, exp - 127) - 7)
+    within = bool(np.all(np.abs(g - r) <= ulp))
+    ops = 2.0 * rows * w.N * w.K
+    return {
+        "value": round(ops / t / 1e12, 6),
+        "unit": "TOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": f"leading {rows} of {w.M} rows, full N={w.N}, K={w.K} (rotate+quantize, exact INT32 GEMM, epilogue)",
+        "seconds": round(t, 3),
+        "sample_parity": {"rows": rows, "outputs": int(y_or.size), "not_bit_identical": int((~same).sum()),
+                          "within_1_bf16_ulp": within},
+    }
+
+
+def calibrate_copy(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (synth.WORKLOADS)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a device copy of BYTES bytes (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path: the layer shards over rows or output channels without communication, "
+              "so each GPU runs this same single-GPU step on its share.", flush=True)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    import numpy as np
+    import torch
+
+    import quantized_diffusion_amd as qd
+    from synth import iter_w, iter_x, make_bias, workload
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    qd.lib()
+    w = workload(args.workload)
+    if w.kind != "w8a8":
+        sys.exit(f"workload {w.cid} is {w.kind}; bench.py measures the INT8 linear")
+    M, K, N = w.M, w.K, w.N
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.name}: generating inputs")
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for r0, r1, bits in iter_x(w):
+        x[r0:r1].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    Wf = torch.empty((N, K), dtype=torch.float32, device=dev)
+    for r0, r1, chunk in iter_w(w):
+        Wf[r0:r1].copy_(torch.from_numpy(chunk))
+    b_bits = make_bias(w)
+    bias = torch.from_numpy(b_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, sw = qd.prepare_weights(Wf)          # offline weight preparation (not timed)
+    del Wf
+    ws = torch.empty(qd.workspace_size(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        qd.int8_linear(x, wq, sw, bias, 256, ws, y)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    ops = 2.0 * M * N * K
+    tops = ops / (ms * 1e-3) / 1e12
+
+    # per-kernel durations (same kernels, launched through their own entry points)
+    aq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = torch.empty(M, dtype=torch.float32, device=dev)
+    y2 = torch.empty_like(y)
+    reps = max(5, args.steps)
+    ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
+    ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+    same = bool(torch.equal(y2, y))
+    q_bytes = 3.0 * M * K + 4.0 * M
+    g_min_bytes = float(M * K + N * K + 2 * M * N + 4 * M + 4 * N + 2 * N)
+    gemm_tops = ops / (ms_g * 1e-3) / 1e12
+    traffic = load_traffic(w.name)
+    out = {
+        "metric": f"INT8 linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}",
+        "value": round(tops, 3),
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tops / (ops / (PAGE_MS[w.cid] * 1e-3) / 1e12), 4) if w.cid in PAGE_MS else None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "rotation": "block-256 Walsh-Hadamard",
+                   "activations": "bf16", "weights": "int8 per-channel fp32 scale", "bias": "bf16",
+                   "output": "bf16", "parallelism": "single GPU"},
+        "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_i8_kernel (fused bf16 epilogue)",
+                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic},
+        "kernels": {
+            "rotquant": {"ms": round(ms_q, 5), "algorithmic_bytes": q_bytes,
+                         "GB_per_s": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
+                         "frac_of_hbm": round(q_bytes / (ms_q * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "gemm": {"ms": round(ms_g, 5), "TOP_per_s": round(gemm_tops, 2),
+                     "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
+                     "min_hbm_bytes": g_min_bytes},
+            "separate_launch_output_identical": same,
+        },
+        "device": torch.cuda.get_device_name(0),
+        "wall_s_timed_region": round(t_wall, 4),
+        "context": "pages' figure for this workload: 10.5752 ms single call on an RTX 5090 D v2 (another machine)"
+        if w.cid == 3 else None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle on host cores)")
+        out["cpu_baseline"] = cpu_baseline(x, y, wq, sw, b_bits, w, torch, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

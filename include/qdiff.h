@@ -1,0 +1,188 @@
+/*
+ * qdiff.h -- C ABI of the MI355X (gfx950) rotated INT8 linear-layer library.
+ *
+ * The library computes the W8A8 "ConvRot" linear layer that the pages
+ * describe: BF16 activations are rotated along K by a 256-wide block
+ * Walsh-Hadamard transform, quantized per row to signed INT8 with an FP32 row
+ * scale, multiplied against pre-quantized INT8 weights (per-output-channel
+ * FP32 scales) with exact INT32 accumulation on the matrix cores, and the
+ * result is rescaled, biased and written as BF16 in the GEMM's epilogue.
+ *
+ * Passages (page title, section):
+ *  - comfy-kitchen 0.2.40 (PyPI), "Huawei Ascend backend": the operations
+ *    quantize_int8_rowwise, quantize_and_rotate_rowwise, int8_linear,
+ *    dequantize_int8_simple / _simple_dtype, convrot_w4a4_linear.
+ *  - comfy-kitchen 0.2.40, "HIP backend": a K that is not a multiple of 16 is
+ *    outside the kernels' domain.
+ *  - SGLang PR "Tune Kitchen INT8 row splitting for SM120", "Accuracy Test":
+ *    BF16 activations and bias, INT8 weights, FP32 row scales, ConvRot256.
+ *  - ComfyUI-AppleSilicon-FP8 README, "What it fixes" row 17: rotate the
+ *    activation online, quantize per row, INT8 x INT8 -> INT32, per-row
+ *    rescale and bias fused into the store epilogue.
+ *
+ * Arithmetic (identical, bit for bit, to the definitions below):
+ *  - rotation R: for each aligned 256-element block of a row, the
+ *    Sylvester-ordered Walsh-Hadamard transform H[i][j] = (-1)^popcount(i&j)
+ *    divided by 16, evaluated in FP32 as the in-place butterfly whose pair
+ *    distance runs 1, 2, 4, ..., 128 (pair (j, j+h) -> (a+c, a-c)), followed
+ *    by the multiply by 1/16.
+ *  - row scale s = amax / qmax (one correctly rounded FP32 division), with
+ *    amax = max |v| over the row and qmax = 127 (INT8) or 7 (INT4).
+ *  - code = clamp(rne(fl(v / s)), -qmax, qmax); a row with s == 0 has all
+ *    codes 0.
+ *  - acc = sum_k a[m,k] * w[n,k] exactly in INT32.
+ *  - y = bf16_rne(((float)acc * sx[m]) * sw[n] + (float)bias[n]), in FP32,
+ *    left to right, no fused multiply-add.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller.  Matrices are
+ *    row-major with a leading dimension (row stride) given in ELEMENTS.
+ *  - Work is enqueued on `stream` (0 = the null stream).  No entry point
+ *    allocates, frees or synchronises; results are ready when the stream
+ *    reaches them.
+ *  - Every argument is validated on the host before any HIP call.  On a
+ *    non-QD_OK status nothing was enqueued (except QD_EHIP, which reports a
+ *    failed launch), outputs are unspecified and qd_last_error() describes the
+ *    problem.  Inputs are never modified.
+ *  - An empty problem (M == 0, or N == 0 for the GEMMs) is valid and enqueues
+ *    nothing.  K must be positive.
+ *  - Calls on different streams may run concurrently as long as their output
+ *    buffers (and workspaces) do not overlap.
+ */
+#ifndef QDIFF_H
+#define QDIFF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QD_OK = 0,
+    QD_EINVAL = 1,        /* null pointer, negative size, ld too small, workspace too small */
+    QD_EUNSUPPORTED = 2,  /* outside the kernels' domain: K % 16, K % 256 with rotation,
+                             K beyond the limit, misaligned pointer or leading dimension,
+                             unknown dtype or block */
+    QD_EHIP = 3           /* the HIP runtime reported an error at launch */
+} qd_status_t;
+
+typedef enum { QD_F32 = 0, QD_BF16 = 1, QD_F16 = 2 } qd_dtype_t;
+
+/* Largest K accepted by the quantizers (a row stays in registers). */
+#define QD_MAX_K_QUANT 65536
+/* Largest K accepted by the GEMMs (keeps K * 128 * 128 < 2^31). */
+#define QD_MAX_K_GEMM 131072
+
+/* Message for the last non-OK status returned on the calling thread
+ * (empty string if none).  The pointer stays valid until the next call. */
+const char* qd_last_error(void);
+
+/* Library version string. */
+const char* qd_version(void);
+
+/*
+ * quantize_and_rotate_rowwise (comfy-kitchen, "Huawei Ascend backend").
+ *   x          [M, K] in x_dtype (F32, BF16 or F16), row stride ldx elements.
+ *   block      rotation width; must be 256.
+ *   q          [M, K] INT8 codes in [-127, 127], row stride ldq bytes.
+ *   row_scale  [M] FP32 scales s = amax/127 of the rotated rows.
+ * Requires K % 256 == 0, K <= QD_MAX_K_QUANT, x and q 16-byte aligned,
+ * ldx * sizeof(x_dtype) and ldq multiples of 16.
+ * Applied to FP32 weights [N, K] this is the offline weight preparation: the
+ * rotated INT8 weights and their per-output-channel scales.
+ */
+qd_status_t qd_quantize_and_rotate_rowwise(const void* x, qd_dtype_t x_dtype, int64_t M,
+                                           int64_t K, int64_t ldx, int32_t block, int8_t* q,
+                                           int64_t ldq, float* row_scale, hipStream_t stream);
+
+/*
+ * Same as qd_quantize_and_rotate_rowwise with signed INT4 codes in [-7, 7]
+ * held one per byte (INT8 storage) and s = amax/7: the activation side of
+ * convrot_w4a4_linear (comfy-kitchen, "Huawei Ascend backend").
+ */
+qd_status_t qd_quantize_and_rotate_rowwise_int4(const void* x, qd_dtype_t x_dtype, int64_t M,
+                                                int64_t K, int64_t ldx, int32_t block,
+                                                int8_t* q, int64_t ldq, float* row_scale,
+                                                hipStream_t stream);
+
+/*
+ * quantize_int8_rowwise (comfy-kitchen, "Huawei Ascend backend"): per-row
+ * dynamic symmetric INT8 quantization without rotation.  Same layout rules
+ * as above except K % 16 == 0 suffices.
+ */
+qd_status_t qd_quantize_int8_rowwise(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                     int64_t ldx, int8_t* q, int64_t ldq, float* row_scale,
+                                     hipStream_t stream);
+
+/*
+ * Quantized matmul on already quantized operands (the GEMM half of
+ * int8_linear; the INT32 product never leaves the registers):
+ *   y[m, n] = bf16_rne(((float)sum_k aq[m,k] * wq[n,k]) * a_scale[m] * w_scale[n] + bias[n])
+ *   aq [M, K] INT8 (row stride lda bytes), a_scale [M] FP32,
+ *   wq [N, K] INT8 (row stride ldw bytes), w_scale [N] FP32,
+ *   bias [N] BF16 or NULL, y [M, N] BF16 (row stride ldy elements).
+ * Requires K % 16 == 0, K <= QD_MAX_K_GEMM, aq/wq/y 16-byte aligned,
+ * lda and ldw multiples of 16, ldy a multiple of 8.
+ */
+qd_status_t qd_int8_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                              const float* a_scale, const int8_t* wq, int64_t N, int64_t ldw,
+                              const float* w_scale, const void* bias_bf16, void* y_bf16,
+                              int64_t ldy, hipStream_t stream);
+
+/* Bytes of workspace qd_int8_linear needs for M rows of K: the INT8 codes
+ * (rows padded to 16 bytes) and the FP32 row scales, 256-byte aligned. */
+size_t qd_int8_linear_workspace_size(int64_t M, int64_t K);
+
+/*
+ * int8_linear (comfy-kitchen, "Huawei Ascend backend"; ConvRot form per the
+ * SGLang PR's "Accuracy Test"): y = x W^T + b through the rotated INT8 path.
+ *   x          [M, K] activations in x_dtype (BF16 on the pages), stride ldx.
+ *   wq, w_scale  weights prepared offline with the SAME rotate_block
+ *              (qd_quantize_and_rotate_rowwise on W [N, K]).
+ *   bias       [N] BF16 or NULL.
+ *   rotate_block 256 (ConvRot256) or 0 (no rotation).
+ *   workspace  device buffer of at least qd_int8_linear_workspace_size(M, K)
+ *              bytes, 256-byte aligned; holds the activation codes and row
+ *              scales between the two launches.
+ *   y          [M, N] BF16, stride ldy.
+ * Exactly two kernels are enqueued: the (rotating) quantizer, then the INT8
+ * GEMM with the fused dequantizing epilogue.
+ */
+qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                           int64_t ldx, const int8_t* wq, int64_t N, int64_t ldw,
+                           const float* w_scale, const void* bias_bf16, int32_t rotate_block,
+                           void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
+                           hipStream_t stream);
+
+/*
+ * dequantize_int8_simple / dequantize_int8_simple_dtype (comfy-kitchen,
+ * "Huawei Ascend backend"): out[m, k] = fl(q[m, k] * s), s = scale[m]
+ * (per_row != 0) or scale[0] (per_row == 0); out_dtype F32 or BF16 (the FP32
+ * product rounded to nearest-even).
+ *   q [M, K] INT8 stride ldq bytes; out [M, K] stride ldo elements.
+ * Requires q and out 16-byte aligned, ldq a multiple of 16, ldo*sizeof(out)
+ * a multiple of 16, K % 16 == 0.
+ */
+qd_status_t qd_dequantize_int8(const int8_t* q, int64_t M, int64_t K, int64_t ldq,
+                               const float* scale, int32_t per_row, qd_dtype_t out_dtype,
+                               void* out, int64_t ldo, hipStream_t stream);
+
+/*
+ * The raw INT32 accumulators of the same GEMM kernel (its INT32-store
+ * epilogue), for verifying the exact contraction:
+ *   acc[m, n] = sum_k aq[m, k] * wq[n, k], acc row stride ldc elements.
+ * Requirements as qd_int8_scaled_mm, ldc a multiple of 4.
+ */
+qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                             const int8_t* wq, int64_t N, int64_t ldw, int32_t* acc,
+                             int64_t ldc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QDIFF_H */

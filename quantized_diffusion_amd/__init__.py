@@ -1,0 +1,280 @@
+"""Rotated, dynamically quantized INT8 linear layer for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/qdiff.h`` (``libqdiff.so``,
+built in-tree by ``python -m quantized_diffusion_amd.build``).  PyTorch only
+supplies device memory and the current stream: every step of the layer runs
+in the library's HIP kernels.  There is no fallback: if the library is
+missing, or a tensor is not on the GPU, the call raises.
+
+Operations (names as on the comfy-kitchen 0.2.40 page, "Huawei Ascend
+backend"):
+  quantize_and_rotate_rowwise(x)        -> (int8 codes, fp32 row scales)
+  quantize_int8_rowwise(x)              -> (int8 codes, fp32 row scales)
+  int8_linear(x, wq, w_scale, bias)     -> bf16 y = x W^T + b (rotated W8A8)
+  dequantize_int8(q, scale, dtype)      -> fp32 / bf16
+plus
+  prepare_weights(W)                    -> offline (wq, w_scale) for int8_linear
+  int8_scaled_mm(aq, a_scale, wq, w_scale, bias) -> bf16 (GEMM half of int8_linear)
+  int8_gemm_i32(aq, wq)                 -> raw int32 accumulators
+  quantize_and_rotate_rowwise_int4(x)   -> INT4 codes in int8 storage
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LIB_PATH", "QDiffError", "lib", "quantize_and_rotate_rowwise", "quantize_and_rotate_rowwise_int4",
+    "quantize_int8_rowwise", "int8_linear", "int8_scaled_mm", "int8_gemm_i32", "dequantize_int8",
+    "prepare_weights", "workspace_size", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
+
+QD_OK, QD_EINVAL, QD_EUNSUPPORTED, QD_EHIP = 0, 1, 2, 3
+QD_F32, QD_BF16, QD_F16 = 0, 1, 2
+
+EXPORTED_SYMBOLS = (
+    "qd_last_error", "qd_version", "qd_quantize_and_rotate_rowwise",
+    "qd_quantize_and_rotate_rowwise_int4", "qd_quantize_int8_rowwise", "qd_int8_scaled_mm",
+    "qd_int8_linear_workspace_size", "qd_int8_linear", "qd_dequantize_int8", "qd_int8_gemm_i32",
+)
+
+
+class QDiffError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libqdiff.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} not found: build it with "
+                              "`python -m quantized_diffusion_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        St = ctypes.c_int
+        L.qd_last_error.restype = ctypes.c_char_p
+        L.qd_version.restype = ctypes.c_char_p
+        L.qd_quantize_and_rotate_rowwise.restype = St
+        L.qd_quantize_and_rotate_rowwise.argtypes = [P, St, I64, I64, I64, I32, P, I64, P, P]
+        L.qd_quantize_and_rotate_rowwise_int4.restype = St
+        L.qd_quantize_and_rotate_rowwise_int4.argtypes = [P, St, I64, I64, I64, I32, P, I64, P, P]
+        L.qd_quantize_int8_rowwise.restype = St
+        L.qd_quantize_int8_rowwise.argtypes = [P, St, I64, I64, I64, P, I64, P, P]
+        L.qd_int8_scaled_mm.restype = St
+        L.qd_int8_scaled_mm.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, I64, P]
+        L.qd_int8_linear_workspace_size.restype = SZ
+        L.qd_int8_linear_workspace_size.argtypes = [I64, I64]
+        L.qd_int8_linear.restype = St
+        L.qd_int8_linear.argtypes = [P, St, I64, I64, I64, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
+        L.qd_dequantize_int8.restype = St
+        L.qd_dequantize_int8.argtypes = [P, I64, I64, I64, P, I32, St, P, I64, P]
+        L.qd_int8_gemm_i32.restype = St
+        L.qd_int8_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != QD_OK:
+        raise QDiffError(status, lib().qd_last_error().decode())
+
+
+# --------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: QD_F32, torch.bfloat16: QD_BF16, torch.float16: QD_F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("qdiff: tensors must be on the GPU (no CPU fallback)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("qdiff: tensors are on different devices")
+    return dev
+
+
+def _mat(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return t
+
+
+def _stream(dev):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _rows_vec(t, n, dtype, name):
+    torch = _torch()
+    if t.dtype != dtype or t.dim() != 1 or t.shape[0] < n or (t.numel() > 1 and t.stride(0) != 1):
+        raise ValueError(f"{name} must be a contiguous 1-D {dtype} tensor of length >= {n}")
+    return t
+
+
+# ------------------------------------------------------------------ quantizers
+
+def _quantize(fn, x, block, out_q, out_scale, rotate: bool):
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, out_q, out_scale)
+    M, K = x.shape
+    ldq = (K + 15) // 16 * 16
+    if out_q is None:
+        buf = torch.empty((M, ldq), dtype=torch.int8, device=dev)
+        out_q = buf[:, :K]
+    if out_scale is None:
+        out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _mat(out_q, "q")
+    args = [_ptr(x), _dtype_code(x), M, K, x.stride(0)]
+    if rotate:
+        args.append(block)
+    args += [_ptr(out_q), out_q.stride(0), _ptr(out_scale), _stream(dev)]
+    _check(fn(*args))
+    return out_q, out_scale
+
+
+def quantize_and_rotate_rowwise(x, block: int = 256, out_q=None, out_scale=None):
+    """Rotate each 256-block of the rows of x (FP32/BF16/FP16 [M, K]) by the
+    normalised Walsh-Hadamard transform, then quantize each row to INT8.
+    Returns (codes int8 [M, K], row scales fp32 [M])."""
+    return _quantize(lib().qd_quantize_and_rotate_rowwise, x, block, out_q, out_scale, True)
+
+
+def quantize_and_rotate_rowwise_int4(x, block: int = 256, out_q=None, out_scale=None):
+    """As quantize_and_rotate_rowwise with INT4 codes in [-7, 7] (int8 storage), s = amax/7."""
+    return _quantize(lib().qd_quantize_and_rotate_rowwise_int4, x, block, out_q, out_scale, True)
+
+
+def quantize_int8_rowwise(x, out_q=None, out_scale=None):
+    """Per-row dynamic symmetric INT8 quantization (no rotation)."""
+    return _quantize(lib().qd_quantize_int8_rowwise, x, 0, out_q, out_scale, False)
+
+
+def prepare_weights(w, block: int = 256):
+    """Offline weight preparation for int8_linear: rotate FP32 W [N, K] along K
+    (block 256, or 0 for none) and quantize per output channel.
+    Returns (wq int8 [N, K], w_scale fp32 [N])."""
+    if block == 0:
+        return quantize_int8_rowwise(w)
+    return quantize_and_rotate_rowwise(w, block)
+
+
+# ------------------------------------------------------------------------ GEMMs
+
+def int8_scaled_mm(aq, a_scale, wq, w_scale, bias=None, out=None):
+    """y[m, n] = bf16(((float)(aq . wq^T)[m, n] * a_scale[m]) * w_scale[n] + bias[n])."""
+    torch = _torch()
+    _mat(aq, "aq"), _mat(wq, "wq")
+    dev = _dev(aq, a_scale, wq, w_scale, bias, out)
+    M, K = aq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("aq and wq disagree on K")
+    _rows_vec(a_scale, M, torch.float32, "a_scale")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _mat(out, "out")
+    _check(lib().qd_int8_scaled_mm(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(wq), N, wq.stride(0),
+                                   _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def int8_gemm_i32(aq, wq, out=None):
+    """Raw int32 accumulators aq . wq^T of the same GEMM kernel."""
+    torch = _torch()
+    _mat(aq, "aq"), _mat(wq, "wq")
+    dev = _dev(aq, wq, out)
+    M, K = aq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("aq and wq disagree on K")
+    if out is None:
+        ldc = (N + 3) // 4 * 4
+        out = torch.empty((M, ldc), dtype=torch.int32, device=dev)[:, :N]
+    _mat(out, "out")
+    _check(lib().qd_int8_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wq), N, wq.stride(0), _ptr(out),
+                                  out.stride(0), _stream(dev)))
+    return out
+
+
+def workspace_size(M: int, K: int) -> int:
+    return int(lib().qd_int8_linear_workspace_size(M, K))
+
+
+def int8_linear(x, wq, w_scale, bias=None, rotate_block: int = 256, workspace=None, out=None):
+    """y = x W^T + b through the rotated INT8 path (two kernels: rotate+quantize,
+    then INT8 GEMM with the fused dequantizing epilogue).  wq/w_scale must come
+    from prepare_weights with the same rotate_block.  Returns bf16 [M, N]."""
+    torch = _torch()
+    _mat(x, "x"), _mat(wq, "wq")
+    dev = _dev(x, wq, w_scale, bias, workspace, out)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("x and wq disagree on K")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    need = workspace_size(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _mat(out, "out")
+    _check(lib().qd_int8_linear(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(wq), N, wq.stride(0),
+                                _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
+                                _stream(dev)))
+    return out
+
+
+# -------------------------------------------------------------- dequantization
+
+def dequantize_int8(q, scale, out_dtype=None, out=None):
+    """out = fl(q * s): s = scale[m] if scale has M entries, else scale[0] (per tensor)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    _mat(q, "q")
+    dev = _dev(q, scale, out)
+    M, K = q.shape
+    per_row = scale.numel() == M and M != 1
+    if scale.dtype != torch.float32 or (scale.numel() > 1 and scale.stride(0) != 1):
+        raise ValueError("scale must be a contiguous fp32 tensor")
+    if out is None:
+        out = torch.empty((M, K), dtype=out_dtype, device=dev)
+    _mat(out, "out")
+    _check(lib().qd_dequantize_int8(_ptr(q), M, K, q.stride(0), _ptr(scale), int(per_row),
+                                    _dtype_code(out), _ptr(out), out.stride(0), _stream(dev)))
+    return out

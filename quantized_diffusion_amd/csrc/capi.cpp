@@ -1,0 +1,211 @@
+// C ABI of the library (declared in include/qdiff.h): argument validation on
+// the host, then kernel launches on the caller's stream.  Nothing here
+// allocates, frees or synchronises, and no C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/qdiff.h"
+#include "qd_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qd_status_t fail(qd_status_t st, const char* fn, const char* fmt, ...) {
+    int n = snprintf(g_err, sizeof(g_err), "%s: ", fn);
+    if (n < 0) n = 0;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err + n, sizeof(g_err) - (size_t)n, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qd_status_t ok() {
+    g_err[0] = '\0';
+    return QD_OK;
+}
+
+qd_status_t hip_status(const char* fn, hipError_t e) {
+    if (e != hipSuccess) return fail(QD_EHIP, fn, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int dtype_size(qd_dtype_t dt) { return dt == QD_F32 ? 4 : 2; }
+
+bool dtype_ok(qd_dtype_t dt) { return dt == QD_F32 || dt == QD_BF16 || dt == QD_F16; }
+
+// Shared checks of the quantizers.
+qd_status_t check_quant(const char* fn, const void* x, qd_dtype_t dt, int64_t M, int64_t K,
+                        int64_t ldx, bool rotate, int32_t block, const int8_t* q, int64_t ldq,
+                        const float* scale) {
+    if (M < 0 || K <= 0) return fail(QD_EINVAL, fn, "need M >= 0 and K > 0 (M=%lld, K=%lld)", (long long)M, (long long)K);
+    if (M > 0 && (!x || !q || !scale)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (!dtype_ok(dt)) return fail(QD_EUNSUPPORTED, fn, "unknown input dtype %d", (int)dt);
+    if (ldx < K) return fail(QD_EINVAL, fn, "ldx (%lld) < K (%lld)", (long long)ldx, (long long)K);
+    if (ldq < K) return fail(QD_EINVAL, fn, "ldq (%lld) < K (%lld)", (long long)ldq, (long long)K);
+    if (rotate && block != 256) return fail(QD_EUNSUPPORTED, fn, "rotation block must be 256 (got %d)", block);
+    if (rotate && K % 256 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of the 256-wide rotation block", (long long)K);
+    if (K % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 16", (long long)K);
+    if (K > QD_MAX_K_QUANT) return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds %d", (long long)K, QD_MAX_K_QUANT);
+    if (M > INT32_MAX) return fail(QD_EUNSUPPORTED, fn, "M (%lld) exceeds INT32_MAX", (long long)M);
+    if (M > 0 && (!aligned16(x) || !aligned16(q)))
+        return fail(QD_EUNSUPPORTED, fn, "x and q must be 16-byte aligned");
+    if ((ldx * dtype_size(dt)) % 16 != 0 || ldq % 16 != 0)
+        return fail(QD_EUNSUPPORTED, fn, "row strides must be multiples of 16 bytes (ldx*%d=%lld, ldq=%lld)",
+                    dtype_size(dt), (long long)(ldx * dtype_size(dt)), (long long)ldq);
+    return QD_OK;
+}
+
+qd_status_t check_gemm(const char* fn, const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                       const int8_t* wq, int64_t N, int64_t ldw, const void* out, int64_t ldo,
+                       int64_t ldo_multiple) {
+    if (M < 0 || N < 0 || K <= 0)
+        return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
+    if (M > 0 && N > 0 && (!aq || !wq || !out)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (lda < K || ldw < K) return fail(QD_EINVAL, fn, "lda/ldw must be >= K");
+    if (ldo < N) return fail(QD_EINVAL, fn, "output leading dimension (%lld) < N (%lld)", (long long)ldo, (long long)N);
+    if (K % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 16", (long long)K);
+    if (K > QD_MAX_K_GEMM) return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds %d", (long long)K, QD_MAX_K_GEMM);
+    if (M > INT32_MAX - 256 || N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "M or N too large");
+    if ((M + 255) / 256 * ((N + 255) / 256) > INT32_MAX)
+        return fail(QD_EUNSUPPORTED, fn, "too many output tiles");
+    if (M > 0 && N > 0 && (!aligned16(aq) || !aligned16(wq) || !aligned16(out)))
+        return fail(QD_EUNSUPPORTED, fn, "aq, wq and the output must be 16-byte aligned");
+    if (lda % 16 != 0 || ldw % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "lda and ldw must be multiples of 16");
+    if (ldo % ldo_multiple != 0)
+        return fail(QD_EUNSUPPORTED, fn, "output leading dimension must be a multiple of %lld", (long long)ldo_multiple);
+    return QD_OK;
+}
+
+qd_status_t quantize_impl(const char* fn, const void* x, qd_dtype_t dt, int64_t M, int64_t K,
+                          int64_t ldx, bool rotate, int32_t block, int qmax, int8_t* q,
+                          int64_t ldq, float* scale, hipStream_t stream) {
+    qd_status_t st = check_quant(fn, x, dt, M, K, ldx, rotate, block, q, ldq, scale);
+    if (st != QD_OK) return st;
+    if (M == 0) return ok();
+    return hip_status(fn, qd::launch_rotquant(x, (int)dt, rotate, qmax, M, K, ldx, q, ldq, scale, stream));
+}
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t ws_codes_bytes(int64_t M, int64_t K) { return round_up((size_t)M * (size_t)round_up((size_t)K, 16), kAlign); }
+
+}  // namespace
+
+extern "C" {
+
+const char* qd_last_error(void) { return g_err; }
+
+const char* qd_version(void) { return "qdiff 0.1.0 (gfx950)"; }
+
+qd_status_t qd_quantize_and_rotate_rowwise(const void* x, qd_dtype_t x_dtype, int64_t M,
+                                           int64_t K, int64_t ldx, int32_t block, int8_t* q,
+                                           int64_t ldq, float* row_scale, hipStream_t stream) {
+    return quantize_impl("qd_quantize_and_rotate_rowwise", x, x_dtype, M, K, ldx, true, block, 127,
+                         q, ldq, row_scale, stream);
+}
+
+qd_status_t qd_quantize_and_rotate_rowwise_int4(const void* x, qd_dtype_t x_dtype, int64_t M,
+                                                int64_t K, int64_t ldx, int32_t block,
+                                                int8_t* q, int64_t ldq, float* row_scale,
+                                                hipStream_t stream) {
+    return quantize_impl("qd_quantize_and_rotate_rowwise_int4", x, x_dtype, M, K, ldx, true, block,
+                         7, q, ldq, row_scale, stream);
+}
+
+qd_status_t qd_quantize_int8_rowwise(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                     int64_t ldx, int8_t* q, int64_t ldq, float* row_scale,
+                                     hipStream_t stream) {
+    return quantize_impl("qd_quantize_int8_rowwise", x, x_dtype, M, K, ldx, false, 0, 127, q, ldq,
+                         row_scale, stream);
+}
+
+qd_status_t qd_int8_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                              const float* a_scale, const int8_t* wq, int64_t N, int64_t ldw,
+                              const float* w_scale, const void* bias_bf16, void* y_bf16,
+                              int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_int8_scaled_mm";
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, wq, N, ldw, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    return hip_status(fn, qd::launch_gemm_bf16(aq, lda, a_scale, wq, ldw, w_scale, bias_bf16,
+                                               y_bf16, ldy, M, N, K, stream));
+}
+
+size_t qd_int8_linear_workspace_size(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    return ws_codes_bytes(M, K) + round_up((size_t)M * sizeof(float), kAlign);
+}
+
+qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                           int64_t ldx, const int8_t* wq, int64_t N, int64_t ldw,
+                           const float* w_scale, const void* bias_bf16, int32_t rotate_block,
+                           void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
+                           hipStream_t stream) {
+    const char* fn = "qd_int8_linear";
+    if (rotate_block != 0 && rotate_block != 256)
+        return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 0 or 256 (got %d)", rotate_block);
+    const bool rotate = rotate_block == 256;
+    if (M < 0 || N < 0 || K <= 0)
+        return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    const int64_t ldq = (int64_t)round_up((size_t)K, 16);
+    if (!workspace) return fail(QD_EINVAL, fn, "null workspace");
+    if ((uintptr_t)workspace % kAlign) return fail(QD_EUNSUPPORTED, fn, "workspace must be 256-byte aligned");
+    if (workspace_bytes < qd_int8_linear_workspace_size(M, K))
+        return fail(QD_EINVAL, fn, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                    qd_int8_linear_workspace_size(M, K));
+    int8_t* aq = static_cast<int8_t*>(workspace);
+    float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_codes_bytes(M, K));
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, rotate, rotate_block, aq, ldq, sx);
+    if (st != QD_OK) return st;
+    st = check_gemm(fn, aq, M, K, ldq, wq, N, ldw, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, rotate, 127, M, K, ldx, aq, ldq, sx, stream);
+    if (e != hipSuccess) return hip_status(fn, e);
+    return hip_status(fn, qd::launch_gemm_bf16(aq, ldq, sx, wq, ldw, w_scale, bias_bf16, y_bf16,
+                                               ldy, M, N, K, stream));
+}
+
+qd_status_t qd_dequantize_int8(const int8_t* q, int64_t M, int64_t K, int64_t ldq,
+                               const float* scale, int32_t per_row, qd_dtype_t out_dtype,
+                               void* out, int64_t ldo, hipStream_t stream) {
+    const char* fn = "qd_dequantize_int8";
+    if (M < 0 || K <= 0) return fail(QD_EINVAL, fn, "need M >= 0 and K > 0");
+    if (M > 0 && (!q || !scale || !out)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (out_dtype != QD_F32 && out_dtype != QD_BF16)
+        return fail(QD_EUNSUPPORTED, fn, "output dtype must be F32 or BF16");
+    if (ldq < K || ldo < K) return fail(QD_EINVAL, fn, "ldq and ldo must be >= K");
+    if (K % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 16", (long long)K);
+    if (M > 0 && (!aligned16(q) || !aligned16(out))) return fail(QD_EUNSUPPORTED, fn, "q and out must be 16-byte aligned");
+    if (ldq % 16 != 0 || (ldo * dtype_size(out_dtype)) % 16 != 0)
+        return fail(QD_EUNSUPPORTED, fn, "row strides must be multiples of 16 bytes");
+    if (M == 0) return ok();
+    return hip_status(fn, qd::launch_dequant(q, ldq, scale, per_row != 0, out_dtype == QD_BF16, out,
+                                             ldo, M, K, stream));
+}
+
+qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                             const int8_t* wq, int64_t N, int64_t ldw, int32_t* acc,
+                             int64_t ldc, hipStream_t stream) {
+    const char* fn = "qd_int8_gemm_i32";
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, wq, N, ldw, acc, ldc, 4);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    return hip_status(fn, qd::launch_gemm_i32(aq, lda, wq, ldw, acc, ldc, M, N, K, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Dequantization of INT8 codes: out[m, k] = fl(q[m, k] * s) with s per row or
+// per tensor, stored as FP32 or rounded to BF16 (nearest-even).  The
+// operation is dequantize_int8_simple / dequantize_int8_simple_dtype of the
+// comfy-kitchen 0.2.40 page ("Huawei Ascend backend").  Memory-bound: one
+// thread converts one 16-byte chunk of codes (16 outputs).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+namespace {
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__ q, int64_t ldq,
+                                                      const float* __restrict__ scale, int per_row,
+                                                      uint8_t* __restrict__ out, int64_t ldo_bytes,
+                                                      int64_t M, int64_t chunks_per_row) {
+#pragma clang fp contract(off)
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * chunks_per_row) return;
+    const int64_t m = idx / chunks_per_row;
+    const int64_t c = idx - m * chunks_per_row;
+    const float s = per_row ? scale[m] : scale[0];
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q + m * ldq + c * 16));
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int8_t b = (int8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+        v[i] = (float)b * s;
+    }
+    if (OUT_BF16) {
+        uint8_t* dst = out + m * ldo_bytes + c * 32;
+        u32x4 lo = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7])};
+        u32x4 hi = {pack_bf16x2(v[8], v[9]), pack_bf16x2(v[10], v[11]), pack_bf16x2(v[12], v[13]),
+                    pack_bf16x2(v[14], v[15])};
+        __builtin_nontemporal_store(lo, reinterpret_cast<u32x4*>(dst));
+        __builtin_nontemporal_store(hi, reinterpret_cast<u32x4*>(dst + 16));
+    } else {
+        uint8_t* dst = out + m * ldo_bytes + c * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 o = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(dst + 16 * i));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(const int8_t* q, int64_t ldq, const float* scale, bool per_row,
+                          bool out_bf16, void* out, int64_t ldo, int64_t M, int64_t K,
+                          hipStream_t stream) {
+    const int64_t cpr = K / 16;
+    const int64_t total = M * cpr;
+    const int64_t grid = (total + 255) / 256;
+    if (out_bf16)
+        dequant_kernel<true><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+            q, ldq, scale, per_row ? 1 : 0, static_cast<uint8_t*>(out), ldo * 2, M, cpr);
+    else
+        dequant_kernel<false><<<dim3((unsigned)grid), dim3(256), 0, stream>>>(
+            q, ldq, scale, per_row ? 1 : 0, static_cast<uint8_t*>(out), ldo * 4, M, cpr);
+    return hipGetLastError();
+}
+
+}  // namespace qd

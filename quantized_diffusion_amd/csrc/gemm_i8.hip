@@ -1,0 +1,279 @@
+// INT8 x INT8 -> INT32 GEMM on the gfx950 matrix cores with a fused
+// dequantizing epilogue.
+//
+// Computes acc[m, n] = sum_k aq[m, k] * wq[n, k] (both operands K-contiguous,
+// "TN") exactly in INT32 and, in the BF16 mode, writes
+// y[m, n] = bf16_rne(((float)acc * a_scale[m]) * w_scale[n] + bias[n])
+// straight from the accumulators, so the INT32 product never reaches memory
+// (the fused rescale-and-bias store of the ComfyUI-AppleSilicon-FP8 README,
+// "What it fixes" row 17; dtypes per the SGLang PR "Tune Kitchen INT8 row
+// splitting for SM120", "Accuracy Test").  The INT32 mode stores the raw
+// accumulators instead and exists to verify the contraction bit for bit.
+//
+// Tiling.  A workgroup of 256 threads (4 waves) owns a 256 x 256 output
+// tile; each wave owns 128 x 128 and keeps it in 16 MFMA accumulators
+// (v_mfma_i32_32x32x32_i8, 256 INT32 registers per lane).  The K loop walks
+// 64-byte slices: every thread fetches four 16-byte chunks of each operand
+// into registers for the next slice while the matrix cores work on the
+// current one from LDS (two LDS stages, one barrier per slice).
+//
+// MFMA roles.  The weight tile is the MFMA "A" operand (its rows index n)
+// and the activation tile is "B" (its columns index m), so each lane ends up
+// holding four consecutive n of one m per 4-register group: the epilogue
+// stores 4 BF16 (8 bytes) or 4 INT32 (16 bytes) per instruction.  A lane
+// feeds row (lane % 32) of either operand with the 16 bytes of K-group
+// (lane / 32); both operands use the same byte order, so the dot product is
+// exact whatever order the hardware assigns within a K-group.
+//
+// LDS layout.  Each operand stage is [256 rows][64 bytes]; the four 16-byte
+// chunks of row r are stored XOR-swizzled by ((r >> 1) ^ (r >> 2)) & 3 so
+// that the 16-byte reads of 32 consecutive rows hit distinct banks.
+//
+// Tile order.  Workgroup g runs on XCD g % 8; tiles are renumbered so that
+// each XCD gets a contiguous range, and inside a range tiles go down groups
+// of GROUP_M tile rows first, so the ~32 tiles an XCD runs at once share
+// A and B panels in its L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+namespace {
+
+constexpr int BM = 256;      // activation rows per tile
+constexpr int BN = 256;      // weight rows (output columns) per tile
+constexpr int BK = 64;       // K bytes per slice
+constexpr int NT = 256;      // threads per workgroup
+constexpr int GROUP_M = 8;   // tile rows per L2 group
+constexpr int NXCD = 8;
+
+enum { MODE_BF16 = 0, MODE_I32 = 1 };
+
+struct EpiArgs {
+    const float* a_scale;
+    const float* w_scale;
+    const uint16_t* bias;   // may be null
+    void* out;              // uint16_t (BF16) or int32_t
+    int64_t ldo;            // elements
+};
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return bits_f((uint32_t)b << 16); }
+
+// Four outputs y[m, n + e] = bf16_rne(((float)acc_e * sx) * sw_e + b_e), FP32, no contraction.
+__device__ __forceinline__ void store_bf16x4(const int32_t* a4, float sx, int n, int N, int64_t m,
+                                             const EpiArgs& ep) {
+#pragma clang fp contract(off)
+    uint16_t* dst = static_cast<uint16_t*>(ep.out) + m * ep.ldo + n;
+    if (n + 3 < N) {
+        const f32x4 sw = *reinterpret_cast<const f32x4*>(ep.w_scale + n);
+        float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ep.bias) {
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(ep.bias + n);
+            b4[0] = bits_f(bb[0] << 16);
+            b4[1] = bits_f(bb[0] & 0xFFFF0000u);
+            b4[2] = bits_f(bb[1] << 16);
+            b4[3] = bits_f(bb[1] & 0xFFFF0000u);
+        }
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float tt = (float)a4[e];
+            tt = tt * sx;
+            tt = tt * sw[e];
+            if (ep.bias) tt = tt + b4[e];
+            o[e] = tt;
+        }
+        u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(dst) = pk;
+    } else {
+        for (int e = 0; e < 4 && n + e < N; ++e) {
+            float tt = (float)a4[e];
+            tt = tt * sx;
+            tt = tt * ep.w_scale[n + e];
+            if (ep.bias) tt = tt + bf16_to_f32(ep.bias[n + e]);
+            dst[e] = (uint16_t)(pack_bf16x2(tt, 0.0f) & 0xFFFFu);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_i32x4(const int32_t* a4, int n, int N, int64_t m,
+                                            const EpiArgs& ep) {
+    int32_t* dst = static_cast<int32_t*>(ep.out) + m * ep.ldo + n;
+    if (n + 3 < N) {
+        i32x4 v = {a4[0], a4[1], a4[2], a4[3]};
+        *reinterpret_cast<i32x4*>(dst) = v;
+    } else {
+        for (int e = 0; e < 4 && n + e < N; ++e) dst[e] = a4[e];
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void gemm_i8_kernel(const int8_t* __restrict__ A, int64_t lda,
+                                                        const int8_t* __restrict__ W, int64_t ldw,
+                                                        int M, int N, int K, EpiArgs ep) {
+    __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) int8_t sW[2][BN * BK];
+
+    // ---- tile coordinates (XCD-contiguous, grouped) ----
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int T = tiles_m * tiles_n;
+    const int g = blockIdx.x;
+    const int xcd = g % NXCD;
+    const int q8 = T / NXCD, rem = T % NXCD;
+    const int t = xcd * q8 + min(xcd, rem) + g / NXCD;
+    const int per_group = GROUP_M * tiles_n;
+    const int group = t / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsz = min(tiles_m - first_m, GROUP_M);
+    const int tg = t - group * per_group;
+    const int tm = first_m + tg % gsz;
+    const int tn = tg / gsz;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave & 1;   // 128-row half of the activation tile
+    const int wn = wave >> 1;  // 128-row half of the weight tile
+
+    // ---- global -> register staging: 4 chunks per operand per thread ----
+    // chunk id q = i*256 + tid -> row q/4, 16-byte column q%4
+    const int ld_c = tid & 3;
+    const int ld_r = tid >> 2;     // + 64*i
+    const int8_t* a_src[4];
+    const int8_t* w_src[4];
+    bool a_ok[4], w_ok[4];
+    int st_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = ld_r + 64 * i;
+        a_ok[i] = (m0 + r) < M;
+        w_ok[i] = (n0 + r) < N;
+        a_src[i] = A + (int64_t)(a_ok[i] ? m0 + r : 0) * lda + ld_c * 16;
+        w_src[i] = W + (int64_t)(w_ok[i] ? n0 + r : 0) * ldw + ld_c * 16;
+        st_off[i] = r * BK + ((ld_c ^ swz(r)) << 4);
+    }
+    u32x4 ra[4], rw[4];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    auto gload = [&](int k0) {
+        const bool kin = (k0 + ld_c * 16) < K;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ra[i] = (a_ok[i] && kin) ? *reinterpret_cast<const u32x4*>(a_src[i] + k0) : zero4;
+            rw[i] = (w_ok[i] && kin) ? *reinterpret_cast<const u32x4*>(w_src[i] + k0) : zero4;
+        }
+    };
+    auto sstore = [&](int s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4*>(&sA[s][st_off[i]]) = ra[i];
+            *reinterpret_cast<u32x4*>(&sW[s][st_off[i]]) = rw[i];
+        }
+    };
+
+    // ---- LDS -> MFMA operand offsets ----
+    // wave reads rows base + 32*blk + lane%32, chunk 2*kk + lane/32
+    const int fr = lane & 31;
+    const int fk = lane >> 5;
+    int a_off[4][2], w_off[4][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int ra_row = wm * 128 + b * 32 + fr;
+        const int rw_row = wn * 128 + b * 32 + fr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = 2 * kk + fk;
+            a_off[b][kk] = ra_row * BK + ((c ^ swz(ra_row)) << 4);
+            w_off[b][kk] = rw_row * BK + ((c ^ swz(rw_row)) << 4);
+        }
+    }
+
+    i32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int nk = (K + BK - 1) / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & 1;
+        if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            i32x4 fa[4], fw[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                fw[b] = *reinterpret_cast<const i32x4*>(&sW[s][w_off[b][kk]]);
+                fa[b] = *reinterpret_cast<const i32x4*>(&sA[s][a_off[b][kk]]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fw[i], fa[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < nk) sstore(s ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+    // acc[i][j][4*g4 + e] holds (n, m) = (n0 + wn*128 + 32*i + 8*g4 + 4*fk + e,
+    //                                     m0 + wm*128 + 32*j + fr)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int m = m0 + wm * 128 + 32 * j + fr;
+        if (m >= M) continue;
+        const float sx = (MODE == MODE_BF16) ? ep.a_scale[m] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int n = n0 + wn * 128 + 32 * i + 8 * g4 + 4 * fk;
+                if (n >= N) continue;
+                const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                       acc[i][j][4 * g4 + 3]};
+                if (MODE == MODE_I32) store_i32x4(a4, n, N, m, ep);
+                else store_bf16x4(a4, sx, n, N, m, ep);
+            }
+        }
+    }
+}
+
+template <int MODE>
+hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, int64_t M,
+                  int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_i8_kernel<MODE><<<dim3((unsigned)tiles), dim3(NT), 0, stream>>>(aq, lda, wq, ldw, (int)M,
+                                                                        (int)N, (int)K, ep);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
+                            int64_t ldw, const float* w_scale, const void* bias, void* y,
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy};
+    return launch<MODE_BF16>(aq, lda, wq, ldw, M, N, K, ep, stream);
+}
+
+hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
+                           int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream) {
+    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc};
+    return launch<MODE_I32>(aq, lda, wq, ldw, M, N, K, ep, stream);
+}
+
+}  // namespace qd

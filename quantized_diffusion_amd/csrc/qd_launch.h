@@ -1,0 +1,29 @@
+// Kernel launchers (host side).  Arguments are validated by the C ABI layer
+// before these are called; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qd {
+
+// dtype: 0 = FP32, 1 = BF16, 2 = FP16.  qmax 127 or 7 (7 only with rotate).
+hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int64_t M, int64_t K,
+                           int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream);
+
+// y (BF16) = epilogue(aq . wq^T); bias may be null.
+hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
+                            int64_t ldw, const float* w_scale, const void* bias, void* y,
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// acc (INT32) = aq . wq^T.
+hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
+                           int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                           hipStream_t stream);
+
+// out = q * scale (per row or per tensor) as FP32 (out_bf16 = false) or BF16.
+hipError_t launch_dequant(const int8_t* q, int64_t ldq, const float* scale, bool per_row,
+                          bool out_bf16, void* out, int64_t ldo, int64_t M, int64_t K,
+                          hipStream_t stream);
+
+}  // namespace qd

@@ -1,0 +1,261 @@
+// Rotate-and-quantize kernel for gfx950 (CDNA4).
+//
+// Computes, per row of x, the block-256 normalised Walsh-Hadamard rotation
+// (Sylvester order, FP32 butterfly with pair distance 1, 2, ..., 128, then
+// x 1/16), the row scale s = amax / qmax and the codes
+// clamp(rne(fl(v / s)), -qmax, qmax).  The operation is the one the
+// comfy-kitchen 0.2.40 page lists as quantize_and_rotate_rowwise ("Huawei
+// Ascend backend"); the rotation is the ConvRot256 of the SGLang PR
+// "Tune Kitchen INT8 row splitting for SM120" ("Accuracy Test").  With
+// ROT == false the same kernel is quantize_int8_rowwise.
+//
+// Work layout.  Four lanes (a "quad") own one 256-element block: lane ql of
+// the quad holds the 16-byte chunks c = 4*i + ql (i = 0 .. NI-1) of the
+// block, so each load instruction of a quad reads 64 contiguous bytes and a
+// wave reads 16 such pieces of consecutive blocks.  With E elements per
+// chunk the element index is (4*i + ql)*E + e, so butterfly stages on the
+// bits of e and of i stay inside a lane's registers and the two stages on
+// the bits of ql cross lanes through DPP quad permutes.
+//
+// Cross-lane stages without per-lane opcodes: a lane computes
+// own + c * partner with c = +1 in the lower lane of the pair and -1 in the
+// upper lane.  The lower lane gets a + c exactly as the butterfly does; the
+// upper lane gets c - a, the exact negation of a - c (round-to-nearest is
+// symmetric).  Both lanes of every later pair carry the same sign, so each
+// lane's values are the true values times tau = (-1)^popcount(ql), and the
+// sign is folded into the reciprocal of the scale when quantizing.
+//
+// Quantization without a division per element.  With r = fl(1/s) the exact
+// product x = v*r differs from Q = v/s by at most |Q|*2^-24 < 2^-17, and
+// |fl(Q) - Q| <= 2^-18 for |Q| < 128.  The code is taken as rne(x) (one FMA
+// with 1.5*2^23); a second FMA gives d = x - rne(x).  When |d| < 0.5 - 2^-15,
+// fl(Q) lies strictly within 0.5 of the same integer, so rne(fl(Q)) equals
+// it.  Otherwise (about 6e-5 of the elements) the element is redone with the
+// correctly rounded division, which is also used for whole rows whose scale
+// is below 2^-100.  The 1/16 of the rotation is applied to amax and to r
+// (powers of two, exact); the slow path applies it to the element exactly as
+// the definition does.
+//
+// Row amax: per-lane max, quad reduction by DPP, then an LDS atomic max over
+// the blocks of the row (non-negative floats order like their bit patterns).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+namespace {
+
+struct InF32 { static constexpr int E = 4; };
+struct InBF16 { static constexpr int E = 8; };
+struct InF16 { static constexpr int E = 8; };
+
+__device__ __forceinline__ void widen(InF32, const u32x4& d, float* v) {
+    v[0] = bits_f(d[0]); v[1] = bits_f(d[1]); v[2] = bits_f(d[2]); v[3] = bits_f(d[3]);
+}
+__device__ __forceinline__ void widen(InBF16, const u32x4& d, float* v) {
+    const uint32_t w[4] = {d[0], d[1], d[2], d[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bits_f(w[i] << 16);
+        v[2 * i + 1] = bits_f(w[i] & 0xFFFF0000u);
+    }
+}
+__device__ __forceinline__ void widen(InF16, const u32x4& d, float* v) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const uint32_t w[4] = {d[0], d[1], d[2], d[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h2 p = __builtin_bit_cast(h2, w[i]);
+        v[2 * i] = (float)p[0];
+        v[2 * i + 1] = (float)p[1];
+    }
+}
+
+constexpr float kMagic = 12582912.0f;             // 1.5 * 2^23
+constexpr float kFastMargin = 0.5f - 0x1p-15f;    // |d| below this: fast code is exact
+constexpr float kSlowScale = 0x1p-100f;           // rows with s below this take the exact path
+
+// Exact code of one element by the definition: v = fl(u * 1/16) (rotated) or
+// v = u, then clamp(rne(fl(v / s))).  `w` is tau * u.  Returned as a byte.
+template <bool ROT, int QMAX>
+__device__ __forceinline__ uint32_t exact_code(float w, float tau, float s) {
+#pragma clang fp contract(off)
+    const float u = tau * w;
+    const float v = ROT ? u * 0.0625f : u;
+    float t = __builtin_rintf(v / s);
+    t = __builtin_fminf(__builtin_fmaxf(t, (float)-QMAX), (float)QMAX);
+    return (uint32_t)(int)t & 0xFFu;
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <class In, bool ROT, int QMAX>
+__global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restrict__ x,
+                                                        int64_t ldx_bytes, int M, int K, int nb,
+                                                        int R, int8_t* __restrict__ q,
+                                                        int64_t ldq, float* __restrict__ scale) {
+    constexpr int E = In::E;             // elements per 16-byte chunk
+    constexpr int NI = 256 / (4 * E);    // chunks per lane per block
+    constexpr int NV = NI * E;           // 64 values per lane
+    constexpr int ESZ = 16 / E;          // bytes per input element
+    __shared__ uint32_t row_amax[256];
+
+    const int tid = threadIdx.x;
+    const int quad = tid >> 2;
+    const int ql = tid & 3;
+    const int rl = quad / nb;
+    const int blk = quad - rl * nb;
+    const int row = blockIdx.x * R + rl;
+    const bool active = (rl < R) && (row < M);
+    if (tid < R) row_amax[tid] = 0u;
+
+    float v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = 0.0f;
+    if (active) {
+        const uint8_t* src = x + (int64_t)row * ldx_bytes + (int64_t)blk * 256 * ESZ;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = i * 4 + ql;
+            if (ROT || blk * 256 + c * E < K) {
+                const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 16));
+                widen(In{}, d, &v[i * E]);
+            }
+        }
+    }
+
+    if (ROT) {
+        // stages on the element bits inside a chunk
+#pragma unroll
+        for (int h = 1; h < E; h *= 2) {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                if (!(j & h)) {
+                    const float a = v[j], c = v[j + h];
+                    v[j] = a + c;
+                    v[j + h] = a - c;
+                }
+            }
+        }
+        // stages on the two quad-lane bits (pair distance E and 2E)
+        const float c0 = (ql & 1) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = __builtin_fmaf(quad_xor1(v[j]), c0, v[j]);
+        const float c1 = (ql & 2) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = __builtin_fmaf(quad_xor2(v[j]), c1, v[j]);
+        // stages on the chunk-index bits (pair distance 4E, 8E, ...)
+#pragma unroll
+        for (int hi = 1; hi < NI; hi *= 2) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                if (!(i & hi)) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float a = v[i * E + e], c = v[(i + hi) * E + e];
+                        v[i * E + e] = a + c;
+                        v[(i + hi) * E + e] = a - c;
+                    }
+                }
+            }
+        }
+    }
+
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) am = __builtin_fmaxf(am, __builtin_fabsf(v[j]));
+    am = __builtin_fmaxf(am, quad_xor1(am));
+    am = __builtin_fmaxf(am, quad_xor2(am));
+    __syncthreads();
+    if (active && ql == 0) atomicMax(&row_amax[rl], f_bits(am));
+    __syncthreads();
+    if (!active) return;
+
+    const float amax_u = bits_f(row_amax[rl]);
+    const float amax = ROT ? amax_u * 0.0625f : amax_u;
+    const float s = amax / (float)QMAX;
+    if (blk == 0 && ql == 0) scale[row] = s;
+    const float tau = (ROT && ((ql ^ (ql >> 1)) & 1)) ? -1.0f : 1.0f;
+
+    // Per row: 0 = all codes zero, 1 = fast path with exact fallback,
+    // 2 = exact division for every element (tiny scales).
+    const int mode = (s >= kSlowScale) ? 1 : (s == 0.0f ? 0 : 2);
+    const float r = 1.0f / s;
+    const float trs = tau * (ROT ? r * 0.0625f : r);
+    int8_t* dst = q + (int64_t)row * ldq + (int64_t)blk * 256;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int c = i * 4 + ql;
+        if (!ROT && blk * 256 + c * E >= K) continue;
+        uint32_t code[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float w = v[i * E + e];
+            const float t = __builtin_fmaf(w, trs, kMagic);
+            const float n = t - kMagic;
+            const float d = __builtin_fmaf(w, trs, -n);
+            uint32_t cb = f_bits(t);
+            if (__builtin_expect(mode != 1 || __builtin_fabsf(d) >= kFastMargin, 0))
+                cb = mode == 0 ? 0u : exact_code<ROT, QMAX>(w, tau, s);
+            code[e] = cb;
+        }
+        if (E == 8) {
+            u32x2 p;
+            p[0] = pack4(code[0], code[1], code[2], code[3]);
+            p[1] = pack4(code[4 % E], code[5 % E], code[6 % E], code[7 % E]);
+            __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(dst + c * E));
+        } else {
+            const uint32_t p = pack4(code[0], code[1], code[2], code[3]);
+            __builtin_nontemporal_store(p, reinterpret_cast<uint32_t*>(dst + c * E));
+        }
+    }
+}
+
+template <class In, bool ROT, int QMAX>
+hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                        float* scale, hipStream_t stream) {
+    constexpr int ESZ = 16 / In::E;
+    const int nb = (int)((K + 255) / 256);
+    // Rows per workgroup: one quad per (row, block); pick the row count that
+    // leaves the fewest idle lanes in whole waves, preferring ~256 threads.
+    int R = 1, best_threads = 0;
+    double best_waste = 2.0;
+    const int r0 = nb >= 64 ? 1 : 64 / nb;
+    for (int r = r0; r <= 2 * r0 && 4 * r * nb <= 1024; ++r) {
+        const int th = (4 * r * nb + 63) / 64 * 64;
+        const double waste = (double)(th - 4 * r * nb) / th;
+        if (waste < best_waste - 1e-9) { best_waste = waste; R = r; best_threads = th; }
+    }
+    if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
+    if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
+    const int64_t grid = (M + R - 1) / R;
+    rotquant_kernel<In, ROT, QMAX><<<dim3((unsigned)grid), dim3(best_threads), 0, stream>>>(
+        static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int64_t M, int64_t K,
+                           int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
+#define QD_DISPATCH(IN)                                                                       \
+    if (rotate) {                                                                             \
+        if (qmax == 7) return launch_typed<IN, true, 7>(x, M, K, ldx, q, ldq, scale, stream); \
+        return launch_typed<IN, true, 127>(x, M, K, ldx, q, ldq, scale, stream);              \
+    }                                                                                         \
+    return launch_typed<IN, false, 127>(x, M, K, ldx, q, ldq, scale, stream);
+    switch (dtype) {
+        case 0: QD_DISPATCH(InF32)
+        case 1: QD_DISPATCH(InBF16)
+        default: QD_DISPATCH(InF16)
+    }
+#undef QD_DISPATCH
+}
+
+}  // namespace qd

@@ -30,7 +30,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "workload", "make_x", "make_w", "make_bias",
+__all__ = ["Workload", "WORKLOADS", "workload", "make_x", "make_w", "make_bias", "iter_x", "iter_w",
            "outlier_columns", "f32_to_bf16_bits", "bf16_bits_to_f32", "random_bf16"]
 
 
@@ -86,20 +86,61 @@ def outlier_columns(w: Workload) -> np.ndarray:
     return np.sort(_rng(4000 + w.cid).choice(w.K, size=w.n_outliers, replace=False))
 
 
-def make_x(w: Workload, rows: slice | None = None) -> np.ndarray:
-    """BF16 activations [M, K] as uint16 bit patterns (optionally a row slice)."""
+CHUNK_ROWS = 2048
+
+
+def iter_x(w: Workload, rows: int | None = None, chunk_rows: int = CHUNK_ROWS):
+    """Yield (r0, r1, bits) for consecutive row chunks of the BF16 activations.
+
+    The values are exactly those of one standard_normal draw of shape [M, K]
+    from the seeded generator (the generator is consumed in row order), so
+    chunking changes nothing.  ``rows`` stops after that many leading rows.
+    ``bits`` is a reused uint16 buffer: consume it before the next step."""
+    import torch
+    M = w.M if rows is None else min(rows, w.M)
     g = _rng(1000 + w.cid)
-    x = g.standard_normal((w.M, w.K), dtype=np.float32)
-    if rows is not None:
-        x = x[rows]
-    x[:, outlier_columns(w)] *= np.float32(20.0)
-    return f32_to_bf16_bits(x)
+    cols = outlier_columns(w)
+    cr = max(1, min(chunk_rows, M))
+    buf = np.empty((cr, w.K), np.float32)
+    tb = torch.empty((cr, w.K), dtype=torch.bfloat16)
+    for r0 in range(0, M, cr):
+        r1 = min(M, r0 + cr)
+        b = buf[: r1 - r0]
+        g.standard_normal(out=b, dtype=np.float32)
+        b[:, cols] *= np.float32(20.0)
+        t = tb[: r1 - r0]
+        t.copy_(torch.from_numpy(b))          # round to nearest-even
+        yield r0, r1, t.view(torch.int16).numpy().view(np.uint16)
+
+
+def make_x(w: Workload, rows: int | None = None) -> np.ndarray:
+    """BF16 activations [M, K] (or the leading ``rows`` rows) as uint16 bit patterns."""
+    M = w.M if rows is None else min(rows, w.M)
+    out = np.empty((M, w.K), np.uint16)
+    for r0, r1, bits in iter_x(w, rows):
+        out[r0:r1] = bits
+    return out
+
+
+def iter_w(w: Workload, chunk_rows: int = CHUNK_ROWS):
+    """Yield (r0, r1, fp32 chunk) of the weights [N, K] ~ N(0, 0.02) (reused buffer)."""
+    g = _rng(2000 + w.cid)
+    cr = min(chunk_rows, w.N)
+    buf = np.empty((cr, w.K), np.float32)
+    for r0 in range(0, w.N, cr):
+        r1 = min(w.N, r0 + cr)
+        b = buf[: r1 - r0]
+        g.standard_normal(out=b, dtype=np.float32)
+        b *= np.float32(0.02)
+        yield r0, r1, b
 
 
 def make_w(w: Workload) -> np.ndarray:
     """FP32 weights [N, K] ~ N(0, 0.02)."""
-    g = _rng(2000 + w.cid)
-    return g.standard_normal((w.N, w.K), dtype=np.float32) * np.float32(0.02)
+    out = np.empty((w.N, w.K), np.float32)
+    for r0, r1, b in iter_w(w):
+        out[r0:r1] = b
+    return out
 
 
 def make_bias(w: Workload) -> np.ndarray:

@@ -1,0 +1,145 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_diffusion_amd as qd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qdiff.h")
+
+FAKE = ctypes.c_void_p(0x100000)        # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x100008)    # 8-byte aligned only
+NULL = None
+STREAM = ctypes.c_void_p(0)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = qd.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in qdiff.h but not exported"
+    assert set(syms) == set(qd.EXPORTED_SYMBOLS)
+
+
+def test_version_and_empty_error():
+    assert b"gfx950" in qd.lib().qd_version()
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, qd.lib().qd_last_error().decode()
+
+
+Q = qd.QD_BF16
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((FAKE, Q, -1, 512, 512, 256, FAKE, 512, FAKE, STREAM), qd.QD_EINVAL, "M >= 0"),
+    ((FAKE, Q, 4, 0, 512, 256, FAKE, 512, FAKE, STREAM), qd.QD_EINVAL, "K > 0"),
+    ((NULL, Q, 4, 512, 512, 256, FAKE, 512, FAKE, STREAM), qd.QD_EINVAL, "null"),
+    ((FAKE, Q, 4, 512, 511, 256, FAKE, 512, FAKE, STREAM), qd.QD_EINVAL, "ldx"),
+    ((FAKE, Q, 4, 512, 512, 256, FAKE, 500, FAKE, STREAM), qd.QD_EINVAL, "ldq"),
+    ((FAKE, Q, 4, 512, 512, 128, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "block"),
+    ((FAKE, Q, 4, 528, 528, 256, FAKE, 528, FAKE, STREAM), qd.QD_EUNSUPPORTED, "multiple of the 256"),
+    ((FAKE, 7, 4, 512, 512, 256, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "dtype"),
+    ((FAKE, Q, 4, 65792, 65792, 256, FAKE, 65792, FAKE, STREAM), qd.QD_EUNSUPPORTED, "exceeds"),
+    ((FAKE_ODD, Q, 4, 512, 512, 256, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "aligned"),
+    ((FAKE, Q, 4, 512, 516, 256, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "multiples of 16"),
+])
+def test_quantize_and_rotate_validation(args, status, needle):
+    st, msg = _status(qd.lib().qd_quantize_and_rotate_rowwise, *args)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_quantize_rowwise_validation():
+    L = qd.lib()
+    st, msg = _status(L.qd_quantize_int8_rowwise, FAKE, Q, 4, 24, 24, FAKE, 32, FAKE, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 16" in msg
+    st, msg = _status(L.qd_quantize_int8_rowwise, FAKE, Q, 0, 48, 48, FAKE, 48, FAKE, STREAM)
+    assert st == qd.QD_OK, msg      # empty problem: nothing enqueued
+    st, msg = _status(L.qd_quantize_and_rotate_rowwise_int4, FAKE, Q, 2, 300, 304, 256, FAKE, 304, FAKE, STREAM)
+    assert st == qd.QD_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("args,status,needle", [
+    ((FAKE, 4, 0, 64, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EINVAL, "K > 0"),
+    ((FAKE, 4, 64, 64, FAKE, FAKE, -1, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EINVAL, "N >= 0"),
+    ((NULL, 4, 64, 64, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EINVAL, "null"),
+    ((FAKE, 4, 64, 32, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EINVAL, "lda"),
+    ((FAKE, 4, 64, 64, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 4, STREAM), qd.QD_EINVAL, "leading dimension"),
+    ((FAKE, 4, 72, 80, FAKE, FAKE, 8, 80, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EUNSUPPORTED, "multiple of 16"),
+    ((FAKE, 4, 64, 64, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 12, STREAM), qd.QD_EUNSUPPORTED, "multiple of 8"),
+    ((FAKE_ODD, 4, 64, 64, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EUNSUPPORTED, "aligned"),
+    ((FAKE, 4, 64, 72, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EUNSUPPORTED, "multiples of 16"),
+    ((FAKE, 4, 64, 64, NULL, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EINVAL, "scale"),
+    ((FAKE, 4, 64, 64, FAKE, FAKE, 8, 64, FAKE_ODD, NULL, FAKE, 8, STREAM), qd.QD_EUNSUPPORTED, "w_scale"),
+    ((FAKE, 4, 262144, 262144, FAKE, FAKE, 8, 262144, FAKE, NULL, FAKE, 8, STREAM), qd.QD_EUNSUPPORTED, "exceeds"),
+    ((FAKE, 0, 64, 64, FAKE, FAKE, 8, 64, FAKE, NULL, FAKE, 8, STREAM), qd.QD_OK, ""),
+])
+def test_scaled_mm_validation(args, status, needle):
+    st, msg = _status(qd.lib().qd_int8_scaled_mm, *args)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_gemm_i32_validation():
+    L = qd.lib()
+    st, msg = _status(L.qd_int8_gemm_i32, FAKE, 4, 64, 64, FAKE, 4, 64, FAKE, 6, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 4" in msg
+    st, msg = _status(L.qd_int8_gemm_i32, FAKE, 4, 64, 64, NULL, 8, 64, FAKE, 8, STREAM)
+    assert st == qd.QD_EINVAL
+
+
+def test_linear_validation_and_workspace():
+    L = qd.lib()
+    M, K, N = 10, 512, 64
+    ws = qd.workspace_size(M, K)
+    assert ws == 5120 + 256         # codes rounded to 256 B, then the scales
+    assert qd.workspace_size(0, K) == 0
+    base = dict(x=FAKE, dt=Q, M=M, K=K, ldx=K, wq=FAKE, N=N, ldw=K, sw=FAKE, b=NULL, rb=256,
+                ws=FAKE, wsb=ws, y=FAKE, ldy=N, s=STREAM)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return _status(L.qd_int8_linear, *a.values())
+
+    assert call(wsb=ws - 1)[0] == qd.QD_EINVAL
+    assert call(ws=NULL)[0] == qd.QD_EINVAL
+    assert call(ws=ctypes.c_void_p(0x100010))[0] == qd.QD_EUNSUPPORTED
+    assert call(rb=128)[0] == qd.QD_EUNSUPPORTED
+    assert call(K=528, ldx=528, ldw=528, wsb=10**6)[0] == qd.QD_EUNSUPPORTED
+    assert call(rb=0, K=528, ldx=528, ldw=528, wsb=10**6, ldy=60)[0] == qd.QD_EINVAL
+    assert call(sw=NULL)[0] == qd.QD_EINVAL
+    assert call(b=ctypes.c_void_p(0x100004))[0] == qd.QD_EUNSUPPORTED   # bias must be 8-byte aligned
+    assert call(M=0)[0] == qd.QD_OK
+    assert call(dt=9)[0] == qd.QD_EUNSUPPORTED
+
+
+def test_dequantize_validation():
+    L = qd.lib()
+    st, msg = _status(L.qd_dequantize_int8, FAKE, 4, 40, 48, FAKE, 1, qd.QD_F32, FAKE, 48, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 16" in msg
+    st, msg = _status(L.qd_dequantize_int8, FAKE, 4, 48, 48, FAKE, 1, qd.QD_F16, FAKE, 48, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "dtype" in msg
+    st, msg = _status(L.qd_dequantize_int8, FAKE, 4, 48, 40, FAKE, 1, qd.QD_F32, FAKE, 48, STREAM)
+    assert st == qd.QD_EINVAL
+    st, msg = _status(L.qd_dequantize_int8, FAKE, 0, 48, 48, FAKE, 1, qd.QD_F32, FAKE, 48, STREAM)
+    assert st == qd.QD_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        qd.quantize_and_rotate_rowwise(torch.zeros(4, 256, dtype=torch.bfloat16))

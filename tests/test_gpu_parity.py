@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle on the
+same seeded inputs.  Codes, row scales and INT32 accumulators must match bit
+for bit; BF16 outputs within one BF16 ulp of the oracle (the expected result
+is bit-identical, and the count of differing values is printed)."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_bf16_within_1ulp, bf16_bits, host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import quantized_diffusion_amd as q
+    q.lib()
+    return q
+
+
+def _x(shape, seed, scale=1.0, outliers=0):
+    from synth import random_bf16
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    if outliers:
+        cols = g.choice(shape[1], size=outliers, replace=False)
+        x[:, cols] *= 20
+    from synth import f32_to_bf16_bits
+    return f32_to_bf16_bits(x)
+
+
+# ---------------------------------------------------------------- quantizers
+
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 512), (63, 768), (256, 512), (257, 5376), (130, 7168),
+                                 (5, 28672), (2, 65536), (1000, 1024)])
+def test_rotquant_bf16(qd, O, M, K):
+    say(f"rotquant bf16 M={M} K={K}")
+    x = _x((M, K), seed=100 + M + K, outliers=max(1, K // 100))
+    q, s = qd.quantize_and_rotate_rowwise(to_dev_bf16(x))
+    qo, so = O.quantize_rowwise(x, "bf16", 256)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("M,K", [(7, 256), (129, 1280), (33, 5376)])
+def test_rotquant_other_dtypes(qd, O, dtype, M, K):
+    import torch
+    say(f"rotquant {dtype} M={M} K={K}")
+    g = np.random.Generator(np.random.PCG64(200 + M))
+    x = (g.standard_normal((M, K)) * 0.5).astype(np.float32 if dtype == "f32" else np.float16)
+    q, s = qd.quantize_and_rotate_rowwise(to_dev(x))
+    qo, so = O.quantize_rowwise(x, dtype, 256)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+def test_rotquant_near_ties_and_degenerate_rows(qd, O):
+    """Rows whose rotated values sit next to half-integer multiples of the scale
+    (the exact-division fallback), tiny-scale rows (the all-exact path), zero
+    rows, subnormal rows and single spikes."""
+    from exact import sylvester
+    say("rotquant near-ties / degenerate rows")
+    H = sylvester(256).astype(np.float64) / 16.0
+    g = np.random.Generator(np.random.PCG64(300))
+    rows = []
+    for t in range(24):
+        v = (g.integers(-126, 126, 512) + 0.5).astype(np.float64)
+        v[0] = 127.0
+        v *= 2.0 ** g.integers(-8, 8)
+        x = np.concatenate([H @ v[:256], H @ v[256:]])          # rotate(x) ~ v
+        rows.append(x.astype(np.float32))
+    rows.append(np.zeros(512, np.float32))
+    rows.append((g.standard_normal(512) * 1e-36).astype(np.float32))      # scale < 2^-100
+    rows.append((g.standard_normal(512) * 1e-30).astype(np.float32))
+    sub = np.zeros(512, np.float32)
+    sub[::7] = np.float32(1e-45) * g.integers(1, 50, sub[::7].size)
+    rows.append(sub)                                                       # subnormal inputs
+    spike = np.zeros(512, np.float32)
+    spike[300] = -3.0
+    rows.append(spike)
+    x = np.stack(rows)
+    q, s = qd.quantize_and_rotate_rowwise(to_dev(x))
+    qo, so = O.quantize_rowwise(x, "f32", 256)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+    # the same through the INT4 quantizer
+    q4, s4 = qd.quantize_and_rotate_rowwise_int4(to_dev(x))
+    qo4, so4 = O.quantize_rowwise(x, "f32", 256, qmax=7)
+    assert np.array_equal(host(s4).view(np.uint32), so4.view(np.uint32))
+    assert np.array_equal(host(q4), qo4)
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 48), (64, 272), (257, 5376), (3, 4096)])
+def test_quantize_int8_rowwise(qd, O, M, K):
+    say(f"quantize_int8_rowwise M={M} K={K}")
+    x = _x((M, K), seed=400 + K, outliers=1)
+    q, s = qd.quantize_int8_rowwise(to_dev_bf16(x))
+    qo, so = O.quantize_rowwise(x, "bf16", 0)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+@pytest.mark.parametrize("M,K", [(9, 512), (300, 28672)])
+def test_rotquant_int4(qd, O, M, K):
+    say(f"rotquant int4 M={M} K={K}")
+    x = _x((M, K), seed=500 + M, outliers=K // 100)
+    q, s = qd.quantize_and_rotate_rowwise_int4(to_dev_bf16(x))
+    qo, so = O.quantize_rowwise(x, "bf16", 256, qmax=7)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+def test_quantize_strided_rows(qd, O):
+    """Row strides larger than K on input and output."""
+    import torch
+    say("rotquant strided")
+    x = _x((40, 1024), seed=600)
+    xd = to_dev_bf16(x)[:, :768]
+    qbuf = torch.zeros((40, 800), dtype=torch.int8, device="cuda")
+    q, s = qd.quantize_and_rotate_rowwise(xd, out_q=qbuf[:, :768])
+    qo, so = O.quantize_rowwise(np.ascontiguousarray(x[:, :768]), "bf16", 256)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    assert np.all(host(qbuf[:, 768:]) == 0)
+
+
+# ---------------------------------------------------------------------- GEMM
+
+GEMM_SHAPES = [(1, 1, 16), (256, 256, 64), (257, 255, 80), (300, 520, 512), (513, 1000, 5376),
+               (64, 4100, 1024), (1024, 1024, 7168)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32_exact(qd, O, M, N, K):
+    say(f"gemm i32 M={M} N={N} K={K}")
+    g = np.random.Generator(np.random.PCG64(M * 7 + N * 3 + K))
+    a = g.integers(-128, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-128, 128, (N, K), dtype=np.int64).astype(np.int8)
+    acc = qd.int8_gemm_i32(to_dev(a), to_dev(w))
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+
+
+def test_gemm_i32_extremes(qd, O):
+    say("gemm i32 extremes")
+    K = 5376
+    a = np.full((300, K), 127, np.int8)
+    a[1::2] = -127
+    w = np.full((260, K), 127, np.int8)
+    w[::3] = -128
+    acc = qd.int8_gemm_i32(to_dev(a), to_dev(w))
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+
+
+@pytest.mark.parametrize("M,N,K,with_bias", [(256, 512, 512, True), (257, 264, 5376, True),
+                                              (77, 1000, 768, False), (1, 8, 16, True)])
+def test_scaled_mm_bf16(qd, O, M, N, K, with_bias):
+    say(f"scaled_mm M={M} N={N} K={K} bias={with_bias}")
+    import torch
+    g = np.random.Generator(np.random.PCG64(M + N + K))
+    a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    sx = (g.uniform(0.5, 2.0, M) * 2.0 ** -7).astype(np.float32)
+    sw = (g.uniform(0.5, 2.0, N) * 2.0 ** -12).astype(np.float32)
+    from synth import random_bf16
+    b = random_bf16(N, seed=K, scale=0.1) if with_bias else None
+    y = qd.int8_scaled_mm(to_dev(a), to_dev(sx), to_dev(w), to_dev(sw), None if b is None else to_dev_bf16(b))
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, b)
+    n = assert_bf16_within_1ulp(bf16_bits(y), yo, "scaled_mm")
+    say(f"  {n} of {yo.size} outputs differ from the oracle (allowed: 1 ulp)")
+
+
+# ------------------------------------------------------------- whole layer
+
+def test_int8_linear_tiny_config(qd, O):
+    """The 256/512/512 workload end to end (bias, outliers, rotation)."""
+    from synth import make_bias, make_w, make_x, workload
+    say("int8_linear tiny workload")
+    w = workload(1)
+    x, W, b = make_x(w), make_w(w), make_bias(w)
+    wq, sw = qd.prepare_weights(to_dev(W))
+    wqo, swo = O.prepare_weights(W)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw), swo)
+    y = qd.int8_linear(to_dev_bf16(x), wq, sw, to_dev_bf16(b))
+    yo = O.linear(x, wqo, swo, b)
+    n = assert_bf16_within_1ulp(bf16_bits(y), yo, "int8_linear")
+    say(f"  {n} of {yo.size} outputs differ from the oracle")
+    # unrotated variant
+    wq0, sw0 = qd.prepare_weights(to_dev(W), block=0)
+    y0 = qd.int8_linear(to_dev_bf16(x), wq0, sw0, to_dev_bf16(b), rotate_block=0)
+    yo0 = O.linear(x, *O.prepare_weights(W, 0), b, block=0)
+    assert_bf16_within_1ulp(bf16_bits(y0), yo0, "int8_linear unrotated")
+
+
+@pytest.mark.parametrize("M", [1, 2, 255, 257, 511])
+def test_int8_linear_ragged_rows(qd, O, M):
+    say(f"int8_linear ragged M={M}")
+    from synth import make_bias, make_w, workload
+    w = workload(1)
+    W, b = make_w(w), make_bias(w)
+    x = _x((M, w.K), seed=700 + M, outliers=4)
+    wqo, swo = O.prepare_weights(W)
+    y = qd.int8_linear(to_dev_bf16(x), to_dev(wqo), to_dev(swo), to_dev_bf16(b))
+    assert_bf16_within_1ulp(bf16_bits(y), O.linear(x, wqo, swo, b), "ragged")
+
+
+def test_dequantize(qd, O):
+    import torch
+    say("dequantize")
+    g = np.random.Generator(np.random.PCG64(800))
+    q = g.integers(-127, 128, (37, 272), dtype=np.int64).astype(np.int8)
+    s = (g.uniform(0.5, 2, 37) * 2.0 ** g.integers(-30, 5, 37)).astype(np.float32)
+    d = qd.dequantize_int8(to_dev(q), to_dev(s))
+    assert np.array_equal(host(d).view(np.uint32), O.dequantize(q, s, True, "f32").view(np.uint32))
+    db = qd.dequantize_int8(to_dev(q), to_dev(s), torch.bfloat16)
+    assert np.array_equal(bf16_bits(db), O.dequantize(q, s, True, "bf16"))
+    dt = qd.dequantize_int8(to_dev(q), to_dev(s[:1]))
+    assert np.array_equal(host(dt), O.dequantize(q, s[:1], False, "f32"))
+
+
+def test_empty_inputs(qd):
+    import torch
+    say("empty inputs")
+    x = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    q, s = qd.quantize_and_rotate_rowwise(x)
+    assert q.shape == (0, 512) and s.shape == (0,)
+    wq = torch.zeros((8, 512), dtype=torch.int8, device="cuda")
+    sw = torch.ones(8, dtype=torch.float32, device="cuda")
+    y = qd.int8_linear(x, wq, sw)
+    assert y.shape == (0, 8)
