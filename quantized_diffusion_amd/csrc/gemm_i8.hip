@@ -10,20 +10,22 @@
 // splitting for SM120", "Accuracy Test").  The INT32 mode stores the raw
 // accumulators instead and exists to verify the contraction bit for bit.
 //
-// Tiling.  A workgroup of 256 threads (4 waves) owns a 256 x 256 output
-// tile; each wave owns 128 x 128 and keeps it in 16 MFMA accumulators
-// (v_mfma_i32_32x32x32_i8, 256 INT32 registers per lane).  The K loop walks
-// 64-byte slices: every thread fetches four 16-byte chunks of each operand
-// into registers for the next slice while the matrix cores work on the
-// current one from LDS (two LDS stages, one barrier per slice).
+// Main kernel (K % 64 == 0): a workgroup of 8 waves owns a 256 x 256 output
+// tile; each wave owns 64 output columns x 128 rows in eight
+// v_mfma_i32_32x32x32_i8 accumulators, two waves per SIMD so that one keeps
+// the matrix pipe fed while the other waits.  Operands move global -> LDS
+// with global_load_lds_dwordx4 (no staging registers) through a ring of
+// four 64-byte K slices; copies run three slices ahead and are spread over
+// the slice so that the copy queue never stalls a wave for long.  The output
+// tile is staged through the ring so that every store writes whole rows.
+// A general kernel (any K % 16 == 0) stages operands through registers.
 //
 // MFMA roles.  The weight tile is the MFMA "A" operand (its rows index n)
 // and the activation tile is "B" (its columns index m), so each lane ends up
-// holding four consecutive n of one m per 4-register group: the epilogue
-// stores 4 BF16 (8 bytes) or 4 INT32 (16 bytes) per instruction.  A lane
-// feeds row (lane % 32) of either operand with the 16 bytes of K-group
-// (lane / 32); both operands use the same byte order, so the dot product is
-// exact whatever order the hardware assigns within a K-group.
+// holding four consecutive n of one m per 4-register group.  A lane feeds
+// row (lane % 32) of either operand with the 16 bytes of K-group (lane / 32);
+// both operands use the same byte order, so the dot product is exact
+// whatever order the hardware assigns within a K-group.
 //
 // LDS layout.  Each operand stage is [256 rows][64 bytes]; the four 16-byte
 // chunks of row r are stored XOR-swizzled by ((r >> 1) ^ (r >> 2)) & 3 so
@@ -98,6 +100,25 @@ __device__ __forceinline__ void store_bf16x4(const int32_t* a4, float sx, int n,
             dst[e] = (uint16_t)(pack_bf16x2(tt, 0.0f) & 0xFFFFu);
         }
     }
+}
+
+// Four outputs bf16_rne(((float)acc_e * sx) * sw_e + b_e) packed as BF16 pairs.
+__device__ __forceinline__ u32x2 epi_bf16x4(const int32_t* a4, float sx, const f32x4& sw, const u32x2& bb,
+                                            bool has_bias) {
+#pragma clang fp contract(off)
+    const float b[4] = {bits_f(bb[0] << 16), bits_f(bb[0] & 0xFFFF0000u), bits_f(bb[1] << 16),
+                        bits_f(bb[1] & 0xFFFF0000u)};
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float tt = (float)a4[e];
+        tt = tt * sx;
+        tt = tt * sw[e];
+        if (has_bias) tt = tt + b[e];
+        o[e] = tt;
+    }
+    u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    return pk;
 }
 
 __device__ __forceinline__ void store_i32x4(const int32_t* a4, int n, int N, int64_t m,
@@ -251,12 +272,289 @@ __global__ __launch_bounds__(NT, 1) void gemm_i8_kernel(const int8_t* __restrict
     }
 }
 
+constexpr int STAGE = (BM + BN) * BK;   // 32 KB per stage
+
+typedef __attribute__((address_space(3))) int8_t lds_i8;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_i8*)p;
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// wait until at most `groups` slices' copies (4 per thread each) are in flight
+__device__ __forceinline__ void wait_groups4(int groups) {
+    switch (groups) {
+        case 0:
+        case -1: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<4>(); break;
+        case 2: wait_vmcnt<8>(); break;
+        default: wait_vmcnt<12>(); break;
+    }
+}
+
+__device__ __forceinline__ void dma16(uint32_t lds, const int8_t* src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Main kernel (K % 64 == 0).  Per K slice t a wave
+//   1. issues the LDS reads of slice t's second K half and the MFMAs of the
+//      first half (operands already in registers), plus its two weight-row
+//      copies of slice t+NS-1, one per four MFMAs;
+//   2. drains its LDS reads, waits until its own copies of slice t+1 have
+//      landed, and meets the other waves at one barrier: after it slice t+1
+//      is visible to all and nobody reads stage t any more;
+//   3. issues the LDS reads of slice t+1's first half and the MFMAs of slice
+//      t's second half, plus its two activation-row copies of slice t+NS
+//      into stage t.
+// The copies are issued from inline assembly so that the compiler does not
+// drain them at every barrier; their completion is awaited explicitly with
+// s_waitcnt vmcnt.  Each copy instruction moves 1 KB (64 lanes x 16 B) into
+// consecutive LDS bytes: 16 rows of 64 bytes, a lane fetching the chunk that
+// belongs at its swizzled slot.  Rows past M or N re-read the last valid row
+// (their outputs are never stored).  The tile's row scales, column scales
+// and bias are copied into LDS above the ring during the prologue.
+constexpr int NT8 = 512;
+constexpr int EPI_LDS = 4 * 1024;   // sx[256] f32, sw[256] f32, bias[256] bf16 (+pad)
+
+template <int MODE, int NS>
+__global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __restrict__ A, int64_t lda,
+                                                           const int8_t* __restrict__ W, int64_t ldw,
+                                                           int M, int N, int K, EpiArgs ep) {
+    static_assert(NS * STAGE >= 256 * 512, "the output tile is staged in the ring");
+    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE + EPI_LDS];
+    float* l_sx = reinterpret_cast<float*>(smem + NS * STAGE);
+    float* l_sw = l_sx + 256;
+    uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + 256);
+
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int T = tiles_m * tiles_n;
+    const int g = blockIdx.x;
+    const int xcd = g % NXCD;
+    const int q8 = T / NXCD, rem = T % NXCD;
+    const int t_lin = xcd * q8 + min(xcd, rem) + g / NXCD;
+    const int per_group = GROUP_M * tiles_n;
+    const int group = t_lin / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsz = min(tiles_m - first_m, GROUP_M);
+    const int tg = t_lin - group * per_group;
+    const int m0 = (first_m + tg % gsz) * BM;
+    const int n0 = (tg / gsz) * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1;    // 128-row half of the activation tile
+    const int wn = wave >> 1;   // 64-row quarter of the weight tile
+
+    // epilogue operands of the tile -> LDS (plain loads, consumed after the K loop)
+    if (MODE == MODE_BF16) {
+        if (tid < 256) {
+            const int m = min(m0 + tid, M - 1);
+            l_sx[tid] = ep.a_scale[m];
+        } else {
+            const int c = tid - 256;
+            const int n = min(n0 + c, N - 1);
+            l_sw[c] = ep.w_scale[n];
+            l_b[c] = ep.bias ? ep.bias[n] : (uint16_t)0;
+        }
+    }
+
+    // copies: instruction i (0, 1) of this wave covers rows 16 * (wave + 8 i) + lane / 4
+    const int8_t* ga[2];
+    const int8_t* gw[2];
+    uint32_t lrow[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int rt = 16 * (wave + 8 * i) + (lane >> 2);
+        const int c = (lane & 3) ^ swz(rt);
+        ga[i] = A + (int64_t)min(m0 + rt, M - 1) * lda + c * 16;
+        gw[i] = W + (int64_t)min(n0 + rt, N - 1) * ldw + c * 16;
+        lrow[i] = (uint32_t)(16 * (wave + 8 * i) * BK);
+    }
+    const uint32_t lds0 = lds_addr(smem);
+    auto copy_part = [&](int u, int part, int i) {
+        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STAGE) + (part ? BM * BK : 0);
+        dma16(sb + lrow[i], (part ? gw[i] : ga[i]) + (int64_t)u * BK);
+    };
+    auto issue = [&](int u) {
+        copy_part(u, 0, 0);
+        copy_part(u, 0, 1);
+        copy_part(u, 1, 0);
+        copy_part(u, 1, 1);
+    };
+
+    const int fr = lane & 31;
+    const int fk = lane >> 5;
+    int a_off[4][2], w_off[2][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int ra_row = wm * 128 + b * 32 + fr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) a_off[b][kk] = ra_row * BK + (((2 * kk + fk) ^ swz(ra_row)) << 4);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int rw_row = wn * 64 + b * 32 + fr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) w_off[b][kk] = BM * BK + rw_row * BK + (((2 * kk + fk) ^ swz(rw_row)) << 4);
+    }
+    auto rd_a = [&](int u, int kk, int b, i32x4* fa) {
+        fa[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STAGE + a_off[b][kk]);
+    };
+    auto rd_w = [&](int u, int kk, int b, i32x4* fw) {
+        fw[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STAGE + w_off[b][kk]);
+    };
+
+    i32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+    const int nk = K / BK;
+    // slices 0 .. NS-2 in flight (4 copies per slice per thread), wait for slice 0
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+        if (u < nk) issue(u);
+    wait_groups4(min(nk, NS - 1) - 1);
+    __syncthreads();   // slice 0 and the epilogue operands are visible
+    if (NS - 1 < nk) {
+        copy_part(NS - 1, 0, 0);
+        copy_part(NS - 1, 0, 1);
+    }
+
+    i32x4 a0[4], w0[2], a1[4], w1[2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) rd_a(0, 0, b, a0);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) rd_w(0, 0, b, w0);
+    for (int t = 0; t < nk; ++t) {
+        const bool late = t + NS - 1 < nk;
+        // first half of slice t; reads of its second half; weight-row copies of slice t+NS-1
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            rd_w(t, 1, q, w1);
+            rd_a(t, 1, 2 * q, a1);
+            rd_a(t, 1, 2 * q + 1, a1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[q][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0[q], a0[j], acc[q][j], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (late) copy_part(t + NS - 1, 1, q);
+        }
+        acc[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[0], a1[0], acc[0][0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        wait_groups4(min(nk - 1, t + NS - 1) - (t + 1));
+        __builtin_amdgcn_s_barrier();
+        const bool early = t + NS < nk;
+        // second half of slice t; reads of slice t+1's first half; activation-row copies of slice t+NS
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            rd_w(t + 1, 0, q, w0);
+            rd_a(t + 1, 0, 2 * q, a0);
+            rd_a(t + 1, 0, 2 * q + 1, a0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (q != 0 || j > 0)
+                    acc[q][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[q], a1[j], acc[q][j], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (early) copy_part(t + NS, 0, q);
+        }
+    }
+
+    if (MODE == MODE_BF16) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        // acc[i][j][4 g4 + e]: (n, m) = (wn*64 + 32 i + 8 g4 + 4 fk + e, wm*128 + 32 j + fr) in the tile
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = wm * 128 + 32 * j + fr;
+            const float sx = l_sx[r];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c = wn * 64 + 32 * i + 8 * g4 + 4 * fk;
+                    const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
+                    const u32x2 bb = *reinterpret_cast<const u32x2*>(l_b + c);
+                    const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                           acc[i][j][4 * g4 + 3]};
+                    const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
+                    const int off = r * 512 + (((c >> 3) ^ (r & 31)) << 4) + ((c & 7) << 1);
+                    *reinterpret_cast<u32x2*>(smem + off) = pk;
+                }
+            }
+        }
+        __syncthreads();
+        uint16_t* out = static_cast<uint16_t*>(ep.out);
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int q = it * NT8 + tid;
+            const int r = q >> 5, c = q & 31;
+            const int m = m0 + r;
+            const int n = n0 + c * 8;
+            if (m >= M || n >= N) continue;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
+            uint16_t* dst = out + (int64_t)m * ep.ldo + n;
+            if (n + 7 < N) {
+                *reinterpret_cast<u32x4*>(dst) = v;
+            } else {
+                for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + wm * 128 + 32 * j + fr;
+            if (m >= M) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = n0 + wn * 64 + 32 * i + 8 * g4 + 4 * fk;
+                    if (n >= N) continue;
+                    const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                           acc[i][j][4 * g4 + 3]};
+                    store_i32x4(a4, n, N, m, ep);
+                }
+            }
+        }
+    }
+}
+
 template <int MODE>
 hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, int64_t M,
                   int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_i8_kernel<MODE><<<dim3((unsigned)tiles), dim3(NT), 0, stream>>>(aq, lda, wq, ldw, (int)M,
-                                                                        (int)N, (int)K, ep);
+    if (K % BK == 0)
+        gemm_i8_w8_kernel<MODE, 4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(aq, lda, wq, ldw, (int)M,
+                                                                                (int)N, (int)K, ep);
+    else
+        gemm_i8_kernel<MODE><<<dim3((unsigned)tiles), dim3(NT), 0, stream>>>(aq, lda, wq, ldw, (int)M,
+                                                                            (int)N, (int)K, ep);
     return hipGetLastError();
 }
 
