@@ -73,13 +73,16 @@ def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float
 
     import oracle
     O = oracle.default()
+    int4 = w.kind == "w4a4"
     wq = wq_dev.cpu().numpy()
+    if int4:
+        wq = O.unpack_int4(wq, w.K)     # packed weights -> INT4 codes in INT8 storage
     sw = sw_dev.cpu().numpy()
 
     def run(rows):
         x = x_dev[:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        y = O.linear(x, wq, sw, b_bits)
+        y = O.linear(x, wq, sw, b_bits, qmax=7 if int4 else 127)
         return time.perf_counter() - t0, y
 
     t_small, _ = run(16)
@@ -99,7 +102,8 @@ def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float
         "unit": "TOP/s",
         "cores": O.num_threads(),
         "kind": "oracle",
-        "sample": f"leading {rows} of {w.M} rows, full N={w.N}, K={w.K} (rotate+quantize, exact INT32 GEMM, epilogue)",
+        "sample": f"leading {rows} of {w.M} rows, full N={w.N}, K={w.K} (rotate+quantize, exact INT32 GEMM, epilogue)"
+                  + (" on unpacked INT4 codes" if int4 else ""),
         "seconds": round(t, 3),
         "sample_parity": {"rows": rows, "outputs": int(y_or.size), "not_bit_identical": int((~same).sum()),
                           "within_1_bf16_ulp": within},
@@ -149,8 +153,7 @@ def main():
         sys.exit("bench.py needs a GPU")
     qd.lib()
     w = workload(args.workload)
-    if w.kind != "w8a8":
-        sys.exit(f"workload {w.cid} is {w.kind}; bench.py measures the INT8 linear")
+    int4 = w.kind == "w4a4"
     M, K, N = w.M, w.K, w.N
     dev = torch.device("cuda:0")
     log(f"[bench] {w.name}: generating inputs")
@@ -162,14 +165,18 @@ def main():
         Wf[r0:r1].copy_(torch.from_numpy(chunk))
     b_bits = make_bias(w)
     bias = torch.from_numpy(b_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    wq, sw = qd.prepare_weights(Wf)          # offline weight preparation (not timed)
+    # offline weight preparation (not timed)
+    wq, sw = qd.prepare_weights_w4a4(Wf) if int4 else qd.prepare_weights(Wf)
     del Wf
     ws = torch.empty(qd.workspace_size(M, K), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     def step():
-        qd.int8_linear(x, wq, sw, bias, 256, ws, y)
+        if int4:
+            qd.convrot_w4a4_linear(x, wq, sw, bias, 256, ws, y)
+        else:
+            qd.int8_linear(x, wq, sw, bias, 256, ws, y)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -194,15 +201,20 @@ def main():
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     y2 = torch.empty_like(y)
     reps = max(5, args.steps)
-    ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
-    ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+    if int4:
+        ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_int4(x, 256, aq, sx), reps, torch)
+        ms_g = time_launches(lambda: qd.int4_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+    else:
+        ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
+        ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     same = bool(torch.equal(y2, y))
     q_bytes = 3.0 * M * K + 4.0 * M
-    g_min_bytes = float(M * K + N * K + 2 * M * N + 4 * M + 4 * N + 2 * N)
+    g_min_bytes = float(M * K + (N * K // 2 if int4 else N * K) + 2 * M * N + 4 * M + 4 * N + 2 * N)
     gemm_tops = ops / (ms_g * 1e-3) / 1e12
     traffic = load_traffic(w.name)
     out = {
-        "metric": f"INT8 linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}",
+        "metric": (f"W4A4 rotated linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}" if int4 else
+                   f"INT8 linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}"),
         "value": round(tops, 3),
         "unit": "TOP/s",
         "n_gpus": 1,
@@ -212,13 +224,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tops / (ops / (PAGE_MS[w.cid] * 1e-3) / 1e12), 4) if w.cid in PAGE_MS else None,
-        "dtype": "i8",
+        "dtype": "i4 codes on i8 MFMA" if int4 else "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "rotation": "block-256 Walsh-Hadamard",
-                   "activations": "bf16", "weights": "int8 per-channel fp32 scale", "bias": "bf16",
-                   "output": "bf16", "parallelism": "single GPU"},
+                   "activations": "bf16 -> int4 codes in int8 storage" if int4 else "bf16",
+                   "weights": ("packed int4 per-channel fp32 scale, unpacked to int8 in the GEMM" if int4
+                               else "int8 per-channel fp32 scale"),
+                   "bias": "bf16", "output": "bf16", "parallelism": "single GPU"},
         "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_i8_kernel (fused bf16 epilogue)",
+        "roofline": {"bound": "mfma", "kernel": ("gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4>" if int4 else
+                                                 "gemm_i8_w8_kernel<MODE_BF16, 4, WF_I8>") + " (fused bf16 epilogue)",
                      "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic},

@@ -181,6 +181,50 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
                              const int8_t* wq, int64_t N, int64_t ldw, int32_t* acc,
                              int64_t ldc, hipStream_t stream);
 
+/*
+ * INT4 storage for convrot_w4a4_linear (comfy-kitchen 0.2.40, "Huawei Ascend
+ * backend": signed INT4 activation codes kept in INT8 storage, packed INT4
+ * weights unpacked to INT8 for INT32 accumulation).
+ *
+ * qd_pack_int4: packed[r, i] = (q[r, 2i] & 15) | (q[r, 2i+1] & 15) << 4 for
+ * codes in [-8, 7] (two's complement nibbles, code 2i in the low nibble).
+ *   q [R, K] INT8 (row stride ldq bytes), packed [R, K/2] (row stride ldp
+ *   bytes).  Requires K % 32 == 0, q/packed 16-byte aligned, ldq and ldp
+ *   multiples of 16, ldp >= K/2.
+ */
+qd_status_t qd_pack_int4(const int8_t* q, int64_t R, int64_t K, int64_t ldq, uint8_t* packed,
+                         int64_t ldp, hipStream_t stream);
+
+/*
+ * The GEMM half of convrot_w4a4_linear: as qd_int8_scaled_mm with the weights
+ * given as packed INT4 w_packed [N, K/2] (row stride ldw BYTES), unpacked to
+ * INT8 inside the kernel.  Requires K % 64 == 0, ldw a multiple of 16 and
+ * >= K/2, otherwise as qd_int8_scaled_mm.
+ */
+qd_status_t qd_int4_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                              const float* a_scale, const uint8_t* w_packed, int64_t N, int64_t ldw,
+                              const float* w_scale, const void* bias_bf16, void* y_bf16,
+                              int64_t ldy, hipStream_t stream);
+
+/* Raw INT32 accumulators of the packed-INT4 GEMM (verification). */
+qd_status_t qd_int4_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                             const uint8_t* w_packed, int64_t N, int64_t ldw, int32_t* acc,
+                             int64_t ldc, hipStream_t stream);
+
+/*
+ * convrot_w4a4_linear: y = x W^T + b through the rotated INT4 path.  x is
+ * rotated (block 256) and quantized per row to INT4 codes in INT8 storage
+ * (s = amax / 7); w_packed [N, K/2] / w_scale [N] come from
+ * qd_quantize_and_rotate_rowwise_int4 on W followed by qd_pack_int4.
+ * rotate_block must be 256; K % 256 == 0.  Workspace as qd_int8_linear
+ * (qd_int8_linear_workspace_size).  Two kernels: quantizer, then GEMM.
+ */
+qd_status_t qd_convrot_w4a4_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                   int64_t ldx, const uint8_t* w_packed, int64_t N, int64_t ldw,
+                                   const float* w_scale, const void* bias_bf16,
+                                   int32_t rotate_block, void* workspace, size_t workspace_bytes,
+                                   void* y_bf16, int64_t ldy, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,9 @@ plus
   int8_scaled_mm(aq, a_scale, wq, w_scale, bias) -> bf16 (GEMM half of int8_linear)
   int8_gemm_i32(aq, wq)                 -> raw int32 accumulators
   quantize_and_rotate_rowwise_int4(x)   -> INT4 codes in int8 storage
+  pack_int4(q), prepare_weights_w4a4(W) -> packed INT4 weights (two per byte)
+  convrot_w4a4_linear(x, wp, w_scale, bias) -> bf16 y through the rotated INT4 path
+  int4_scaled_mm / int4_gemm_i32        -> the packed-INT4 GEMM alone
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ import os
 __all__ = [
     "LIB_PATH", "QDiffError", "lib", "quantize_and_rotate_rowwise", "quantize_and_rotate_rowwise_int4",
     "quantize_int8_rowwise", "int8_linear", "int8_scaled_mm", "int8_gemm_i32", "dequantize_int8",
-    "prepare_weights", "workspace_size", "EXPORTED_SYMBOLS",
+    "prepare_weights", "workspace_size", "EXPORTED_SYMBOLS", "pack_int4", "prepare_weights_w4a4",
+    "int4_scaled_mm", "int4_gemm_i32", "convrot_w4a4_linear",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -38,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "qd_last_error", "qd_version", "qd_quantize_and_rotate_rowwise",
     "qd_quantize_and_rotate_rowwise_int4", "qd_quantize_int8_rowwise", "qd_int8_scaled_mm",
     "qd_int8_linear_workspace_size", "qd_int8_linear", "qd_dequantize_int8", "qd_int8_gemm_i32",
+    "qd_pack_int4", "qd_int4_scaled_mm", "qd_int4_gemm_i32", "qd_convrot_w4a4_linear",
 )
 
 
@@ -78,6 +83,14 @@ def lib():
         L.qd_dequantize_int8.argtypes = [P, I64, I64, I64, P, I32, St, P, I64, P]
         L.qd_int8_gemm_i32.restype = St
         L.qd_int8_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
+        L.qd_pack_int4.restype = St
+        L.qd_pack_int4.argtypes = [P, I64, I64, I64, P, I64, P]
+        L.qd_int4_scaled_mm.restype = St
+        L.qd_int4_scaled_mm.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, I64, P]
+        L.qd_int4_gemm_i32.restype = St
+        L.qd_int4_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
+        L.qd_convrot_w4a4_linear.restype = St
+        L.qd_convrot_w4a4_linear.argtypes = [P, St, I64, I64, I64, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
         _lib = L
     return _lib
 
@@ -131,6 +144,13 @@ def _stream(dev):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _bf16_out(M, N, dev):
+    """BF16 [M, N] output whose row stride is a multiple of 8 elements (the
+    GEMM stores 16 bytes at a time)."""
+    torch = _torch()
+    return torch.empty((M, (N + 7) // 8 * 8), dtype=torch.bfloat16, device=dev)[:, :N]
 
 
 def _rows_vec(t, n, dtype, name):
@@ -204,7 +224,7 @@ def int8_scaled_mm(aq, a_scale, wq, w_scale, bias=None, out=None):
     if bias is not None:
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out = _bf16_out(M, N, dev)
     _mat(out, "out")
     _check(lib().qd_int8_scaled_mm(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(wq), N, wq.stride(0),
                                    _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
@@ -251,7 +271,7 @@ def int8_linear(x, wq, w_scale, bias=None, rotate_block: int = 256, workspace=No
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out = _bf16_out(M, N, dev)
     _mat(out, "out")
     _check(lib().qd_int8_linear(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(wq), N, wq.stride(0),
                                 _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
@@ -277,4 +297,93 @@ def dequantize_int8(q, scale, out_dtype=None, out=None):
     _mat(out, "out")
     _check(lib().qd_dequantize_int8(_ptr(q), M, K, q.stride(0), _ptr(scale), int(per_row),
                                     _dtype_code(out), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+# ------------------------------------------------------------ W4A4 (INT4) path
+
+def pack_int4(q, out=None):
+    """Pack INT4 codes (int8 storage, values in [-8, 7]) two per byte along K:
+    byte i = (q[2i] & 15) | (q[2i+1] & 15) << 4.  Returns uint8 [R, K/2]."""
+    torch = _torch()
+    _mat(q, "q")
+    dev = _dev(q, out)
+    R, K = q.shape
+    if out is None:
+        ldp = (K // 2 + 15) // 16 * 16
+        out = torch.empty((R, ldp), dtype=torch.uint8, device=dev)[:, : K // 2]
+    _mat(out, "packed")
+    _check(lib().qd_pack_int4(_ptr(q), R, K, q.stride(0), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def prepare_weights_w4a4(w, block: int = 256):
+    """Offline weight preparation for convrot_w4a4_linear: rotate FP32 W [N, K]
+    along K, quantize per output channel to INT4 (s = amax/7), pack two codes
+    per byte.  Returns (packed uint8 [N, K/2], w_scale fp32 [N])."""
+    q, s = quantize_and_rotate_rowwise_int4(w, block)
+    return pack_int4(q), s
+
+
+def _w4_common(aq, wp, name):
+    _mat(aq, "aq"), _mat(wp, name)
+    M, K = aq.shape
+    N = wp.shape[0]
+    if wp.shape[1] * 2 != K:
+        raise ValueError(f"{name} must be [N, K/2] packed bytes for K={K}")
+    return M, K, N
+
+
+def int4_scaled_mm(aq, a_scale, wp, w_scale, bias=None, out=None):
+    """y = bf16(((float)(aq . unpack(wp)^T) * a_scale[m]) * w_scale[n] + bias[n])."""
+    torch = _torch()
+    M, K, N = _w4_common(aq, wp, "wp")
+    dev = _dev(aq, a_scale, wp, w_scale, bias, out)
+    _rows_vec(a_scale, M, torch.float32, "a_scale")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_int4_scaled_mm(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(wp), N, wp.stride(0),
+                                   _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def int4_gemm_i32(aq, wp, out=None):
+    """Raw int32 accumulators aq . unpack(wp)^T of the packed-INT4 GEMM kernel."""
+    torch = _torch()
+    M, K, N = _w4_common(aq, wp, "wp")
+    dev = _dev(aq, wp, out)
+    if out is None:
+        out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
+    _mat(out, "out")
+    _check(lib().qd_int4_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wp), N, wp.stride(0), _ptr(out),
+                                  out.stride(0), _stream(dev)))
+    return out
+
+
+def convrot_w4a4_linear(x, wp, w_scale, bias=None, rotate_block: int = 256, workspace=None, out=None):
+    """y = x W^T + b through the rotated INT4 path (quantizer to INT4 codes in
+    int8 storage, then the packed-INT4 GEMM with the fused epilogue)."""
+    torch = _torch()
+    _mat(x, "x"), _mat(wp, "wp")
+    dev = _dev(x, wp, w_scale, bias, workspace, out)
+    M, K = x.shape
+    N = wp.shape[0]
+    if wp.shape[1] * 2 != K:
+        raise ValueError("wp must be [N, K/2] packed bytes")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_convrot_w4a4_linear(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(wp), N, wp.stride(0),
+                                        _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
+                                        _stream(dev)))
     return out

@@ -208,4 +208,87 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
     return hip_status(fn, qd::launch_gemm_i32(aq, lda, wq, ldw, acc, ldc, M, N, K, stream));
 }
 
+qd_status_t qd_pack_int4(const int8_t* q, int64_t R, int64_t K, int64_t ldq, uint8_t* packed,
+                         int64_t ldp, hipStream_t stream) {
+    const char* fn = "qd_pack_int4";
+    if (R < 0 || K <= 0) return fail(QD_EINVAL, fn, "need R >= 0 and K > 0");
+    if (R > 0 && (!q || !packed)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (ldq < K || ldp < K / 2) return fail(QD_EINVAL, fn, "ldq must be >= K and ldp >= K/2");
+    if (K % 32 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 32", (long long)K);
+    if (R > 0 && (!aligned16(q) || !aligned16(packed))) return fail(QD_EUNSUPPORTED, fn, "q and packed must be 16-byte aligned");
+    if (ldq % 16 != 0 || ldp % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "ldq and ldp must be multiples of 16");
+    if (R == 0) return ok();
+    return hip_status(fn, qd::launch_pack_int4(q, ldq, packed, ldp, R, K, stream));
+}
+
+namespace {
+qd_status_t check_w4(const char* fn, int64_t K, int64_t ldw, int64_t N) {
+    if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 64 for packed INT4 weights", (long long)K);
+    if (ldw < K / 2) return fail(QD_EINVAL, fn, "ldw (%lld bytes) < K/2", (long long)ldw);
+    if (ldw % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "ldw must be a multiple of 16 bytes");
+    (void)N;
+    return QD_OK;
+}
+}  // namespace
+
+qd_status_t qd_int4_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                              const float* a_scale, const uint8_t* w_packed, int64_t N, int64_t ldw,
+                              const float* w_scale, const void* bias_bf16, void* y_bf16,
+                              int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_int4_scaled_mm";
+    // validate as an INT8 GEMM with a K-byte weight stride, then the packed layout
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, reinterpret_cast<const int8_t*>(w_packed), N, K, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if ((st = check_w4(fn, K, ldw, N)) != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    return hip_status(fn, qd::launch_gemm_w4_bf16(aq, lda, a_scale, w_packed, ldw, w_scale, bias_bf16, y_bf16,
+                                                  ldy, M, N, K, stream));
+}
+
+qd_status_t qd_int4_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                             const uint8_t* w_packed, int64_t N, int64_t ldw, int32_t* acc,
+                             int64_t ldc, hipStream_t stream) {
+    const char* fn = "qd_int4_gemm_i32";
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, reinterpret_cast<const int8_t*>(w_packed), N, K, acc, ldc, 4);
+    if (st != QD_OK) return st;
+    if ((st = check_w4(fn, K, ldw, N)) != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    return hip_status(fn, qd::launch_gemm_w4_i32(aq, lda, w_packed, ldw, acc, ldc, M, N, K, stream));
+}
+
+qd_status_t qd_convrot_w4a4_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                   int64_t ldx, const uint8_t* w_packed, int64_t N, int64_t ldw,
+                                   const float* w_scale, const void* bias_bf16,
+                                   int32_t rotate_block, void* workspace, size_t workspace_bytes,
+                                   void* y_bf16, int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_convrot_w4a4_linear";
+    if (rotate_block != 256) return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 256 (got %d)", rotate_block);
+    if (M < 0 || N < 0 || K <= 0)
+        return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    const int64_t ldq = (int64_t)round_up((size_t)K, 16);
+    if (!workspace) return fail(QD_EINVAL, fn, "null workspace");
+    if ((uintptr_t)workspace % kAlign) return fail(QD_EUNSUPPORTED, fn, "workspace must be 256-byte aligned");
+    if (workspace_bytes < qd_int8_linear_workspace_size(M, K))
+        return fail(QD_EINVAL, fn, "workspace too small: %zu < %zu bytes", workspace_bytes,
+                    qd_int8_linear_workspace_size(M, K));
+    int8_t* aq = static_cast<int8_t*>(workspace);
+    float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_codes_bytes(M, K));
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, true, rotate_block, aq, ldq, sx);
+    if (st != QD_OK) return st;
+    st = check_gemm(fn, aq, M, K, ldq, reinterpret_cast<const int8_t*>(w_packed), N, K, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if ((st = check_w4(fn, K, ldw, N)) != QD_OK) return st;
+    if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, true, 7, M, K, ldx, aq, ldq, sx, stream);
+    if (e != hipSuccess) return hip_status(fn, e);
+    return hip_status(fn, qd::launch_gemm_w4_bf16(aq, ldq, sx, w_packed, ldw, w_scale, bias_bf16, y_bf16,
+                                                  ldy, M, N, K, stream));
+}
+
 }  // extern "C"

@@ -48,7 +48,39 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int8_t* __restrict__
     }
 }
 
+// Two signed INT4 codes per byte, code 2i in the low nibble of byte i (the
+// layout convrot_w4a4_linear's packed weights use); one thread packs 32 codes.
+__global__ __launch_bounds__(256) void pack_int4_kernel(const int8_t* __restrict__ q, int64_t ldq,
+                                                        uint8_t* __restrict__ out, int64_t ldo, int64_t R,
+                                                        int64_t chunks_per_row) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= R * chunks_per_row) return;
+    const int64_t r = idx / chunks_per_row;
+    const int64_t c = idx - r * chunks_per_row;
+    const int8_t* src = q + r * ldq + c * 32;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(src);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(src + 16);
+    const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t t = w[i] & 0x0F0F0F0Fu;    // low nibbles of codes 4i .. 4i+3
+        const uint32_t u = t | (t >> 4);          // byte 0: c0 | c1 << 4, byte 2: c2 | c3 << 4
+        h[i] = (u & 0xFFu) | ((u >> 8) & 0xFF00u);
+    }
+    u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    *reinterpret_cast<u32x4*>(out + r * ldo + c * 16) = o;
+}
+
 }  // namespace
+
+hipError_t launch_pack_int4(const int8_t* q, int64_t ldq, uint8_t* out, int64_t ldo, int64_t R, int64_t K,
+                            hipStream_t stream) {
+    const int64_t cpr = K / 32;
+    const int64_t grid = (R * cpr + 255) / 256;
+    pack_int4_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(q, ldq, out, ldo, R, cpr);
+    return hipGetLastError();
+}
 
 hipError_t launch_dequant(const int8_t* q, int64_t ldq, const float* scale, bool per_row,
                           bool out_bf16, void* out, int64_t ldo, int64_t M, int64_t K,

@@ -287,15 +287,33 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// wait until at most `groups` slices' copies (4 per thread each) are in flight
-__device__ __forceinline__ void wait_groups4(int groups) {
+// wait until at most `groups` slices' copies (PER per thread each) are in flight
+template <int PER>
+__device__ __forceinline__ void wait_groups(int groups) {
     switch (groups) {
         case 0:
         case -1: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<4>(); break;
-        case 2: wait_vmcnt<8>(); break;
-        default: wait_vmcnt<12>(); break;
+        case 1: wait_vmcnt<PER>(); break;
+        case 2: wait_vmcnt<2 * PER>(); break;
+        default: wait_vmcnt<3 * PER>(); break;
     }
+}
+
+// 16 signed INT4 codes packed two per byte (code 2i in the low nibble of
+// byte i) -> 16 INT8 bytes in code order.  Byte-wise sign extension of a
+// nibble v: ((v ^ 8) + 0x78) ^ 0x80, which never carries across bytes.
+__device__ __forceinline__ i32x4 unpack_int4x16(const u32x2& p) {
+    i32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        uint32_t lo = p[h] & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6 of this word
+        uint32_t hi = (p[h] >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+        lo = ((lo ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+        hi = ((hi ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+        r[2 * h] = (int32_t)__builtin_amdgcn_perm(hi, lo, 0x05010400u);
+        r[2 * h + 1] = (int32_t)__builtin_amdgcn_perm(hi, lo, 0x07030602u);
+    }
+    return r;
 }
 
 __device__ __forceinline__ void dma16(uint32_t lds, const int8_t* src) {
@@ -323,13 +341,21 @@ __device__ __forceinline__ void dma16(uint32_t lds, const int8_t* src) {
 constexpr int NT8 = 512;
 constexpr int EPI_LDS = 4 * 1024;   // sx[256] f32, sw[256] f32, bias[256] bf16 (+pad)
 
-template <int MODE, int NS>
+enum { WF_I8 = 0, WF_I4 = 1 };   // weight operand: INT8, or INT4 packed two per byte
+
+// packed-INT4 weight stage: [256 rows][32 bytes], 16-byte chunk c of row r at c ^ ((r >> 3) & 1)
+__device__ __forceinline__ int swz4(int row) { return (row >> 3) & 1; }
+
+template <int MODE, int NS, int WF>
 __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __restrict__ A, int64_t lda,
                                                            const int8_t* __restrict__ W, int64_t ldw,
                                                            int M, int N, int K, EpiArgs ep) {
-    static_assert(NS * STAGE >= 256 * 512, "the output tile is staged in the ring");
-    __shared__ __attribute__((aligned(1024))) int8_t smem[NS * STAGE + EPI_LDS];
-    float* l_sx = reinterpret_cast<float*>(smem + NS * STAGE);
+    constexpr int WROW = WF == WF_I4 ? BK / 2 : BK;          // weight bytes per row per slice
+    constexpr int STG = BM * BK + BN * WROW;                 // bytes per stage
+    constexpr int PER = WF == WF_I4 ? 3 : 4;                 // copies per slice per thread
+    constexpr int RING = NS * STG > 256 * 512 ? NS * STG : 256 * 512;   // the output tile is staged here too
+    __shared__ __attribute__((aligned(1024))) int8_t smem[RING + EPI_LDS];
+    float* l_sx = reinterpret_cast<float*>(smem + RING);
     float* l_sw = l_sx + 256;
     uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + 256);
 
@@ -367,22 +393,33 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
         }
     }
 
-    // copies: instruction i (0, 1) of this wave covers rows 16 * (wave + 8 i) + lane / 4
+    // copies: activation instruction i (0, 1) of this wave covers rows
+    // 16 * (wave + 8 i) + lane / 4; INT8 weights likewise; packed INT4 weights
+    // take one instruction per wave for rows 32 * wave + lane / 2
     const int8_t* ga[2];
     const int8_t* gw[2];
-    uint32_t lrow[2];
+    uint32_t lrow[2], lwrow[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int rt = 16 * (wave + 8 * i) + (lane >> 2);
         const int c = (lane & 3) ^ swz(rt);
         ga[i] = A + (int64_t)min(m0 + rt, M - 1) * lda + c * 16;
-        gw[i] = W + (int64_t)min(n0 + rt, N - 1) * ldw + c * 16;
         lrow[i] = (uint32_t)(16 * (wave + 8 * i) * BK);
+        if (WF == WF_I8) {
+            gw[i] = W + (int64_t)min(n0 + rt, N - 1) * ldw + c * 16;
+            lwrow[i] = lrow[i];
+        } else {
+            const int rw = 32 * wave + (lane >> 1);
+            const int cw = (lane & 1) ^ swz4(rw);
+            gw[i] = W + (int64_t)min(n0 + rw, N - 1) * ldw + cw * 16;
+            lwrow[i] = (uint32_t)(32 * wave * WROW);
+        }
     }
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
-        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STAGE) + (part ? BM * BK : 0);
-        dma16(sb + lrow[i], (part ? gw[i] : ga[i]) + (int64_t)u * BK);
+        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
+        if (part == 0) dma16(sb + lrow[i], ga[i] + (int64_t)u * BK);
+        else if (WF == WF_I8 || i == 0) dma16(sb + BM * BK + lwrow[i], gw[i] + (int64_t)u * WROW);
     };
     auto issue = [&](int u) {
         copy_part(u, 0, 0);
@@ -404,13 +441,19 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     for (int b = 0; b < 2; ++b) {
         const int rw_row = wn * 64 + b * 32 + fr;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) w_off[b][kk] = BM * BK + rw_row * BK + (((2 * kk + fk) ^ swz(rw_row)) << 4);
+        for (int kk = 0; kk < 2; ++kk) {
+            if (WF == WF_I8)
+                w_off[b][kk] = BM * BK + rw_row * BK + (((2 * kk + fk) ^ swz(rw_row)) << 4);
+            else   // 16 codes = 8 packed bytes: chunk kk, half fk
+                w_off[b][kk] = BM * BK + rw_row * WROW + ((kk ^ swz4(rw_row)) << 4) + (fk << 3);
+        }
     }
     auto rd_a = [&](int u, int kk, int b, i32x4* fa) {
-        fa[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STAGE + a_off[b][kk]);
+        fa[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STG + a_off[b][kk]);
     };
     auto rd_w = [&](int u, int kk, int b, i32x4* fw) {
-        fw[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STAGE + w_off[b][kk]);
+        if (WF == WF_I8) fw[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STG + w_off[b][kk]);
+        else fw[b] = unpack_int4x16(*reinterpret_cast<const u32x2*>(smem + (u % NS) * STG + w_off[b][kk]));
     };
 
     i32x16 acc[2][4];
@@ -426,7 +469,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
         if (u < nk) issue(u);
-    wait_groups4(min(nk, NS - 1) - 1);
+    wait_groups<PER>(min(nk, NS - 1) - 1);
     __syncthreads();   // slice 0 and the epilogue operands are visible
     if (NS - 1 < nk) {
         copy_part(NS - 1, 0, 0);
@@ -461,7 +504,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
         acc[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[0], a1[0], acc[0][0], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        wait_groups4(min(nk - 1, t + NS - 1) - (t + 1));
+        wait_groups<PER>(min(nk - 1, t + NS - 1) - (t + 1));
         __builtin_amdgcn_s_barrier();
         const bool early = t + NS < nk;
         // second half of slice t; reads of slice t+1's first half; activation-row copies of slice t+NS
@@ -520,7 +563,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
             const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
             uint16_t* dst = out + (int64_t)m * ep.ldo + n;
             if (n + 7 < N) {
-                *reinterpret_cast<u32x4*>(dst) = v;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));   // whole lines, streamed out
             } else {
                 for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
             }
@@ -550,7 +593,7 @@ hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, 
                   int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     if (K % BK == 0)
-        gemm_i8_w8_kernel<MODE, 4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(aq, lda, wq, ldw, (int)M,
+        gemm_i8_w8_kernel<MODE, 4, WF_I8><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(aq, lda, wq, ldw, (int)M,
                                                                                 (int)N, (int)K, ep);
     else
         gemm_i8_kernel<MODE><<<dim3((unsigned)tiles), dim3(NT), 0, stream>>>(aq, lda, wq, ldw, (int)M,
@@ -572,6 +615,27 @@ hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int6
                            hipStream_t stream) {
     EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc};
     return launch<MODE_I32>(aq, lda, wq, ldw, M, N, K, ep, stream);
+}
+
+// Packed-INT4 weights (K % 64 == 0): five 24 KB stages, four slices in flight.
+hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const uint8_t* wp,
+                               int64_t ldw, const float* w_scale, const void* bias, void* y,
+                               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy};
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+        aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4_i32(const int8_t* aq, int64_t lda, const uint8_t* wp, int64_t ldw,
+                              int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream) {
+    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc};
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_i8_w8_kernel<MODE_I32, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+        aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);
+    return hipGetLastError();
 }
 
 }  // namespace qd

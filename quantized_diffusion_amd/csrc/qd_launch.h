@@ -21,6 +21,18 @@ hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int6
                            int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream);
 
+// Packed-INT4 weights wp [N, K/2] (row stride ldw bytes), K % 64 == 0.
+hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const uint8_t* wp,
+                               int64_t ldw, const float* w_scale, const void* bias, void* y,
+                               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_w4_i32(const int8_t* aq, int64_t lda, const uint8_t* wp, int64_t ldw,
+                              int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              hipStream_t stream);
+
+// out[r, i] = (q[r, 2i] & 15) | (q[r, 2i+1] & 15) << 4, K % 32 == 0.
+hipError_t launch_pack_int4(const int8_t* q, int64_t ldq, uint8_t* out, int64_t ldo, int64_t R, int64_t K,
+                            hipStream_t stream);
+
 // out = q * scale (per row or per tensor) as FP32 (out_bf16 = false) or BF16.
 hipError_t launch_dequant(const int8_t* q, int64_t ldq, const float* scale, bool per_row,
                           bool out_bf16, void* out, int64_t ldo, int64_t M, int64_t K,

@@ -38,6 +38,10 @@
 //
 // Row amax: per-lane max, quad reduction by DPP, then an LDS atomic max over
 // the blocks of the row (non-negative floats order like their bit patterns).
+//
+// Memory: a quad's load instruction covers half a 128-byte line and the next
+// one the other half, so loads and stores use the default cache policy (the
+// L2 merges the halves); streaming hints fetch and write partial lines here.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
         for (int i = 0; i < NI; ++i) {
             const int c = i * 4 + ql;
             if (ROT || blk * 256 + c * E < K) {
-                const u32x4 d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + c * 16));
+                const u32x4 d = *reinterpret_cast<const u32x4*>(src + c * 16);
                 widen(In{}, d, &v[i * E]);
             }
         }
@@ -209,10 +213,10 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
             u32x2 p;
             p[0] = pack4(code[0], code[1], code[2], code[3]);
             p[1] = pack4(code[4 % E], code[5 % E], code[6 % E], code[7 % E]);
-            __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(dst + c * E));
+            *reinterpret_cast<u32x2*>(dst + c * E) = p;
         } else {
             const uint32_t p = pack4(code[0], code[1], code[2], code[3]);
-            __builtin_nontemporal_store(p, reinterpret_cast<uint32_t*>(dst + c * E));
+            *reinterpret_cast<uint32_t*>(dst + c * E) = p;
         }
     }
 }

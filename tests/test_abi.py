@@ -143,3 +143,24 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError, match="GPU"):
         qd.quantize_and_rotate_rowwise(torch.zeros(4, 256, dtype=torch.bfloat16))
+
+
+def test_w4a4_validation():
+    L = qd.lib()
+    st, msg = _status(L.qd_pack_int4, FAKE, 4, 48, 48, FAKE, 32, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 32" in msg
+    st, msg = _status(L.qd_pack_int4, FAKE, 4, 64, 64, FAKE, 16, STREAM)
+    assert st == qd.QD_EINVAL
+    st, msg = _status(L.qd_int4_scaled_mm, FAKE, 4, 96, 96, FAKE, FAKE, 8, 48, FAKE, NULL, FAKE, 8, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 64" in msg
+    st, msg = _status(L.qd_int4_scaled_mm, FAKE, 4, 128, 128, FAKE, FAKE, 8, 48, FAKE, NULL, FAKE, 8, STREAM)
+    assert st == qd.QD_EINVAL and "K/2" in msg
+    st, msg = _status(L.qd_int4_gemm_i32, FAKE, 4, 128, 128, FAKE, 8, 72, FAKE, 8, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 16" in msg
+    ws = qd.workspace_size(4, 512)
+    st, msg = _status(L.qd_convrot_w4a4_linear, FAKE, Q, 4, 512, 512, FAKE, 8, 256, FAKE, NULL, 0, FAKE, ws,
+                      FAKE, 8, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "rotate_block" in msg
+    st, msg = _status(L.qd_convrot_w4a4_linear, FAKE, Q, 0, 512, 512, FAKE, 8, 256, FAKE, NULL, 256, FAKE, ws,
+                      FAKE, 8, STREAM)
+    assert st == qd.QD_OK

@@ -1,0 +1,127 @@
+"""GPU parity of the rotated INT4 (W4A4) path against the oracle: packing
+bit-exact, INT32 accumulators of the packed-INT4 GEMM exact, BF16 outputs
+within one ulp (expected bit-identical), small ragged shapes and the full
+M8192/K28672/N7168 workload (sampled outputs)."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_bf16_within_1ulp, bf16_bits, host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import quantized_diffusion_amd as q
+    q.lib()
+    return q
+
+
+def _codes(shape, seed, lo=-8, hi=8):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.integers(lo, hi, shape, dtype=np.int64).astype(np.int8)
+
+
+@pytest.mark.parametrize("R,K", [(1, 32), (7, 96), (300, 28672)])
+def test_pack_int4(qd, O, R, K):
+    say(f"pack_int4 R={R} K={K}")
+    q = _codes((R, K), seed=R + K)
+    p = qd.pack_int4(to_dev(q))
+    assert np.array_equal(host(p), O.pack_int4(q))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (256, 256, 64), (257, 300, 512), (300, 1000, 28672), (64, 8, 1024)])
+def test_int4_gemm_i32_exact(qd, O, M, N, K):
+    say(f"int4 gemm i32 M={M} N={N} K={K}")
+    a = _codes((M, K), seed=M * 3 + K, lo=-7)
+    w = _codes((N, K), seed=N * 5 + K)
+    wp = O.pack_int4(w)
+    acc = qd.int4_gemm_i32(to_dev(a), to_dev(wp))
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+
+
+def test_int4_scaled_mm(qd, O):
+    say("int4 scaled_mm")
+    from synth import random_bf16
+    M, N, K = 300, 520, 1024
+    g = np.random.Generator(np.random.PCG64(77))
+    a = _codes((M, K), seed=78, lo=-7)
+    w = _codes((N, K), seed=79, lo=-7)
+    sx = (g.uniform(0.5, 2, M) * 2.0 ** -3).astype(np.float32)
+    sw = (g.uniform(0.5, 2, N) * 2.0 ** -6).astype(np.float32)
+    b = random_bf16(N, seed=80, scale=0.1)
+    y = qd.int4_scaled_mm(to_dev(a), to_dev(sx), to_dev(O.pack_int4(w)), to_dev(sw), to_dev_bf16(b))
+    n = assert_bf16_within_1ulp(bf16_bits(y), O.epilogue(O.gemm_i32(a, w), sx, sw, b), "int4_scaled_mm")
+    say(f"  {n} outputs differ")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 8), (257, 1024, 300), (512, 2048, 1024)])
+def test_convrot_w4a4_linear(qd, O, M, K, N):
+    say(f"convrot_w4a4_linear M={M} K={K} N={N}")
+    from synth import f32_to_bf16_bits, random_bf16
+    g = np.random.Generator(np.random.PCG64(M + K + N))
+    x = g.standard_normal((M, K), dtype=np.float32)
+    x[:, g.choice(K, max(1, K // 100), replace=False)] *= 20
+    x = f32_to_bf16_bits(x)
+    W = (g.standard_normal((N, K), dtype=np.float32) * np.float32(0.02))
+    b = random_bf16(N, seed=K, scale=0.1)
+    wp, sw = qd.prepare_weights_w4a4(to_dev(W))
+    wq_o, sw_o = O.prepare_weights(W, 256, qmax=7)
+    assert np.array_equal(host(sw).view(np.uint32), sw_o.view(np.uint32))
+    assert np.array_equal(host(wp), O.pack_int4(wq_o))
+    y = qd.convrot_w4a4_linear(to_dev_bf16(x), wp, sw, to_dev_bf16(b))
+    yo = O.linear(x, wq_o, sw_o, b, qmax=7)
+    n = assert_bf16_within_1ulp(bf16_bits(y), yo, "w4a4")
+    say(f"  {n} outputs differ")
+
+
+def test_w4a4_full_size(qd, O):
+    """M8192/K28672/N7168 in the launch configuration bench.py uses."""
+    import torch
+
+    from synth import iter_w, iter_x, make_bias, workload
+    w = workload(5)
+    M, K, N = w.M, w.K, w.N
+    dev = torch.device("cuda:0")
+    say(f"full-size {w.name}")
+    x_host = np.empty((M, K), np.uint16)
+    xd = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for r0, r1, bits in iter_x(w):
+        x_host[r0:r1] = bits
+        xd[r0:r1].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    W = np.empty((N, K), np.float32)
+    Wd = torch.empty((N, K), dtype=torch.float32, device=dev)
+    for r0, r1, chunk in iter_w(w):
+        W[r0:r1] = chunk
+        Wd[r0:r1].copy_(torch.from_numpy(chunk))
+    b = make_bias(w)
+    wp, sw = qd.prepare_weights_w4a4(Wd)
+    del Wd
+    wq_o, sw_o = O.prepare_weights(W, 256, qmax=7)
+    del W
+    assert np.array_equal(host(sw).view(np.uint32), sw_o.view(np.uint32))
+    assert np.array_equal(host(wp), O.pack_int4(wq_o))
+    say("  activation codes")
+    q, s = qd.quantize_and_rotate_rowwise_int4(xd)
+    qo, so = O.quantize_rowwise(x_host, "bf16", 256, qmax=7)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+    del q
+    say("  convrot_w4a4_linear")
+    ws = torch.empty(qd.workspace_size(M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    qd.convrot_w4a4_linear(xd, wp, sw, torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev), 256, ws, y)
+    g = np.random.Generator(np.random.PCG64(9005))
+    rows = np.concatenate([g.integers(0, M, 8000), np.zeros(N, np.int64), np.full(N, M - 1)])
+    cols = np.concatenate([g.integers(0, N, 8000), np.arange(N), np.arange(N)])
+    yo, acco = O.linear_points(qo, so, rows, wq_o, sw_o, b, cols)
+    ri = torch.from_numpy(rows).to(dev)
+    ci = torch.from_numpy(cols).to(dev)
+    n = assert_bf16_within_1ulp(bf16_bits(y[ri, ci]), yo, "w4a4 full size")
+    say(f"  {n} of {yo.size} sampled outputs not bit-identical")
+    aq = ws[: M * K].view(M, K).view(torch.int8)
+    acc = qd.int4_gemm_i32(aq, wp)
+    assert np.array_equal(host(acc[ri, ci]), acco)
