@@ -51,9 +51,9 @@ def load_traffic(workload_name: str):
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_hash") != kernel_hash(GEMM_SRC) or d.get("workload") != workload_name:
-        return None
-    return d.get("hbm_bytes_per_launch")
+    if d.get("kernel_hash") != kernel_hash(GEMM_SRC):
+        return None                      # counters were taken on another version of the kernel
+    return d.get("workloads", {}).get(workload_name, {}).get("hbm_bytes_per_launch")
 
 
 def time_launches(fn, n, torch):
