@@ -40,8 +40,13 @@
 // the blocks of the row (non-negative floats order like their bit patterns).
 //
 // Memory: a quad's load instruction covers half a 128-byte line and the next
-// one the other half, so loads and stores use the default cache policy (the
-// L2 merges the halves); streaming hints fetch and write partial lines here.
+// one the other half, so loads use the default cache policy (the L2 merges
+// the halves; streaming hints would fetch partial lines).  The codes of the
+// rotated path are staged through LDS per wave: each lane writes its chunks
+// into its quad's 256-byte block image, then lane l stores bytes
+// [16 l, 16 l + 16) of four consecutive block images, so one store
+// instruction writes four whole blocks (1 KB, whole 128-byte lines) and the
+// stores can bypass the caches.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +85,9 @@ __device__ __forceinline__ void widen(InF16, const u32x4& d, float* v) {
 constexpr float kMagic = 12582912.0f;             // 1.5 * 2^23
 constexpr float kFastMargin = 0.5f - 0x1p-15f;    // |d| below this: fast code is exact
 constexpr float kSlowScale = 0x1p-100f;           // rows with s below this take the exact path
+constexpr int kStageStride = 288;                 // bytes per block image in LDS (256 + 32: spreads banks)
+constexpr int kStageWave = 16 * kStageStride;     // per wave: 16 quads
+__host__ __device__ constexpr bool kStageRows(int nb) { return true; }   // rows of nb blocks use staged stores
 
 // Exact code of one element by the definition: v = fl(u * 1/16) (rotated) or
 // v = u, then clamp(rne(fl(v / s))).  `w` is tau * u.  Returned as a byte.
@@ -93,13 +101,34 @@ __device__ __forceinline__ uint32_t exact_code(float w, float tau, float s) {
     return (uint32_t)(int)t & 0xFFu;
 }
 
+// One cross-lane butterfly stage for one value: own + sign * partner, the
+// partner read through DPP inside the FMA (a separate v_mov_b32_dpp would
+// double the VALU work of the stage).  The two wait states cover the
+// hazard of a DPP read of a VGPR written by the previous VALU instruction.
+__device__ __forceinline__ float fmac_quad_xor1(float own, float sign) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                 : "+v"(own) : "v"(sign));
+    return own;
+}
+__device__ __forceinline__ float fmac_quad_xor2(float own, float sign) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                 : "+v"(own) : "v"(sign));
+    return own;
+}
+
 __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
     const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-template <class In, bool ROT, int QMAX>
+template <class In, bool ROT, int QMAX, bool STAGE>
+__device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bits, int row, int blk,
+                                               int ql, int K, int8_t* __restrict__ q, int64_t ldq,
+                                               float* __restrict__ scale, uint8_t* img);
+
+// STAGE (rotated path only): codes leave through the LDS block images.
+template <class In, bool ROT, int QMAX, bool STAGE>
 __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restrict__ x,
                                                         int64_t ldx_bytes, int M, int K, int nb,
                                                         int R, int8_t* __restrict__ q,
@@ -109,27 +138,44 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
     constexpr int NV = NI * E;           // 64 values per lane
     constexpr int ESZ = 16 / E;          // bytes per input element
     __shared__ uint32_t row_amax[256];
+    extern __shared__ __attribute__((aligned(16))) uint8_t stage[];   // kStageWave per wave (rotated path)
 
     const int tid = threadIdx.x;
     const int quad = tid >> 2;
     const int ql = tid & 3;
-    const int rl = quad / nb;
+    // quad / nb by a 24-bit multiply: with inv = ceil(2^20 / nb) the error of
+    // quad * inv / 2^20 is below quad / 2^20 < 1/nb for quad < 4096.
+    const uint32_t nb_inv = ((1u << 20) + nb - 1) / nb;
+    const int rl = (int)(__umul24((uint32_t)quad, nb_inv) >> 20);
     const int blk = quad - rl * nb;
     const int row = blockIdx.x * R + rl;
     const bool active = (rl < R) && (row < M);
     if (tid < R) row_amax[tid] = 0u;
 
     float v[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = 0.0f;
-    if (active) {
-        const uint8_t* src = x + (int64_t)row * ldx_bytes + (int64_t)blk * 256 * ESZ;
+    if (ROT) {
+        // Whole blocks: every lane loads (idle quads read a valid row and
+        // discard the result), so the loads need neither a branch nor zeroed
+        // registers.  Quads never mix active and idle lanes.
+        const int lrow = min(min(blockIdx.x * R + min(rl, R - 1), row), M - 1);
+        const uint8_t* src = x + (int64_t)lrow * ldx_bytes + (int64_t)blk * 256 * ESZ;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int c = i * 4 + ql;
-            if (ROT || blk * 256 + c * E < K) {
-                const u32x4 d = *reinterpret_cast<const u32x4*>(src + c * 16);
-                widen(In{}, d, &v[i * E]);
+            const u32x4 d = *reinterpret_cast<const u32x4*>(src + (i * 4 + ql) * 16);
+            widen(In{}, d, &v[i * E]);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = 0.0f;
+        if (active) {
+            const uint8_t* src = x + (int64_t)row * ldx_bytes + (int64_t)blk * 256 * ESZ;
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int c = i * 4 + ql;
+                if (blk * 256 + c * E < K) {
+                    const u32x4 d = *reinterpret_cast<const u32x4*>(src + c * 16);
+                    widen(In{}, d, &v[i * E]);
+                }
             }
         }
     }
@@ -150,10 +196,10 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
         // stages on the two quad-lane bits (pair distance E and 2E)
         const float c0 = (ql & 1) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] = __builtin_fmaf(quad_xor1(v[j]), c0, v[j]);
+        for (int j = 0; j < NV; ++j) v[j] = fmac_quad_xor1(v[j], c0);
         const float c1 = (ql & 2) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] = __builtin_fmaf(quad_xor2(v[j]), c1, v[j]);
+        for (int j = 0; j < NV; ++j) v[j] = fmac_quad_xor2(v[j], c1);
         // stages on the chunk-index bits (pair distance 4E, 8E, ...)
 #pragma unroll
         for (int hi = 1; hi < NI; hi *= 2) {
@@ -179,9 +225,40 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
     __syncthreads();
     if (active && ql == 0) atomicMax(&row_amax[rl], f_bits(am));
     __syncthreads();
-    if (!active) return;
+    if (active) quantize_store<In, ROT, QMAX, STAGE>(v, row_amax[rl], row, blk, ql, K, q, ldq, scale,
+                                                     stage + (tid >> 6) * kStageWave + ((tid >> 2) & 15) * kStageStride);
+    if (STAGE) {
+        // Whole-block stores of the wave's 16 block images (see the header).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int lane = tid & 63;
+        const uint8_t* img = stage + (tid >> 6) * kStageWave + (lane >> 4) * kStageStride + 16 * (lane & 15);
+        u32x4 val[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) val[j] = *reinterpret_cast<const u32x4*>(img + 4 * j * kStageStride);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int qq = (tid >> 6) * 16 + 4 * j + (lane >> 4);   // quad of the workgroup
+            const int rl2 = (int)(__umul24((uint32_t)qq, nb_inv) >> 20);
+            const int row2 = blockIdx.x * R + rl2;
+            if (rl2 < R && row2 < M) {
+                int8_t* dst = q + (int64_t)row2 * ldq + (qq - rl2 * nb) * 256 + 16 * (lane & 15);
+                __builtin_nontemporal_store(val[j], reinterpret_cast<u32x4*>(dst));
+            }
+        }
+    }
+}
 
-    const float amax_u = bits_f(row_amax[rl]);
+// Scale and codes of one quad's values (see the header).  Rotated path: the
+// codes go to the quad's block image `img` in LDS; otherwise straight to q.
+template <class In, bool ROT, int QMAX, bool STAGE>
+__device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bits, int row, int blk,
+                                               int ql, int K, int8_t* __restrict__ q, int64_t ldq,
+                                               float* __restrict__ scale, uint8_t* img) {
+    constexpr int E = In::E;
+    constexpr int NI = 256 / (4 * E);
+    const float amax_u = bits_f(amax_bits);
     const float amax = ROT ? amax_u * 0.0625f : amax_u;
     const float s = amax / (float)QMAX;
     if (blk == 0 && ql == 0) scale[row] = s;
@@ -197,34 +274,58 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
     for (int i = 0; i < NI; ++i) {
         const int c = i * 4 + ql;
         if (!ROT && blk * 256 + c * E >= K) continue;
+        // Fast codes for the chunk; one test of the largest |d| decides
+        // whether any element of the chunk needs the exact path.
         uint32_t code[E];
+        float dmax = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float w = v[i * E + e];
             const float t = __builtin_fmaf(w, trs, kMagic);
             const float n = t - kMagic;
             const float d = __builtin_fmaf(w, trs, -n);
-            uint32_t cb = f_bits(t);
-            if (__builtin_expect(mode != 1 || __builtin_fabsf(d) >= kFastMargin, 0))
-                cb = mode == 0 ? 0u : exact_code<ROT, QMAX>(w, tau, s);
-            code[e] = cb;
+            dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d));
+            code[e] = f_bits(t);
         }
+        if (__builtin_expect(mode != 1 || dmax >= kFastMargin, 0)) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float w = v[i * E + e];
+                const float t = __builtin_fmaf(w, trs, kMagic);
+                const float n = t - kMagic;
+                const float d = __builtin_fmaf(w, trs, -n);
+                if (mode != 1 || __builtin_fabsf(d) >= kFastMargin)
+                    code[e] = mode == 0 ? 0u : exact_code<ROT, QMAX>(w, tau, s);
+            }
+        }
+        uint8_t* out = STAGE ? img + c * E : reinterpret_cast<uint8_t*>(dst) + c * E;
         if (E == 8) {
             u32x2 p;
             p[0] = pack4(code[0], code[1], code[2], code[3]);
             p[1] = pack4(code[4 % E], code[5 % E], code[6 % E], code[7 % E]);
-            *reinterpret_cast<u32x2*>(dst + c * E) = p;
+            *reinterpret_cast<u32x2*>(out) = p;
         } else {
             const uint32_t p = pack4(code[0], code[1], code[2], code[3]);
-            *reinterpret_cast<uint32_t*>(dst + c * E) = p;
+            *reinterpret_cast<uint32_t*>(out) = p;
         }
     }
+}
+
+template <class In, bool ROT, int QMAX, bool STAGE>
+hipError_t launch_staged(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                         float* scale, hipStream_t stream, int R, int threads) {
+    constexpr int ESZ = 16 / In::E;
+    const int nb = (int)((K + 255) / 256);
+    const int64_t grid = (M + R - 1) / R;
+    const size_t lds = STAGE ? (size_t)(threads / 64) * kStageWave : 0;
+    rotquant_kernel<In, ROT, QMAX, STAGE><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
+        static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
+    return hipGetLastError();
 }
 
 template <class In, bool ROT, int QMAX>
 hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                         float* scale, hipStream_t stream) {
-    constexpr int ESZ = 16 / In::E;
     const int nb = (int)((K + 255) / 256);
     // Rows per workgroup: one quad per (row, block); pick the row count that
     // leaves the fewest idle lanes in whole waves, preferring ~256 threads.
@@ -238,10 +339,9 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     }
     if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
-    const int64_t grid = (M + R - 1) / R;
-    rotquant_kernel<In, ROT, QMAX><<<dim3((unsigned)grid), dim3(best_threads), 0, stream>>>(
-        static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
-    return hipGetLastError();
+    if (ROT && kStageRows(nb))
+        return launch_staged<In, ROT, QMAX, true>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
+    return launch_staged<In, ROT, QMAX, false>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
 }
 
 }  // namespace
