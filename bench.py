@@ -57,14 +57,17 @@ def load_traffic(workload_name: str):
 
 
 def time_launches(fn, n, torch):
-    """Average duration (ms) of fn() measured with events around each launch on the current stream."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
+    """Average duration (ms) of fn() over n back-to-back launches, timed with one pair of HIP
+    events on the current stream (the stream the binding launches on)."""
+    fn()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / n
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
 
 
 def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float):

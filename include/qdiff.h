@@ -182,6 +182,42 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
                              int64_t ldc, hipStream_t stream);
 
 /*
+ * Tensor-wise scaling (comfy-kitchen 0.2.40, "Huawei Ascend backend":
+ * quantize_int8_tensorwise; "HIP backend": tensor-wise is the scaling its
+ * GEMMs take).
+ *
+ * qd_quantize_int8_tensorwise: one scale for the whole tensor, no rotation:
+ *   s = amax / 127 (one correctly rounded FP32 division), amax = max |x|
+ *   over all M x K elements; q[m, k] = clamp(rne(fl(x[m, k] / s)), -127, 127);
+ *   s == 0 gives all-zero codes.
+ *   x [M, K] in x_dtype (stride ldx elements), q [M, K] INT8 (stride ldq
+ *   bytes), scale: ONE float, written.
+ *   workspace: at least qd_quantize_tensorwise_workspace_size() bytes,
+ *   4-byte aligned, for per-workgroup partial maxima (its contents on entry
+ *   do not matter; calls that share it must not overlap).
+ * Requirements as qd_quantize_int8_rowwise (K % 16 == 0, 16-byte alignment).
+ * Two kernels are enqueued: partial maxima, then the quantizer.
+ */
+size_t qd_quantize_tensorwise_workspace_size(void);
+qd_status_t qd_quantize_int8_tensorwise(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                        int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * qd_int8_scaled_mm with the scale granularity chosen per operand:
+ *   y[m, n] = bf16_rne(((float)acc[m, n] * sa(m)) * sw(n) + bias[n]),
+ *   sa(m) = a_scale[m] if a_scale_len == M, a_scale[0] if a_scale_len == 1;
+ *   sw(n) = w_scale[n] if w_scale_len == N, w_scale[0] if w_scale_len == 1.
+ * (1, 1) is the tensor-wise GEMM; (M, N) is qd_int8_scaled_mm.  Other
+ * lengths are QD_EINVAL.  A per-channel w_scale must be 16-byte aligned.
+ * Otherwise as qd_int8_scaled_mm.
+ */
+qd_status_t qd_int8_scaled_mm_ex(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                                 const float* a_scale, int64_t a_scale_len, const int8_t* wq,
+                                 int64_t N, int64_t ldw, const float* w_scale, int64_t w_scale_len,
+                                 const void* bias_bf16, void* y_bf16, int64_t ldy, hipStream_t stream);
+
+/*
  * INT4 storage for convrot_w4a4_linear (comfy-kitchen 0.2.40, "Huawei Ascend
  * backend": signed INT4 activation codes kept in INT8 storage, packed INT4
  * weights unpacked to INT8 for INT32 accumulation).

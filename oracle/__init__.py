@@ -62,6 +62,8 @@ def _bind(L):
     L.oracle_quantize_rows.argtypes = [P, I64, I64, I, P, I64, P]
     L.oracle_quantize_rowwise.restype = I
     L.oracle_quantize_rowwise.argtypes = [P, I, I64, I64, I64, I, I, P, I64, P]
+    L.oracle_quantize_tensorwise.restype = I
+    L.oracle_quantize_tensorwise.argtypes = [P, I, I64, I64, I64, I, P, I64, P]
     L.oracle_gemm_i32.restype = I64
     L.oracle_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P]
     L.oracle_epilogue.argtypes = [P, I64, I64, P, P, P, P]
@@ -132,6 +134,15 @@ class Oracle:
         rc = self.L.oracle_quantize_rowwise(_p(x), _DTYPES[dtype], M, K, K, block, qmax, _p(q), K, _p(s))
         if rc:
             raise ValueError(f"oracle_quantize_rowwise failed rc={rc}")
+        return q, s
+
+    def quantize_tensorwise(self, x, dtype: str = "bf16", qmax: int = 127):
+        """(codes int8 [M, K], scale float32 [1]) of tensor-wise quantization (no rotation)."""
+        x = _x_in(x, dtype)
+        M, K = x.shape
+        q = np.empty((M, K), np.int8)
+        s = np.empty(1, np.float32)
+        self.L.oracle_quantize_tensorwise(_p(x), _DTYPES[dtype], M, K, K, qmax, _p(q), K, _p(s))
         return q, s
 
     def prepare_weights(self, w, block: int = 256, qmax: int = 127):

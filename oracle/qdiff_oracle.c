@@ -167,6 +167,37 @@ int oracle_quantize_rowwise(const void* x, int dtype, int64_t M, int64_t K, int6
     return rc;
 }
 
+/* ---- tensor-wise symmetric quantization --------------------------------- */
+
+/* quantize_int8_tensorwise (comfy-kitchen 0.2.40, "Huawei Ascend backend"):
+ * one scale for the whole [M, K] tensor, s = amax / qmax with amax the
+ * largest |x| over every element; codes clamp(rne(fl(x / s))); s == 0 gives
+ * all-zero codes.  No rotation.  *scale receives s. */
+int oracle_quantize_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                               int qmax, int8_t* q, int64_t ldq, float* scale) {
+    float tmax = 0.0f;
+    for (int64_t r = 0; r < M; r++)
+        for (int64_t k = 0; k < K; k++) {
+            float a = fabsf(load_elem(x, dtype, r * ldx + k));
+            if (a > tmax) tmax = a;
+        }
+    const float ts = tmax / (float)qmax;
+    *scale = ts;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k = 0; k < K; k++) {
+            int c = 0;
+            if (ts != 0.0f) {
+                float t = rintf(load_elem(x, dtype, m * ldx + k) / ts);
+                if (t > (float)qmax) t = (float)qmax;
+                if (t < (float)-qmax) t = (float)-qmax;
+                c = (int)t;
+            }
+            q[m * ldq + k] = (int8_t)c;
+        }
+    return 0;
+}
+
 /* ---- exact integer GEMM ------------------------------------------------ */
 
 /* acc[m, n] = sum_k a[m, k] * w[n, k]; a is [M, K], w is [N, K] (both K

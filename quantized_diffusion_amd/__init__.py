@@ -30,7 +30,8 @@ __all__ = [
     "LIB_PATH", "QDiffError", "lib", "quantize_and_rotate_rowwise", "quantize_and_rotate_rowwise_int4",
     "quantize_int8_rowwise", "int8_linear", "int8_scaled_mm", "int8_gemm_i32", "dequantize_int8",
     "prepare_weights", "workspace_size", "EXPORTED_SYMBOLS", "pack_int4", "prepare_weights_w4a4",
-    "int4_scaled_mm", "int4_gemm_i32", "convrot_w4a4_linear",
+    "int4_scaled_mm", "int4_gemm_i32", "convrot_w4a4_linear", "quantize_int8_tensorwise",
+    "tensorwise_workspace_size", "int8_scaled_mm_ex",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -43,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "qd_quantize_and_rotate_rowwise_int4", "qd_quantize_int8_rowwise", "qd_int8_scaled_mm",
     "qd_int8_linear_workspace_size", "qd_int8_linear", "qd_dequantize_int8", "qd_int8_gemm_i32",
     "qd_pack_int4", "qd_int4_scaled_mm", "qd_int4_gemm_i32", "qd_convrot_w4a4_linear",
+    "qd_quantize_tensorwise_workspace_size", "qd_quantize_int8_tensorwise", "qd_int8_scaled_mm_ex",
 )
 
 
@@ -91,6 +93,12 @@ def lib():
         L.qd_int4_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
         L.qd_convrot_w4a4_linear.restype = St
         L.qd_convrot_w4a4_linear.argtypes = [P, St, I64, I64, I64, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
+        L.qd_quantize_tensorwise_workspace_size.restype = SZ
+        L.qd_quantize_tensorwise_workspace_size.argtypes = []
+        L.qd_quantize_int8_tensorwise.restype = St
+        L.qd_quantize_int8_tensorwise.argtypes = [P, St, I64, I64, I64, P, I64, P, P, SZ, P]
+        L.qd_int8_scaled_mm_ex.restype = St
+        L.qd_int8_scaled_mm_ex.argtypes = [P, I64, I64, I64, P, I64, P, I64, I64, P, I64, P, P, I64, P]
         _lib = L
     return _lib
 
@@ -199,6 +207,32 @@ def quantize_int8_rowwise(x, out_q=None, out_scale=None):
     return _quantize(lib().qd_quantize_int8_rowwise, x, 0, out_q, out_scale, False)
 
 
+def tensorwise_workspace_size() -> int:
+    """Bytes of workspace quantize_int8_tensorwise needs (partial maxima)."""
+    return int(lib().qd_quantize_tensorwise_workspace_size())
+
+
+def quantize_int8_tensorwise(x, out_q=None, out_scale=None, workspace=None):
+    """Tensor-wise dynamic symmetric INT8 quantization (no rotation): one FP32
+    scale s = max|x| / 127 for the whole tensor.  Returns (codes int8 [M, K],
+    scale fp32 [1])."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, out_q, out_scale, workspace)
+    M, K = x.shape
+    if out_q is None:
+        out_q = torch.empty((M, (K + 15) // 16 * 16), dtype=torch.int8, device=dev)[:, :K]
+    if out_scale is None:
+        out_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(tensorwise_workspace_size(), dtype=torch.uint8, device=dev)
+    _mat(out_q, "q")
+    _check(lib().qd_quantize_int8_tensorwise(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(out_q),
+                                             out_q.stride(0), _ptr(out_scale), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out_q, out_scale
+
+
 def prepare_weights(w, block: int = 256):
     """Offline weight preparation for int8_linear: rotate FP32 W [N, K] along K
     (block 256, or 0 for none) and quantize per output channel.
@@ -228,6 +262,30 @@ def int8_scaled_mm(aq, a_scale, wq, w_scale, bias=None, out=None):
     _mat(out, "out")
     _check(lib().qd_int8_scaled_mm(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(wq), N, wq.stride(0),
                                    _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def int8_scaled_mm_ex(aq, a_scale, wq, w_scale, bias=None, out=None):
+    """int8_scaled_mm with per-tensor scales allowed: a_scale of length M (per
+    row) or 1 (one for all rows), w_scale of length N (per output channel) or 1."""
+    torch = _torch()
+    _mat(aq, "aq"), _mat(wq, "wq")
+    dev = _dev(aq, a_scale, wq, w_scale, bias, out)
+    M, K = aq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("aq and wq disagree on K")
+    for t, name in ((a_scale, "a_scale"), (w_scale, "w_scale")):
+        if t.dtype != torch.float32 or t.dim() != 1 or (t.numel() > 1 and t.stride(0) != 1):
+            raise ValueError(f"{name} must be a contiguous 1-D float32 tensor")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_int8_scaled_mm_ex(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), a_scale.numel(), _ptr(wq), N,
+                                      wq.stride(0), _ptr(w_scale), w_scale.numel(), _ptr(bias), _ptr(out),
+                                      out.stride(0), _stream(dev)))
     return out
 
 

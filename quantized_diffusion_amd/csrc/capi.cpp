@@ -142,6 +142,45 @@ qd_status_t qd_int8_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t ld
                                                y_bf16, ldy, M, N, K, stream));
 }
 
+qd_status_t qd_int8_scaled_mm_ex(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                                 const float* a_scale, int64_t a_scale_len, const int8_t* wq,
+                                 int64_t N, int64_t ldw, const float* w_scale, int64_t w_scale_len,
+                                 const void* bias_bf16, void* y_bf16, int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_int8_scaled_mm_ex";
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, wq, N, ldw, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
+    if (a_scale_len != M && a_scale_len != 1)
+        return fail(QD_EINVAL, fn, "a_scale_len must be M (%lld) or 1 (got %lld)", (long long)M, (long long)a_scale_len);
+    if (w_scale_len != N && w_scale_len != 1)
+        return fail(QD_EINVAL, fn, "w_scale_len must be N (%lld) or 1 (got %lld)", (long long)N, (long long)w_scale_len);
+    const int a_step = a_scale_len == M ? 1 : 0;
+    const int w_step = w_scale_len == N ? 1 : 0;
+    if ((w_step && ((uintptr_t)w_scale & 15u)) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "a per-channel w_scale must be 16-byte and bias 8-byte aligned");
+    return hip_status(fn, qd::launch_gemm_bf16(aq, lda, a_scale, wq, ldw, w_scale, bias_bf16, y_bf16, ldy, M,
+                                               N, K, stream, a_step, w_step));
+}
+
+size_t qd_quantize_tensorwise_workspace_size(void) { return (size_t)qd::kTensorwisePartials * sizeof(float); }
+
+qd_status_t qd_quantize_int8_tensorwise(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                        int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const char* fn = "qd_quantize_int8_tensorwise";
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, false, 0, q, ldq, scale);
+    if (st != QD_OK) return st;
+    if (M == 0) return ok();
+    if (!workspace) return fail(QD_EINVAL, fn, "null workspace");
+    if (workspace_bytes < qd_quantize_tensorwise_workspace_size())
+        return fail(QD_EINVAL, fn, "workspace too small (%zu < %zu bytes)", workspace_bytes,
+                    qd_quantize_tensorwise_workspace_size());
+    if ((uintptr_t)workspace & 3u) return fail(QD_EUNSUPPORTED, fn, "workspace must be 4-byte aligned");
+    return hip_status(fn, qd::launch_quant_tensorwise(x, (int)x_dtype, M, K, ldx, q, ldq, scale,
+                                                      static_cast<float*>(workspace), stream));
+}
+
 size_t qd_int8_linear_workspace_size(int64_t M, int64_t K) {
     if (M <= 0 || K <= 0) return 0;
     return ws_codes_bytes(M, K) + round_up((size_t)M * sizeof(float), kAlign);

@@ -59,6 +59,8 @@ struct EpiArgs {
     const uint16_t* bias;   // may be null
     void* out;              // uint16_t (BF16) or int32_t
     int64_t ldo;            // elements
+    int a_step;             // 1: a_scale[m]; 0: a_scale[0] for every row
+    int w_step;             // 1: w_scale[n]; 0: w_scale[0] for every column
 };
 
 __device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
@@ -71,7 +73,8 @@ __device__ __forceinline__ void store_bf16x4(const int32_t* a4, float sx, int n,
 #pragma clang fp contract(off)
     uint16_t* dst = static_cast<uint16_t*>(ep.out) + m * ep.ldo + n;
     if (n + 3 < N) {
-        const f32x4 sw = *reinterpret_cast<const f32x4*>(ep.w_scale + n);
+        const f32x4 sw = ep.w_step ? *reinterpret_cast<const f32x4*>(ep.w_scale + n)
+                                   : f32x4{ep.w_scale[0], ep.w_scale[0], ep.w_scale[0], ep.w_scale[0]};
         float b4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (ep.bias) {
             const u32x2 bb = *reinterpret_cast<const u32x2*>(ep.bias + n);
@@ -95,7 +98,7 @@ __device__ __forceinline__ void store_bf16x4(const int32_t* a4, float sx, int n,
         for (int e = 0; e < 4 && n + e < N; ++e) {
             float tt = (float)a4[e];
             tt = tt * sx;
-            tt = tt * ep.w_scale[n + e];
+            tt = tt * ep.w_scale[(n + e) * ep.w_step];
             if (ep.bias) tt = tt + bf16_to_f32(ep.bias[n + e]);
             dst[e] = (uint16_t)(pack_bf16x2(tt, 0.0f) & 0xFFFFu);
         }
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_i8_kernel(const int8_t* __restrict
     for (int j = 0; j < 4; ++j) {
         const int m = m0 + wm * 128 + 32 * j + fr;
         if (m >= M) continue;
-        const float sx = (MODE == MODE_BF16) ? ep.a_scale[m] : 0.0f;
+        const float sx = (MODE == MODE_BF16) ? ep.a_scale[m * ep.a_step] : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -384,11 +387,11 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     if (MODE == MODE_BF16) {
         if (tid < 256) {
             const int m = min(m0 + tid, M - 1);
-            l_sx[tid] = ep.a_scale[m];
+            l_sx[tid] = ep.a_scale[m * ep.a_step];
         } else {
             const int c = tid - 256;
             const int n = min(n0 + c, N - 1);
-            l_sw[c] = ep.w_scale[n];
+            l_sw[c] = ep.w_scale[n * ep.w_step];
             l_b[c] = ep.bias ? ep.bias[n] : (uint16_t)0;
         }
     }
@@ -605,23 +608,25 @@ hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, 
 
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
-                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy};
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                            int a_step, int w_step) {
+    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, a_step, w_step};
     return launch<MODE_BF16>(aq, lda, wq, ldw, M, N, K, ep, stream);
 }
 
 hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
                            int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream) {
-    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc};
+    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
     return launch<MODE_I32>(aq, lda, wq, ldw, M, N, K, ep, stream);
 }
 
 // Packed-INT4 weights (K % 64 == 0): five 24 KB stages, four slices in flight.
 hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const uint8_t* wp,
                                int64_t ldw, const float* w_scale, const void* bias, void* y,
-                               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy};
+                               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                               int a_step, int w_step) {
+    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, a_step, w_step};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
         aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);
@@ -631,7 +636,7 @@ hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_sca
 hipError_t launch_gemm_w4_i32(const int8_t* aq, int64_t lda, const uint8_t* wp, int64_t ldw,
                               int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream) {
-    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc};
+    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     gemm_i8_w8_kernel<MODE_I32, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
         aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);

@@ -11,10 +11,18 @@ namespace qd {
 hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int64_t M, int64_t K,
                            int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream);
 
-// y (BF16) = epilogue(aq . wq^T); bias may be null.
+// Tensor-wise quantization: two launches; partial holds kTensorwisePartials
+// floats (K % 16 == 0).
+constexpr int kTensorwisePartials = 1024;
+hipError_t launch_quant_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                   int64_t ldq, float* scale, float* partial, hipStream_t stream);
+
+// y (BF16) = epilogue(aq . wq^T); bias may be null.  a_step / w_step: 1 for a
+// scale per row / per output channel, 0 for one scale for the whole operand.
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
-                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                            int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                            int a_step = 1, int w_step = 1);
 
 // acc (INT32) = aq . wq^T.
 hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
@@ -24,7 +32,8 @@ hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int6
 // Packed-INT4 weights wp [N, K/2] (row stride ldw bytes), K % 64 == 0.
 hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const uint8_t* wp,
                                int64_t ldw, const float* w_scale, const void* bias, void* y,
-                               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                               int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                               int a_step = 1, int w_step = 1);
 hipError_t launch_gemm_w4_i32(const int8_t* aq, int64_t lda, const uint8_t* wp, int64_t ldw,
                               int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream);

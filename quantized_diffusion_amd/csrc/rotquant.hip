@@ -52,54 +52,13 @@
 
 #include "qd_device.h"
 #include "qd_launch.h"
+#include "qd_quant.h"
 
 namespace qd {
 namespace {
 
-struct InF32 { static constexpr int E = 4; };
-struct InBF16 { static constexpr int E = 8; };
-struct InF16 { static constexpr int E = 8; };
-
-__device__ __forceinline__ void widen(InF32, const u32x4& d, float* v) {
-    v[0] = bits_f(d[0]); v[1] = bits_f(d[1]); v[2] = bits_f(d[2]); v[3] = bits_f(d[3]);
-}
-__device__ __forceinline__ void widen(InBF16, const u32x4& d, float* v) {
-    const uint32_t w[4] = {d[0], d[1], d[2], d[3]};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bits_f(w[i] << 16);
-        v[2 * i + 1] = bits_f(w[i] & 0xFFFF0000u);
-    }
-}
-__device__ __forceinline__ void widen(InF16, const u32x4& d, float* v) {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const uint32_t w[4] = {d[0], d[1], d[2], d[3]};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        h2 p = __builtin_bit_cast(h2, w[i]);
-        v[2 * i] = (float)p[0];
-        v[2 * i + 1] = (float)p[1];
-    }
-}
-
-constexpr float kMagic = 12582912.0f;             // 1.5 * 2^23
-constexpr float kFastMargin = 0.5f - 0x1p-15f;    // |d| below this: fast code is exact
-constexpr float kSlowScale = 0x1p-100f;           // rows with s below this take the exact path
 constexpr int kStageStride = 288;                 // bytes per block image in LDS (256 + 32: spreads banks)
 constexpr int kStageWave = 16 * kStageStride;     // per wave: 16 quads
-__host__ __device__ constexpr bool kStageRows(int nb) { return true; }   // rows of nb blocks use staged stores
-
-// Exact code of one element by the definition: v = fl(u * 1/16) (rotated) or
-// v = u, then clamp(rne(fl(v / s))).  `w` is tau * u.  Returned as a byte.
-template <bool ROT, int QMAX>
-__device__ __forceinline__ uint32_t exact_code(float w, float tau, float s) {
-#pragma clang fp contract(off)
-    const float u = tau * w;
-    const float v = ROT ? u * 0.0625f : u;
-    float t = __builtin_rintf(v / s);
-    t = __builtin_fminf(__builtin_fmaxf(t, (float)-QMAX), (float)QMAX);
-    return (uint32_t)(int)t & 0xFFu;
-}
 
 // One cross-lane butterfly stage for one value: own + sign * partner, the
 // partner read through DPP inside the FMA (a separate v_mov_b32_dpp would
@@ -114,12 +73,6 @@ __device__ __forceinline__ float fmac_quad_xor2(float own, float sign) {
     asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
                  : "+v"(own) : "v"(sign));
     return own;
-}
-
-__device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-    const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0C0C0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0C0C0400u);
-    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 template <class In, bool ROT, int QMAX, bool STAGE>
@@ -339,7 +292,7 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     }
     if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
-    if (ROT && kStageRows(nb))
+    if (ROT)
         return launch_staged<In, ROT, QMAX, true>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
     return launch_staged<In, ROT, QMAX, false>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
 }

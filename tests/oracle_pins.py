@@ -217,6 +217,52 @@ def check_roundtrip_bound(O):
     assert np.all(np.abs(v.astype(np.float64) - d.astype(np.float64)) <= bound)
 
 
+def check_tensorwise_bruteforce(O):
+    """Tensor-wise codes and scale against exact rationals: one amax over the
+    whole tensor, s = fl(amax / 127), codes rne(fl(x / s)) clamped."""
+    g = np.random.Generator(np.random.PCG64(26))
+    cases = []
+    for e in (-3, 0, 2):
+        cases.append(g.standard_normal((5, 16)).astype(np.float32) * np.float32(10.0 ** e))
+    x = np.zeros((3, 16), np.float32)                       # near-ties of the global scale
+    amax = np.float32(37.5)
+    s = float(rn32(as_frac(amax) / 127))
+    x[0, 0] = amax
+    n = g.integers(-126, 126, size=x.size - 1)
+    near = [np.float32((k + 0.5) * s) for k in n]
+    near = [np.nextafter(v, np.float32(g.choice([-1, 1]) * np.inf)) if g.random() < 0.5 else v for v in near]
+    x.reshape(-1)[1:] = near
+    cases.append(x)
+    cases.append(g.uniform(-1, 1, (2, 16)).astype(np.float32) * np.float32(2.0 ** -140))   # subnormal
+    cases.append(np.zeros((2, 16), np.float32))
+    for x in cases:
+        q, s = O.quantize_tensorwise(x, "f32")
+        codes, sref = _quant_ref(x.reshape(-1), 127)
+        assert as_frac(s[0]) == sref
+        assert q.reshape(-1).tolist() == codes
+    # BF16 input: the same definition on the widened values
+    from synth import random_bf16
+    xb = random_bf16((4, 32), seed=27, scale=2.0)
+    q, s = O.quantize_tensorwise(xb, "bf16")
+    codes, sref = _quant_ref([np.float32(bf16_bits_to_float(b)) for b in xb.reshape(-1)], 127)
+    assert as_frac(s[0]) == sref and q.reshape(-1).tolist() == codes
+
+
+def check_tensorwise_is_flattened_rowwise(O):
+    """A tensor-wise scale is the row scale of the tensor flattened to one row;
+    rows with different maxima must not get their own scales."""
+    from synth import random_bf16
+    x = random_bf16((6, 64), seed=28)
+    x[2] = random_bf16((1, 64), seed=29, scale=40.0)[0]     # one row with a much larger amax
+    q, s = O.quantize_tensorwise(x, "bf16")
+    qf, sf = O.quantize_rowwise(x.reshape(1, -1), "bf16", 0)
+    assert np.array_equal(q.reshape(1, -1), qf) and np.array_equal(s, sf)
+    qr, sr = O.quantize_rowwise(x, "bf16", 0)
+    assert not np.array_equal(q, qr)                         # per-row scales differ here
+    i = np.unravel_index(np.argmax(np.abs((x.astype(np.uint32) << 16).view(np.float32))), x.shape)
+    assert abs(int(q[i])) == 127
+
+
 # ------------------------------------------------------------------ GEMM
 
 def check_gemm_bruteforce(O):

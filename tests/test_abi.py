@@ -164,3 +164,47 @@ def test_w4a4_validation():
     st, msg = _status(L.qd_convrot_w4a4_linear, FAKE, Q, 0, 512, 512, FAKE, 8, 256, FAKE, NULL, 256, FAKE, ws,
                       FAKE, 8, STREAM)
     assert st == qd.QD_OK
+
+
+def test_tensorwise_validation():
+    L = qd.lib()
+    ws = L.qd_quantize_tensorwise_workspace_size()
+    assert ws >= 4 * 256
+    ok_args = (FAKE, Q, 4, 512, 512, FAKE, 512, FAKE, FAKE, ws, STREAM)
+    cases = [
+        ((FAKE, Q, 4, 512, 512, FAKE, 512, FAKE, NULL, ws, STREAM), qd.QD_EINVAL, "workspace"),
+        ((FAKE, Q, 4, 512, 512, FAKE, 512, FAKE, FAKE, ws - 4, STREAM), qd.QD_EINVAL, "too small"),
+        ((FAKE, Q, 4, 520, 520, FAKE, 520, FAKE, FAKE, ws, STREAM), qd.QD_EUNSUPPORTED, "multiple of 16"),
+        ((FAKE, Q, 4, 512, 512, NULL, 512, FAKE, FAKE, ws, STREAM), qd.QD_EINVAL, "null"),
+        ((FAKE, Q, 4, 512, 512, FAKE, 512, FAKE, ctypes.c_void_p(0x100002), ws, STREAM), qd.QD_EUNSUPPORTED,
+         "4-byte"),
+    ]
+    for args, status, needle in cases:
+        st, msg = _status(L.qd_quantize_int8_tensorwise, *args)
+        assert st == status and needle in msg, (args, st, msg)
+    # M == 0 is a no-op that launches nothing
+    assert L.qd_quantize_int8_tensorwise(FAKE, Q, 0, 512, 512, FAKE, 512, FAKE, FAKE, ws, STREAM) == qd.QD_OK
+    assert ok_args  # the valid form is exercised on the GPU
+
+
+def test_scaled_mm_ex_validation():
+    L = qd.lib()
+    base = dict(aq=FAKE, M=8, K=64, lda=64, a_scale=FAKE, a_len=8, wq=FAKE, N=16, ldw=64, w_scale=FAKE,
+                w_len=16, bias=NULL, y=FAKE, ldy=16, s=STREAM)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return _status(L.qd_int8_scaled_mm_ex, a["aq"], a["M"], a["K"], a["lda"], a["a_scale"], a["a_len"],
+                       a["wq"], a["N"], a["ldw"], a["w_scale"], a["w_len"], a["bias"], a["y"], a["ldy"], a["s"])
+    for kw, status, needle in [
+        (dict(a_len=3), qd.QD_EINVAL, "a_scale_len"),
+        (dict(w_len=2), qd.QD_EINVAL, "w_scale_len"),
+        (dict(a_scale=NULL), qd.QD_EINVAL, "null scale"),
+        (dict(w_scale=FAKE_ODD), qd.QD_EUNSUPPORTED, "16-byte"),
+        (dict(K=40, lda=40, ldw=40), qd.QD_EUNSUPPORTED, "multiple of 16"),
+    ]:
+        st, msg = call(**kw)
+        assert st == status and needle in msg, (kw, st, msg)
+    # a per-tensor w_scale needs no 16-byte alignment: validation passes up to the launch,
+    # which an empty problem skips
+    assert call(w_len=1, w_scale=ctypes.c_void_p(0x100004), M=0)[0] == qd.QD_OK

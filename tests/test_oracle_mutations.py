@@ -23,6 +23,8 @@ MUTATIONS = {
     "int4_nibbles_swapped": ("packed[r * (K / 2) + i] = (uint8_t)(lo | (hi << 4));", "packed[r * (K / 2) + i] = (uint8_t)(hi | (lo << 4));"),
     "rotation_skips_last_block": ("for (int64_t b = 0; b < K; b += 256)", "for (int64_t b = 0; b + 256 < K; b += 256)"),
     "bf16_widen_wrong_shift": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "tensorwise_first_row_only": ("for (int64_t r = 0; r < M; r++)", "for (int64_t r = 0; r < 1; r++)"),
+    "tensorwise_qmax_off_by_one": ("const float ts = tmax / (float)qmax;", "const float ts = tmax / (float)(qmax + 1);"),
 }
 
 
