@@ -70,7 +70,7 @@ def time_launches(fn, n, torch):
     return a.elapsed_time(b) / n
 
 
-def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float):
+def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float, act: int = 0):
     """Time the oracle on the leading rows of the same workload; check those rows."""
     import numpy as np
 
@@ -85,7 +85,7 @@ def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float
     def run(rows):
         x = x_dev[:rows].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
-        y = O.linear(x, wq, sw, b_bits, qmax=7 if int4 else 127)
+        y = O.linear(x, wq, sw, b_bits, qmax=7 if int4 else 127, act=act)
         return time.perf_counter() - t0, y
 
     t_small, _ = run(16)
@@ -131,6 +131,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload id (synth.WORKLOADS)")
+    ap.add_argument("--act", choices=["none", "gelu_tanh", "gelu_erf", "silu", "relu"], default="none",
+                    help="input activation folded into the quantizer (int8_linear(input_act=...))")
+    ap.add_argument("--op", choices=["linear", "tensorwise"], default="linear",
+                    help="linear: the whole layer (default); tensorwise: quantize_int8_tensorwise on the "
+                         "workload's activations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -156,7 +161,12 @@ def main():
         sys.exit("bench.py needs a GPU")
     qd.lib()
     w = workload(args.workload)
+    if args.op == "tensorwise":
+        return bench_tensorwise(args, w)
     int4 = w.kind == "w4a4"
+    act = ["none", "gelu_tanh", "gelu_erf", "silu", "relu"].index(args.act)
+    if act and int4:
+        sys.exit("an input activation is measured on the INT8 layer only")
     M, K, N = w.M, w.K, w.N
     dev = torch.device("cuda:0")
     log(f"[bench] {w.name}: generating inputs")
@@ -178,6 +188,8 @@ def main():
     def step():
         if int4:
             qd.convrot_w4a4_linear(x, wq, sw, bias, 256, ws, y)
+        elif act:
+            qd.int8_linear_act(x, wq, sw, bias, act, 256, ws, y)
         else:
             qd.int8_linear(x, wq, sw, bias, 256, ws, y)
 
@@ -207,6 +219,9 @@ def main():
     if int4:
         ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_int4(x, 256, aq, sx), reps, torch)
         ms_g = time_launches(lambda: qd.int4_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+    elif act:
+        ms_q = time_launches(lambda: qd.quantize_rowwise_act(x, act, 256, aq, sx), reps, torch)
+        ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     else:
         ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
         ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
@@ -217,6 +232,8 @@ def main():
     traffic = load_traffic(w.name)
     out = {
         "metric": (f"W4A4 rotated linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}" if int4 else
+                   f"INT8 linear TOPS with input_act={args.act} (incl. act+rotate+quant) & % of INT8 MFMA peak, "
+                   f"M{M}/K{K}/N{N}" if act else
                    f"INT8 linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}"),
         "value": round(tops, 3),
         "unit": "TOP/s",
@@ -229,7 +246,8 @@ def main():
         "vs_baseline": round(tops / (ops / (PAGE_MS[w.cid] * 1e-3) / 1e12), 4) if w.cid in PAGE_MS else None,
         "dtype": "i4 codes on i8 MFMA" if int4 else "i8",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": M, "K": K, "N": N, "rotation": "block-256 Walsh-Hadamard",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "input_act": args.act,
+                   "rotation": "block-256 Walsh-Hadamard",
                    "activations": "bf16 -> int4 codes in int8 storage" if int4 else "bf16",
                    "weights": ("packed int4 per-channel fp32 scale, unpacked to int8 in the GEMM" if int4
                                else "int8 per-channel fp32 scale"),
@@ -256,7 +274,63 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
-        out["cpu_baseline"] = cpu_baseline(x, y, wq, sw, b_bits, w, torch, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(x, y, wq, sw, b_bits, w, torch, args.cpu_budget, act)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_tensorwise(args, w):
+    """quantize_int8_tensorwise on the workload's activation tensor: HBM-bound,
+    algorithmic bytes 3MK + 4 (BF16 in, codes out, one scale)."""
+    import numpy as np
+    import torch
+
+    import quantized_diffusion_amd as qd
+    from synth import iter_x
+
+    M, K = w.M, w.K
+    dev = torch.device("cuda:0")
+    log(f"[bench] tensorwise {w.name}: generating inputs")
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for r0, r1, bits in iter_x(w):
+        x[r0:r1].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    q = torch.empty((M, K), dtype=torch.int8, device=dev)
+    s = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = torch.empty(qd.tensorwise_workspace_size(), dtype=torch.uint8, device=dev)
+
+    def step():
+        qd.quantize_int8_tensorwise(x, q, s, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = time_launches(step, args.steps, torch)
+    alg = 3.0 * M * K + 4.0
+    gbs = alg / (ms * 1e-3) / 1e9
+    out = {
+        "metric": f"tensor-wise INT8 quantize GB/s (3MK+4 algorithmic bytes), M{M}/K{K}",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 -> i8", "data": "synthetic",
+        "config": {"workload": w.name + " activations", "M": M, "K": K, "op": "quantize_int8_tensorwise",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "tw_amax_kernel + tw_quant_kernel (one step)",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "note": "two passes over x: 5MK bytes move per step (x read twice)"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        O = oracle.default()
+        xh = x.view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        qo, so = O.quantize_tensorwise(xh, "bf16")
+        t = time.perf_counter() - t0
+        same = bool(np.array_equal(q.cpu().numpy(), qo)) and bool(s.cpu().numpy()[0] == so[0])
+        out["cpu_baseline"] = {"value": round(alg / t / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(),
+                               "kind": "oracle", "sample": f"the whole {M}x{K} tensor", "seconds": round(t, 3),
+                               "sample_parity": {"codes_and_scale_identical": same}}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

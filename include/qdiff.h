@@ -72,6 +72,18 @@ typedef enum {
 
 typedef enum { QD_F32 = 0, QD_BF16 = 1, QD_F16 = 2 } qd_dtype_t;
 
+/* Input activations (int8_linear's input_act, comfy-kitchen 0.2.40, "HIP
+ * backend"): applied to each input element inside the quantizer's load.
+ *   GELU_TANH  x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+ *   GELU_ERF   x/2 (1 + erf(x / sqrt(2)))
+ *   SILU       x / (1 + exp(-x))
+ *   RELU       x if x > 0, else +0
+ * The result is act(x) rounded to nearest-even in the input's 16-bit type
+ * (what an unfused act() would store), so activations need BF16 or FP16
+ * inputs. */
+typedef enum { QD_ACT_NONE = 0, QD_ACT_GELU_TANH = 1, QD_ACT_GELU_ERF = 2, QD_ACT_SILU = 3,
+               QD_ACT_RELU = 4 } qd_act_t;
+
 /* Largest K accepted by the quantizers (a row stays in registers). */
 #define QD_MAX_K_QUANT 65536
 /* Largest K accepted by the GEMMs (keeps K * 128 * 128 < 2^31). */
@@ -157,6 +169,38 @@ qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t
                            const float* w_scale, const void* bias_bf16, int32_t rotate_block,
                            void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
                            hipStream_t stream);
+
+/*
+ * int8_linear(input_act=...) (comfy-kitchen 0.2.40, "HIP backend": the
+ * activation is folded into the quantizer's load so act's output never goes
+ * to memory): y = act(x) W^T + b through the same path as qd_int8_linear,
+ * where act(x) is the activation rounded to x's type.  x_dtype must be BF16
+ * or FP16 when input_act != QD_ACT_NONE; with GELU or SiLU, K <= 32768.
+ * Otherwise exactly qd_int8_linear (QD_ACT_NONE gives identical results).
+ */
+qd_status_t qd_int8_linear_act(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               qd_act_t input_act, const int8_t* wq, int64_t N, int64_t ldw,
+                               const float* w_scale, const void* bias_bf16, int32_t rotate_block,
+                               void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
+                               hipStream_t stream);
+
+/*
+ * The quantizer half of qd_int8_linear_act: codes and row scales of act(x),
+ * rotated (rotate_block 256, as qd_quantize_and_rotate_rowwise) or not
+ * (rotate_block 0, as qd_quantize_int8_rowwise).  Requirements as those two
+ * plus the activation's (16-bit input; K <= 32768 for GELU and SiLU).
+ */
+qd_status_t qd_quantize_rowwise_act(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                    qd_act_t input_act, int32_t rotate_block, int8_t* q, int64_t ldq,
+                                    float* row_scale, hipStream_t stream);
+
+/*
+ * The activation alone, elementwise, by the same device code the quantizer
+ * uses: out[i] = act(x[i]) in x's 16-bit type (BF16 or FP16 bits), n
+ * elements, 2-byte aligned.  For verifying every input value of a type.
+ */
+qd_status_t qd_input_act(const void* x, qd_dtype_t x_dtype, int64_t n, qd_act_t act, void* out,
+                         hipStream_t stream);
 
 /*
  * dequantize_int8_simple / dequantize_int8_simple_dtype (comfy-kitchen,

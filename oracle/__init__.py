@@ -68,6 +68,11 @@ def _bind(L):
     L.oracle_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P]
     L.oracle_epilogue.argtypes = [P, I64, I64, P, P, P, P]
     L.oracle_epilogue_f32.argtypes = [P, I64, I64, P, P, P, P]
+    L.oracle_linear_act.restype = I
+    L.oracle_linear_act.argtypes = [P, I, I64, I64, I64, I, P, P, P, I64, I, I, P]
+    L.oracle_quantize_rowwise_act.restype = I
+    L.oracle_quantize_rowwise_act.argtypes = [P, I, I64, I64, I64, I, I, I, P, I64, P]
+    L.oracle_input_act.argtypes = [P, I, I64, I, P]
     L.oracle_linear.restype = I
     L.oracle_linear.argtypes = [P, I, I64, I64, I64, P, P, P, I64, I, I, P]
     L.oracle_linear_points.argtypes = [P, I64, P, P, P, P, P, P, I64, P, P]
@@ -125,13 +130,17 @@ class Oracle:
         self.L.oracle_quantize_rows(_p(v), M, K, qmax, _p(q), K, _p(s))
         return q, s
 
-    def quantize_rowwise(self, x, dtype: str = "bf16", block: int = 256, qmax: int = 127):
-        """(codes int8 [M, K], row scales float32 [M]) of rotate-then-quantize."""
+    def quantize_rowwise(self, x, dtype: str = "bf16", block: int = 256, qmax: int = 127, act: int = 0):
+        """(codes int8 [M, K], row scales float32 [M]) of [activation,] rotate-then-quantize."""
         x = _x_in(x, dtype)
         M, K = x.shape
         q = np.empty((M, K), np.int8)
         s = np.empty(M, np.float32)
-        rc = self.L.oracle_quantize_rowwise(_p(x), _DTYPES[dtype], M, K, K, block, qmax, _p(q), K, _p(s))
+        if act:
+            rc = self.L.oracle_quantize_rowwise_act(_p(x), _DTYPES[dtype], M, K, K, block, act, qmax, _p(q), K,
+                                                    _p(s))
+        else:
+            rc = self.L.oracle_quantize_rowwise(_p(x), _DTYPES[dtype], M, K, K, block, qmax, _p(q), K, _p(s))
         if rc:
             raise ValueError(f"oracle_quantize_rowwise failed rc={rc}")
         return q, s
@@ -183,8 +192,15 @@ class Oracle:
         self.L.oracle_epilogue_f32(_p(acc), M, N, _p(sx), _p(sw), _p(b), _p(t))
         return t
 
+    def input_act(self, x, dtype: str, act: int) -> np.ndarray:
+        """act(x) elementwise, rounded to the 16-bit input type; uint16 bits."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        out = np.empty_like(x)
+        self.L.oracle_input_act(_p(x), _DTYPES[dtype], x.size, act, _p(out))
+        return out
+
     def linear(self, x, wq, sw, bias=None, dtype: str = "bf16", block: int = 256,
-               qmax: int = 127) -> np.ndarray:
+               qmax: int = 127, act: int = 0) -> np.ndarray:
         """The whole layer: BF16 output bits [M, N]."""
         x = _x_in(x, dtype)
         M, K = x.shape
@@ -193,7 +209,7 @@ class Oracle:
         sw = np.ascontiguousarray(sw, dtype=np.float32)
         b = None if bias is None else np.ascontiguousarray(bias, dtype=np.uint16)
         y = np.empty((M, N), np.uint16)
-        rc = self.L.oracle_linear(_p(x), _DTYPES[dtype], M, K, K, _p(wq), _p(sw), _p(b), N,
+        rc = self.L.oracle_linear_act(_p(x), _DTYPES[dtype], M, K, K, act, _p(wq), _p(sw), _p(b), N,
                                   block, qmax, _p(y))
         if rc:
             raise RuntimeError(f"oracle_linear failed rc={rc}")

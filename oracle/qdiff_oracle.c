@@ -40,6 +40,13 @@
  *  - Dequantization out = fl(q * s), optionally rounded to BF16.
  *  - INT4 packing: byte i of a row holds code 2i in its low nibble and code
  *    2i+1 in its high nibble, both two's complement.
+ *  - Input activation (int8_linear's input_act, comfy-kitchen 0.2.40, "HIP
+ *    backend"): act(x) is applied to each input element and rounded to
+ *    nearest in the input's 16-bit type, as an unfused act() would store
+ *    it (an exact activation value is never halfway between two neighbours);
+ *    the layer then proceeds on those values.  GELU (tanh form
+ *    with 0.044715), GELU (erf form), SiLU and ReLU, evaluated in long
+ *    double.
  */
 #include <math.h>
 #include <stdint.h>
@@ -95,6 +102,75 @@ static float load_elem(const void* x, int dtype, int64_t idx) {
     }
 }
 
+/* ---- input activations --------------------------------------------------- */
+
+#define ORACLE_ACT_GELU_TANH 1
+#define ORACLE_ACT_GELU_ERF 2
+#define ORACLE_ACT_SILU 3
+#define ORACLE_ACT_RELU 4
+
+/* The activation in long double, written without cancellation:
+ * x/2 (1 + tanh u) = x / (1 + e^(-2u)); x/2 (1 + erf(x/sqrt2)) = x/2 erfc(-x/sqrt2). */
+static long double act_value(int act, long double x) {
+    const long double pi = acosl(-1.0L);
+    switch (act) {
+        case ORACLE_ACT_GELU_TANH: {
+            long double u = sqrtl(2.0L / pi) * (x + 0.044715L * x * x * x);
+            return x / (1.0L + expl(-2.0L * u));
+        }
+        case ORACLE_ACT_GELU_ERF: return 0.5L * x * erfcl(-x / sqrtl(2.0L));
+        case ORACLE_ACT_SILU: return x / (1.0L + expl(-x));
+        case ORACLE_ACT_RELU: return x > 0.0L ? x : 0.0L;
+        default: return x;
+    }
+}
+
+/* Round the computed activation d to nearest on the grid of a binary type with
+ * `mant` fraction bits and smallest normal exponent `emin` (subnormals
+ * included).  The exact activation is never halfway between grid points; a
+ * computed d that is exactly halfway is x/2 with the positive remainder
+ * x/2 * g(x) (g = tanh(u), tanh(x/2) or erf(x/sqrt2)) lost to rounding, which
+ * happens for the smallest |x|, so such a d is rounded up. */
+static float round_to_grid(long double d, int mant, int emin) {
+    if (d == 0.0L) return (float)d;
+    int e = ilogbl(d);
+    if (e < emin) e = emin;
+    long double t = ldexpl(d, mant - e);      /* |t| < 2^(mant+1), exact */
+    long double r = floorl(t + 0.5L);         /* nearest, halfway upwards */
+    if (r == 0.0L && d < 0.0L) r = -0.0L;
+    return (float)(r * ldexpl(1.0L, e - mant));
+}
+
+/* act(v) rounded to the 16-bit input type (BF16: 7 fraction bits, FP16: 10). */
+static float act_elem(int act, int dtype, float v) {
+    if (act == 0) return v;
+    long double a = act_value(act, (long double)v);
+    return dtype == ORACLE_BF16 ? round_to_grid(a, 7, -126) : round_to_grid(a, 10, -14);
+}
+
+/* Exact FP16 bits of a float that lies on the FP16 grid. */
+static uint16_t f16_bits_exact(float f) {
+    uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    float a = fabsf(f);
+    if (a == 0.0f) return sign;
+    int e = ilogbf(a);
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    if (e < -14) return (uint16_t)(sign | (uint16_t)ldexpf(a, 24));
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)((int)ldexpf(a, 10 - e) - 1024));
+}
+
+/* out[i] = act(x[i]) in the 16-bit input type (BF16 or FP16 bits). */
+void oracle_input_act(const uint16_t* x, int dtype, int64_t n, int act, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        float v = load_elem(x, dtype, i);
+        float a = act_elem(act, dtype, v);
+        uint32_t u;
+        memcpy(&u, &a, 4);
+        out[i] = dtype == ORACLE_BF16 ? (uint16_t)(u >> 16) : f16_bits_exact(a);
+    }
+}
+
 /* ---- rotation ---------------------------------------------------------- */
 
 /* In-place normalised Walsh-Hadamard transform of one 256-element block. */
@@ -111,21 +187,28 @@ void oracle_hadamard256(float* u) {
     for (int j = 0; j < 256; j++) u[j] = u[j] * 0.0625f;
 }
 
-/* Widen rows of x ([M, K], row stride ldx elements) to FP32 and, when
- * block == 256, rotate every 256-block.  out is [M, K] dense.
- * Returns 0, or -1 for an unsupported block / K. */
-int oracle_rotate_rows(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
-                       int block, float* out) {
+/* Widen rows of x ([M, K], row stride ldx elements) to FP32, apply the input
+ * activation `act` (0: none; 16-bit inputs only) and, when block == 256,
+ * rotate every 256-block.  out is [M, K] dense.
+ * Returns 0, or -1 for an unsupported block / K / activation. */
+int oracle_rotate_rows_act(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                           int block, int act, float* out) {
     if (block != 0 && block != 256) return -1;
     if (block == 256 && K % 256 != 0) return -1;
+    if (act != 0 && dtype == ORACLE_F32) return -1;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; m++) {
         float* row = out + m * K;
-        for (int64_t k = 0; k < K; k++) row[k] = load_elem(x, dtype, m * ldx + k);
+        for (int64_t k = 0; k < K; k++) row[k] = act_elem(act, dtype, load_elem(x, dtype, m * ldx + k));
         if (block == 256)
             for (int64_t b = 0; b < K; b += 256) oracle_hadamard256(row + b);
     }
     return 0;
+}
+
+int oracle_rotate_rows(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                       int block, float* out) {
+    return oracle_rotate_rows_act(x, dtype, M, K, ldx, block, 0, out);
 }
 
 /* ---- per-row symmetric quantization ------------------------------------ */
@@ -156,15 +239,21 @@ void oracle_quantize_rows(const float* v, int64_t M, int64_t K, int qmax,
     }
 }
 
-/* Rotate (block 256) or not (block 0), then quantize per row. */
-int oracle_quantize_rowwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
-                            int block, int qmax, int8_t* q, int64_t ldq, float* scale) {
+/* Activation (act, 0 for none), rotation (block 256) or not (block 0), then
+ * per-row quantization. */
+int oracle_quantize_rowwise_act(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                                int block, int act, int qmax, int8_t* q, int64_t ldq, float* scale) {
     float* v = (float*)malloc((size_t)(M * K) * sizeof(float));
     if (!v) return -2;
-    int rc = oracle_rotate_rows(x, dtype, M, K, ldx, block, v);
+    int rc = oracle_rotate_rows_act(x, dtype, M, K, ldx, block, act, v);
     if (rc == 0) oracle_quantize_rows(v, M, K, qmax, q, ldq, scale);
     free(v);
     return rc;
+}
+
+int oracle_quantize_rowwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                            int block, int qmax, int8_t* q, int64_t ldq, float* scale) {
+    return oracle_quantize_rowwise_act(x, dtype, M, K, ldx, block, 0, qmax, q, ldq, scale);
 }
 
 /* ---- tensor-wise symmetric quantization --------------------------------- */
@@ -253,20 +342,26 @@ void oracle_epilogue_f32(const int32_t* acc, int64_t M, int64_t N, const float* 
  * INT8 codes (already rotated offline), sw [N], bias [N] BF16 or NULL,
  * y [M, N] BF16 bits.  qmax 127 (INT8) or 7 (INT4 codes in INT8 storage).
  * Returns 0, -1 (bad arguments), -2 (no memory) or -3 (INT32 overflow). */
-int oracle_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
-                  const int8_t* wq, const float* sw, const uint16_t* bias, int64_t N,
-                  int block, int qmax, uint16_t* y) {
+int oracle_linear_act(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int act,
+                      const int8_t* wq, const float* sw, const uint16_t* bias, int64_t N,
+                      int block, int qmax, uint16_t* y) {
     int8_t* q = (int8_t*)malloc((size_t)(M * K));
     float* sx = (float*)malloc((size_t)M * sizeof(float));
     int32_t* acc = (int32_t*)malloc((size_t)(M * N) * sizeof(int32_t));
     int rc = (q && sx && acc) ? 0 : -2;
-    if (rc == 0) rc = oracle_quantize_rowwise(x, dtype, M, K, ldx, block, qmax, q, K, sx);
+    if (rc == 0) rc = oracle_quantize_rowwise_act(x, dtype, M, K, ldx, block, act, qmax, q, K, sx);
     if (rc == 0 && oracle_gemm_i32(q, M, K, K, wq, N, K, acc) != 0) rc = -3;
     if (rc == 0) oracle_epilogue(acc, M, N, sx, sw, bias, y);
     free(q);
     free(sx);
     free(acc);
     return rc;
+}
+
+int oracle_linear(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                  const int8_t* wq, const float* sw, const uint16_t* bias, int64_t N,
+                  int block, int qmax, uint16_t* y) {
+    return oracle_linear_act(x, dtype, M, K, ldx, 0, wq, sw, bias, N, block, qmax, y);
 }
 
 /* Selected outputs only: y_out[i] = y[rows[i], cols[i]] for a layer whose

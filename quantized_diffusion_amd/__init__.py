@@ -31,13 +31,15 @@ __all__ = [
     "quantize_int8_rowwise", "int8_linear", "int8_scaled_mm", "int8_gemm_i32", "dequantize_int8",
     "prepare_weights", "workspace_size", "EXPORTED_SYMBOLS", "pack_int4", "prepare_weights_w4a4",
     "int4_scaled_mm", "int4_gemm_i32", "convrot_w4a4_linear", "quantize_int8_tensorwise",
-    "tensorwise_workspace_size", "int8_scaled_mm_ex",
+    "tensorwise_workspace_size", "int8_scaled_mm_ex", "input_act", "quantize_rowwise_act", "int8_linear_act",
+    "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
 
 QD_OK, QD_EINVAL, QD_EUNSUPPORTED, QD_EHIP = 0, 1, 2, 3
 QD_F32, QD_BF16, QD_F16 = 0, 1, 2
+ACT_NONE, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SILU, ACT_RELU = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (
     "qd_last_error", "qd_version", "qd_quantize_and_rotate_rowwise",
@@ -45,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "qd_int8_linear_workspace_size", "qd_int8_linear", "qd_dequantize_int8", "qd_int8_gemm_i32",
     "qd_pack_int4", "qd_int4_scaled_mm", "qd_int4_gemm_i32", "qd_convrot_w4a4_linear",
     "qd_quantize_tensorwise_workspace_size", "qd_quantize_int8_tensorwise", "qd_int8_scaled_mm_ex",
+    "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act",
 )
 
 
@@ -99,6 +102,12 @@ def lib():
         L.qd_quantize_int8_tensorwise.argtypes = [P, St, I64, I64, I64, P, I64, P, P, SZ, P]
         L.qd_int8_scaled_mm_ex.restype = St
         L.qd_int8_scaled_mm_ex.argtypes = [P, I64, I64, I64, P, I64, P, I64, I64, P, I64, P, P, I64, P]
+        L.qd_int8_linear_act.restype = St
+        L.qd_int8_linear_act.argtypes = [P, St, I64, I64, I64, St, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
+        L.qd_quantize_rowwise_act.restype = St
+        L.qd_quantize_rowwise_act.argtypes = [P, St, I64, I64, I64, St, I32, P, I64, P, P]
+        L.qd_input_act.restype = St
+        L.qd_input_act.argtypes = [P, St, I64, St, P, P]
         _lib = L
     return _lib
 
@@ -335,6 +344,61 @@ def int8_linear(x, wq, w_scale, bias=None, rotate_block: int = 256, workspace=No
                                 _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
                                 _stream(dev)))
+    return out
+
+
+def int8_linear_act(x, wq, w_scale, bias=None, input_act: int = ACT_NONE, rotate_block: int = 256,
+                    workspace=None, out=None):
+    """int8_linear(input_act=...): y = act(x) W^T + b, the activation applied in
+    the quantizer's load (act(x) rounded to x's dtype, BF16 or FP16)."""
+    torch = _torch()
+    _mat(x, "x"), _mat(wq, "wq")
+    dev = _dev(x, wq, w_scale, bias, workspace, out)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("x and wq disagree on K")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    need = workspace_size(M, K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_int8_linear_act(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act), _ptr(wq), N,
+                                    wq.stride(0), _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
+                                    _stream(dev)))
+    return out
+
+
+def quantize_rowwise_act(x, input_act: int, rotate_block: int = 256, out_q=None, out_scale=None):
+    """Codes and row scales of act(x) (rotated when rotate_block == 256)."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, out_q, out_scale)
+    M, K = x.shape
+    if out_q is None:
+        out_q = torch.empty((M, (K + 15) // 16 * 16), dtype=torch.int8, device=dev)[:, :K]
+    if out_scale is None:
+        out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _mat(out_q, "q")
+    _check(lib().qd_quantize_rowwise_act(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act), rotate_block,
+                                         _ptr(out_q), out_q.stride(0), _ptr(out_scale), _stream(dev)))
+    return out_q, out_scale
+
+
+def input_act(x, act: int, out=None):
+    """act(x) elementwise in x's 16-bit dtype (the quantizer's activation, alone)."""
+    torch = _torch()
+    dev = _dev(x, out)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib().qd_input_act(_ptr(x), _dtype_code(x), x.numel(), int(act), _ptr(out), _stream(dev)))
     return out
 
 

@@ -82,13 +82,29 @@ qd_status_t check_gemm(const char* fn, const int8_t* aq, int64_t M, int64_t K, i
     return QD_OK;
 }
 
+// An input activation needs a 16-bit input (the activation's result is
+// rounded to that type); the FP64 activations allow rows of up to 32768.
+qd_status_t check_act(const char* fn, qd_act_t act, qd_dtype_t dt, int64_t K) {
+    if ((int)act < (int)QD_ACT_NONE || (int)act > (int)QD_ACT_RELU)
+        return fail(QD_EUNSUPPORTED, fn, "unknown activation %d", (int)act);
+    if (act == QD_ACT_NONE) return QD_OK;
+    if (dt != QD_BF16 && dt != QD_F16)
+        return fail(QD_EUNSUPPORTED, fn, "an input activation needs a BF16 or FP16 input");
+    if (act != QD_ACT_RELU && K > 32768)
+        return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds 32768 with this activation", (long long)K);
+    return QD_OK;
+}
+
 qd_status_t quantize_impl(const char* fn, const void* x, qd_dtype_t dt, int64_t M, int64_t K,
                           int64_t ldx, bool rotate, int32_t block, int qmax, int8_t* q,
-                          int64_t ldq, float* scale, hipStream_t stream) {
+                          int64_t ldq, float* scale, hipStream_t stream, qd_act_t act = QD_ACT_NONE) {
     qd_status_t st = check_quant(fn, x, dt, M, K, ldx, rotate, block, q, ldq, scale);
     if (st != QD_OK) return st;
+    st = check_act(fn, act, dt, K);
+    if (st != QD_OK) return st;
     if (M == 0) return ok();
-    return hip_status(fn, qd::launch_rotquant(x, (int)dt, rotate, qmax, M, K, ldx, q, ldq, scale, stream));
+    return hip_status(fn, qd::launch_rotquant(x, (int)dt, rotate, qmax, M, K, ldx, q, ldq, scale, stream,
+                                              (int)act));
 }
 
 constexpr size_t kAlign = 256;
@@ -186,12 +202,11 @@ size_t qd_int8_linear_workspace_size(int64_t M, int64_t K) {
     return ws_codes_bytes(M, K) + round_up((size_t)M * sizeof(float), kAlign);
 }
 
-qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
-                           int64_t ldx, const int8_t* wq, int64_t N, int64_t ldw,
-                           const float* w_scale, const void* bias_bf16, int32_t rotate_block,
-                           void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
-                           hipStream_t stream) {
-    const char* fn = "qd_int8_linear";
+static qd_status_t linear_impl(const char* fn, const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                               int64_t ldx, qd_act_t act, const int8_t* wq, int64_t N, int64_t ldw,
+                               const float* w_scale, const void* bias_bf16, int32_t rotate_block,
+                               void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
+                               hipStream_t stream) {
     if (rotate_block != 0 && rotate_block != 256)
         return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 0 or 256 (got %d)", rotate_block);
     const bool rotate = rotate_block == 256;
@@ -208,15 +223,59 @@ qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t
     float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_codes_bytes(M, K));
     qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, rotate, rotate_block, aq, ldq, sx);
     if (st != QD_OK) return st;
+    st = check_act(fn, act, x_dtype, K);
+    if (st != QD_OK) return st;
     st = check_gemm(fn, aq, M, K, ldq, wq, N, ldw, y_bf16, ldy, 8);
     if (st != QD_OK) return st;
     if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
     if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
         return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
-    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, rotate, 127, M, K, ldx, aq, ldq, sx, stream);
+    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, rotate, 127, M, K, ldx, aq, ldq, sx, stream, (int)act);
     if (e != hipSuccess) return hip_status(fn, e);
     return hip_status(fn, qd::launch_gemm_bf16(aq, ldq, sx, wq, ldw, w_scale, bias_bf16, y_bf16,
                                                ldy, M, N, K, stream));
+}
+
+qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                           int64_t ldx, const int8_t* wq, int64_t N, int64_t ldw,
+                           const float* w_scale, const void* bias_bf16, int32_t rotate_block,
+                           void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
+                           hipStream_t stream) {
+    return linear_impl("qd_int8_linear", x, x_dtype, M, K, ldx, QD_ACT_NONE, wq, N, ldw, w_scale, bias_bf16,
+                       rotate_block, workspace, workspace_bytes, y_bf16, ldy, stream);
+}
+
+qd_status_t qd_int8_linear_act(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                               qd_act_t input_act, const int8_t* wq, int64_t N, int64_t ldw,
+                               const float* w_scale, const void* bias_bf16, int32_t rotate_block,
+                               void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
+                               hipStream_t stream) {
+    return linear_impl("qd_int8_linear_act", x, x_dtype, M, K, ldx, input_act, wq, N, ldw, w_scale, bias_bf16,
+                       rotate_block, workspace, workspace_bytes, y_bf16, ldy, stream);
+}
+
+qd_status_t qd_quantize_rowwise_act(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                    qd_act_t input_act, int32_t rotate_block, int8_t* q, int64_t ldq,
+                                    float* row_scale, hipStream_t stream) {
+    const char* fn = "qd_quantize_rowwise_act";
+    if (rotate_block != 0 && rotate_block != 256)
+        return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 0 or 256 (got %d)", rotate_block);
+    return quantize_impl(fn, x, x_dtype, M, K, ldx, rotate_block == 256, rotate_block, 127, q, ldq, row_scale,
+                         stream, input_act);
+}
+
+qd_status_t qd_input_act(const void* x, qd_dtype_t x_dtype, int64_t n, qd_act_t act, void* out,
+                         hipStream_t stream) {
+    const char* fn = "qd_input_act";
+    if (n < 0) return fail(QD_EINVAL, fn, "need n >= 0 (n=%lld)", (long long)n);
+    if (n > 0 && (!x || !out)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (x_dtype != QD_BF16 && x_dtype != QD_F16)
+        return fail(QD_EUNSUPPORTED, fn, "an input activation needs a BF16 or FP16 input");
+    qd_status_t st = check_act(fn, act, x_dtype, 0);
+    if (st != QD_OK) return st;
+    if (((uintptr_t)x & 1u) || ((uintptr_t)out & 1u)) return fail(QD_EUNSUPPORTED, fn, "x and out must be 2-byte aligned");
+    if (n == 0) return ok();
+    return hip_status(fn, qd::launch_input_act(x, (int)x_dtype, n, (int)act, out, stream));
 }
 
 qd_status_t qd_dequantize_int8(const int8_t* q, int64_t M, int64_t K, int64_t ldq,

@@ -8,8 +8,14 @@
 namespace qd {
 
 // dtype: 0 = FP32, 1 = BF16, 2 = FP16.  qmax 127 or 7 (7 only with rotate).
+// act: input activation (0 none, 1 GELU tanh, 2 GELU erf, 3 SiLU, 4 ReLU);
+// non-zero only with 16-bit inputs and qmax 127.
 hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int64_t M, int64_t K,
-                           int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream);
+                           int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream,
+                           int act = 0);
+
+// out[i] = act(x[i]) rounded to the 16-bit input type (dtype 1 BF16, 2 FP16).
+hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* out, hipStream_t stream);
 
 // Tensor-wise quantization: two launches; partial holds kTensorwisePartials
 // floats (K % 16 == 0).

@@ -53,9 +53,38 @@
 #include "qd_device.h"
 #include "qd_launch.h"
 #include "qd_quant.h"
+#include "qd_act.h"
 
 namespace qd {
 namespace {
+
+template <class In> struct In16 { static constexpr int value = 0; };
+template <> struct In16<InBF16> { static constexpr int value = 1; };
+template <> struct In16<InF16> { static constexpr int value = 2; };
+
+// act() on the eight 16-bit values of a chunk, results in the same type.
+template <int ACT, int IN16>
+__device__ __forceinline__ u32x4 act_chunk(u32x4 d) {
+    if (IN16 == 0) return d;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t out = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t b = (d[w] >> (16 * h)) & 0xFFFFu;
+            const float f = IN16 == 1 ? bits_f(b << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+            const float a = input_act<ACT, IN16>(f);
+            const uint32_t r = IN16 == 1 ? f_bits(a) >> 16 : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a);
+            out |= r << (16 * h);
+        }
+        d[w] = out;
+    }
+    return d;
+}
+
+// Largest workgroup: 1024 threads (4 waves per SIMD, 128 VGPRs); 512 with an
+// FP64 activation, whose temporaries need more registers.
+template <int ACT> struct kMaxThreads { static constexpr int value = (ACT == 0 || ACT == 4) ? 1024 : 512; };
 
 constexpr int kStageStride = 288;                 // bytes per block image in LDS (256 + 32: spreads banks)
 constexpr int kStageWave = 16 * kStageStride;     // per wave: 16 quads
@@ -81,8 +110,9 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
                                                float* __restrict__ scale, uint8_t* img);
 
 // STAGE (rotated path only): codes leave through the LDS block images.
-template <class In, bool ROT, int QMAX, bool STAGE>
-__global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restrict__ x,
+// ACT: input activation applied to each widened element (16-bit inputs).
+template <class In, bool ROT, int QMAX, bool STAGE, int ACT>
+__global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const uint8_t* __restrict__ x,
                                                         int64_t ldx_bytes, int M, int K, int nb,
                                                         int R, int8_t* __restrict__ q,
                                                         int64_t ldq, float* __restrict__ scale) {
@@ -112,11 +142,19 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
         // registers.  Quads never mix active and idle lanes.
         const int lrow = min(min(blockIdx.x * R + min(rl, R - 1), row), M - 1);
         const uint8_t* src = x + (int64_t)lrow * ldx_bytes + (int64_t)blk * 256 * ESZ;
+        u32x4 d[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const u32x4 d = *reinterpret_cast<const u32x4*>(src + (i * 4 + ql) * 16);
-            widen(In{}, d, &v[i * E]);
+        for (int i = 0; i < NI; ++i) d[i] = *reinterpret_cast<const u32x4*>(src + (i * 4 + ql) * 16);
+        if (ACT != ACT_NONE) {
+            // on the raw 16-bit words, before widening: fewer live registers
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                d[i] = act_chunk<ACT, In16<In>::value>(d[i]);
+                __builtin_amdgcn_sched_barrier(0);   // one chunk at a time: bounded FP64 temporaries
+            }
         }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) widen(In{}, d[i], &v[i * E]);
     } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) v[j] = 0.0f;
@@ -126,7 +164,8 @@ __global__ __launch_bounds__(1024) void rotquant_kernel(const uint8_t* __restric
             for (int i = 0; i < NI; ++i) {
                 const int c = i * 4 + ql;
                 if (blk * 256 + c * E < K) {
-                    const u32x4 d = *reinterpret_cast<const u32x4*>(src + c * 16);
+                    u32x4 d = *reinterpret_cast<const u32x4*>(src + c * 16);
+                    if (ACT != ACT_NONE) d = act_chunk<ACT, In16<In>::value>(d);
                     widen(In{}, d, &v[i * E]);
                 }
             }
@@ -264,19 +303,19 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
     }
 }
 
-template <class In, bool ROT, int QMAX, bool STAGE>
+template <class In, bool ROT, int QMAX, bool STAGE, int ACT>
 hipError_t launch_staged(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                          float* scale, hipStream_t stream, int R, int threads) {
     constexpr int ESZ = 16 / In::E;
     const int nb = (int)((K + 255) / 256);
     const int64_t grid = (M + R - 1) / R;
     const size_t lds = STAGE ? (size_t)(threads / 64) * kStageWave : 0;
-    rotquant_kernel<In, ROT, QMAX, STAGE><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
+    rotquant_kernel<In, ROT, QMAX, STAGE, ACT><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
         static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
     return hipGetLastError();
 }
 
-template <class In, bool ROT, int QMAX>
+template <class In, bool ROT, int QMAX, int ACT = ACT_NONE>
 hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                         float* scale, hipStream_t stream) {
     const int nb = (int)((K + 255) / 256);
@@ -284,35 +323,91 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     // leaves the fewest idle lanes in whole waves, preferring ~256 threads.
     int R = 1, best_threads = 0;
     double best_waste = 2.0;
+    constexpr int MAXT = kMaxThreads<ACT>::value;
     const int r0 = nb >= 64 ? 1 : 64 / nb;
-    for (int r = r0; r <= 2 * r0 && 4 * r * nb <= 1024; ++r) {
+    for (int r = r0; r <= 2 * r0 && 4 * r * nb <= MAXT; ++r) {
         const int th = (4 * r * nb + 63) / 64 * 64;
         const double waste = (double)(th - 4 * r * nb) / th;
         if (waste < best_waste - 1e-9) { best_waste = waste; R = r; best_threads = th; }
     }
     if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
+    if (best_threads > MAXT) return hipErrorInvalidValue;   // rows longer than the caller's checks allow
     if (ROT)
-        return launch_staged<In, ROT, QMAX, true>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
-    return launch_staged<In, ROT, QMAX, false>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
+        return launch_staged<In, ROT, QMAX, true, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
+    return launch_staged<In, ROT, QMAX, false, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
 }
 
 }  // namespace
 
 hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int64_t M, int64_t K,
-                           int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream) {
+                           int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream, int act) {
 #define QD_DISPATCH(IN)                                                                       \
     if (rotate) {                                                                             \
         if (qmax == 7) return launch_typed<IN, true, 7>(x, M, K, ldx, q, ldq, scale, stream); \
         return launch_typed<IN, true, 127>(x, M, K, ldx, q, ldq, scale, stream);              \
     }                                                                                         \
     return launch_typed<IN, false, 127>(x, M, K, ldx, q, ldq, scale, stream);
+// INT8 codes with an input activation: 16-bit inputs only (checked by the caller).
+#define QD_DISPATCH_ACT(IN, A)                                                                \
+    if (rotate) return launch_typed<IN, true, 127, A>(x, M, K, ldx, q, ldq, scale, stream);   \
+    return launch_typed<IN, false, 127, A>(x, M, K, ldx, q, ldq, scale, stream);
+#define QD_DISPATCH_ACTS(IN)                                                                  \
+    switch (act) {                                                                            \
+        case ACT_GELU_TANH: QD_DISPATCH_ACT(IN, ACT_GELU_TANH)                                \
+        case ACT_GELU_ERF: QD_DISPATCH_ACT(IN, ACT_GELU_ERF)                                  \
+        case ACT_SILU: QD_DISPATCH_ACT(IN, ACT_SILU)                                          \
+        default: QD_DISPATCH_ACT(IN, ACT_RELU)                                                \
+    }
+    if (act != ACT_NONE) {
+        if (dtype == 1) { QD_DISPATCH_ACTS(InBF16) }
+        QD_DISPATCH_ACTS(InF16)
+    }
     switch (dtype) {
         case 0: QD_DISPATCH(InF32)
         case 1: QD_DISPATCH(InBF16)
         default: QD_DISPATCH(InF16)
     }
 #undef QD_DISPATCH
+#undef QD_DISPATCH_ACT
+#undef QD_DISPATCH_ACTS
+}
+
+namespace {
+
+template <int ACT, int IN16>
+__global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                  uint16_t* __restrict__ out) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const uint16_t b = x[i];
+        float f;
+        if (IN16 == 1) f = bits_f((uint32_t)b << 16);
+        else f = (float)__builtin_bit_cast(_Float16, b);
+        const float a = input_act<ACT, IN16>(f);
+        // a is exactly representable in the 16-bit type
+        out[i] = IN16 == 1 ? (uint16_t)(f_bits(a) >> 16) : __builtin_bit_cast(uint16_t, (_Float16)a);
+    }
+}
+
+template <int IN16>
+hipError_t launch_act16(const void* x, int64_t n, int act, void* out, hipStream_t stream) {
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    const uint16_t* xi = static_cast<const uint16_t*>(x);
+    uint16_t* o = static_cast<uint16_t*>(out);
+    switch (act) {
+        case ACT_GELU_TANH: act_kernel<ACT_GELU_TANH, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
+        case ACT_GELU_ERF: act_kernel<ACT_GELU_ERF, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
+        case ACT_SILU: act_kernel<ACT_SILU, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
+        case ACT_RELU: act_kernel<ACT_RELU, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
+        default: act_kernel<ACT_NONE, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* out, hipStream_t stream) {
+    return dtype == 1 ? launch_act16<1>(x, n, act, out, stream) : launch_act16<2>(x, n, act, out, stream);
 }
 
 }  // namespace qd

@@ -73,3 +73,96 @@ def sylvester(n: int) -> np.ndarray:
     j = np.arange(n)[None, :]
     pc = np.vectorize(popcount)(i & j)
     return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------
+# High-precision activations (Python decimal), for pinning the oracle's
+# input activations independently of any libm.
+
+import decimal as _dec
+
+_CTX = _dec.Context(prec=70, Emax=10 ** 7, Emin=-10 ** 7)
+
+
+def _atan_inv(n: int) -> _dec.Decimal:
+    """atan(1/n) by its Taylor series."""
+    with _dec.localcontext(_CTX):
+        x = _dec.Decimal(1) / n
+        x2 = x * x
+        term, total, k = x, x, 1
+        while True:
+            term = -term * x2
+            add = term / (2 * k + 1)
+            if abs(add) < _dec.Decimal(10) ** -75:
+                return total
+            total += add
+            k += 1
+
+
+def dec_pi() -> _dec.Decimal:
+    """pi by Machin's formula 16 atan(1/5) - 4 atan(1/239)."""
+    with _dec.localcontext(_CTX):
+        return 16 * _atan_inv(5) - 4 * _atan_inv(239)
+
+
+_PI = dec_pi()
+
+
+def dec_erfc(z: _dec.Decimal) -> _dec.Decimal:
+    """erfc(z): Taylor series of erf for |z| <= 6, continued fraction beyond."""
+    with _dec.localcontext(_CTX):
+        if z < 0:
+            return 2 - dec_erfc(-z)
+        if z <= 6:
+            z2 = z * z
+            term, total, n = z, z, 0
+            while True:
+                n += 1
+                term = -term * z2 / n
+                add = term / (2 * n + 1)
+                total += add
+                if abs(add) < _dec.Decimal(10) ** -68:
+                    break
+            return 1 - 2 / _PI.sqrt() * total
+        if z * z > 10 ** 6:
+            return _dec.Decimal(0)
+        # erfc(z) = e^{-z^2}/sqrt(pi) / (z + (1/2)/(z + 1/(z + (3/2)/(z + ...)))), evaluated backwards
+        t = z
+        for n in range(2000, 0, -1):
+            t = z + (_dec.Decimal(n) / 2) / t
+        return (-(z * z)).exp() / _PI.sqrt() / t
+
+
+def dec_act(act: int, x: float):
+    """The activation at x as a Decimal (None for 'rounds to zero with x's sign')."""
+    with _dec.localcontext(_CTX):
+        d = _dec.Decimal(x)
+        if act == 1:                                  # GELU, tanh form, 0.044715
+            u = (2 / _PI).sqrt() * (d + _dec.Decimal("0.044715") * d * d * d)
+            a = -2 * u
+            if a > 10 ** 5:
+                return None
+            return d / (1 + a.exp())
+        if act == 2:                                  # GELU, erf form
+            return _dec.Decimal("0.5") * d * dec_erfc(-d / _dec.Decimal(2).sqrt())
+        if act == 3:                                  # SiLU
+            if -d > 10 ** 5:
+                return None
+            return d / (1 + (-d).exp())
+        return d if d > 0 else _dec.Decimal(0)       # ReLU
+
+
+def round_grid(v: Fraction, mant: int, emin: int) -> Fraction:
+    """Round a rational to nearest-even on the grid of a binary type with `mant`
+    fraction bits and smallest normal exponent `emin` (subnormals included)."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - mant)
+    return (1 if v > 0 else -1) * rne_int(a / q) * q

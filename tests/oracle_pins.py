@@ -14,6 +14,7 @@ references.
 """
 from __future__ import annotations
 
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -411,4 +412,104 @@ def check_linear_accuracy(O):
     assert errs[256] < 0.8 * errs[0], errs
 
 
+# ------------------------------------------------------- input activations
+
+def _act_expected_bits(act: int, xs_float, dtype: str) -> np.ndarray:
+    """Expected 16-bit results: the activation in 70-digit decimal arithmetic,
+    rounded to nearest on the BF16/FP16 grid by exact rationals (the exact
+    value is never halfway).  Large inputs are split over worker processes;
+    results are cached per (act, dtype, inputs) since they do not depend on
+    the oracle under test."""
+    xs_float = np.asarray(xs_float, np.float32)
+    key = (act, dtype, xs_float.tobytes())
+    if key in _EXPECTED:
+        return _EXPECTED[key]
+    if len(xs_float) > 4096:
+        import multiprocessing as mp
+        parts = np.array_split(xs_float, 32)
+        with mp.get_context("fork").Pool(min(8, os.cpu_count() or 1)) as pool:
+            res = pool.starmap(_act_expected_chunk, [(act, p, dtype) for p in parts])
+        out = np.concatenate(res)
+    else:
+        out = _act_expected_chunk(act, xs_float, dtype)
+    _EXPECTED[key] = out
+    return out
+
+
+_EXPECTED: dict = {}
+
+
+def _act_expected_chunk(act: int, xs_float, dtype: str) -> np.ndarray:
+    from exact import dec_act, round_grid
+    mant, emin = (7, -126) if dtype == "bf16" else (10, -14)
+    out = np.empty(len(xs_float), np.uint16)
+    for i, x in enumerate(xs_float):
+        v = dec_act(act, float(x))
+        r = Fraction(0) if v is None else round_grid(Fraction(v), mant, emin)
+        if r == 0:
+            neg = act != 4 and (x < 0 or (x == 0 and np.signbit(x)))
+            f = -0.0 if neg else 0.0
+        else:
+            f = float(r)
+        if dtype == "bf16":
+            out[i] = np.array([f], np.float32).view(np.uint32)[0] >> 16
+        else:
+            out[i] = np.array([f], np.float16).view(np.uint16)[0]
+    return out
+
+
+def _finite_patterns(dtype: str, stride: int = 1, offset: int = 0) -> np.ndarray:
+    b = np.arange(offset, 65536, stride, dtype=np.uint32).astype(np.uint16)
+    expo = (b >> 7) & 0xFF if dtype == "bf16" else (b >> 10) & 0x1F
+    return b[expo != (0xFF if dtype == "bf16" else 0x1F)]
+
+
+def _as_float(bits: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32)
+    return bits.view(np.float16).astype(np.float32)
+
+
+def _check_act(O, act, dtype, bits):
+    got = O.input_act(bits, dtype, act)
+    want = _act_expected_bits(act, _as_float(bits, dtype), dtype)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (act, dtype, bad.size, hex(int(bits[bad[0]])), hex(int(got[bad[0]])), hex(int(want[bad[0]])))
+
+
+def check_act_relu_exact(O):
+    for dtype in ("bf16", "f16"):
+        b = _finite_patterns(dtype)
+        got = O.input_act(b, dtype, 4)
+        x = _as_float(b, dtype)
+        want = np.where(x > 0, b, np.uint16(0))
+        assert np.array_equal(got, want), dtype
+
+
+def check_act_composition(O):
+    """The layer with an activation equals the layer on the activation's
+    16-bit output without one (the unfused path)."""
+    from synth import random_bf16
+    x = random_bf16((5, 512), seed=33, scale=2.0)
+    g = np.random.Generator(np.random.PCG64(34))
+    wq = g.integers(-127, 128, (24, 512), dtype=np.int64).astype(np.int8)
+    sw = (g.uniform(0.5, 2, 24) * 2.0 ** -9).astype(np.float32)
+    for act in (1, 2, 3, 4):
+        y = O.linear(x, wq, sw, None, "bf16", 256, act=act)
+        y2 = O.linear(O.input_act(x, "bf16", act), wq, sw, None, "bf16", 256)
+        assert np.array_equal(y, y2), act
+        q, s = O.quantize_rowwise(x, "bf16", 0, act=act)
+        q2, s2 = O.quantize_rowwise(O.input_act(x, "bf16", act), "bf16", 0)
+        assert np.array_equal(q, q2) and np.array_equal(s, s2), act
+
+
+def slowcheck_act_all_inputs(O):
+    """Every finite BF16 and FP16 input of GELU (tanh and erf forms) and SiLU."""
+    for dtype in ("bf16", "f16"):
+        for act in (1, 2, 3):
+            _check_act(O, act, dtype, _finite_patterns(dtype))
+
+
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]
+# Slow exhaustive checks run after the quick ones.
+CHECKS += [v for k, v in sorted(globals().items()) if k.startswith("slowcheck_")]

@@ -208,3 +208,33 @@ def test_scaled_mm_ex_validation():
     # a per-tensor w_scale needs no 16-byte alignment: validation passes up to the launch,
     # which an empty problem skips
     assert call(w_len=1, w_scale=ctypes.c_void_p(0x100004), M=0)[0] == qd.QD_OK
+
+
+def test_act_validation():
+    L = qd.lib()
+    F16, F32 = qd.QD_F16, qd.QD_F32
+    # quantizer with an activation
+    for args, status, needle in [
+        ((FAKE, F32, 4, 512, 512, 1, 256, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "BF16 or FP16"),
+        ((FAKE, Q, 4, 512, 512, 9, 256, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "unknown activation"),
+        ((FAKE, Q, 4, 33024, 33024, 1, 256, FAKE, 33024, FAKE, STREAM), qd.QD_EUNSUPPORTED, "32768"),
+        ((FAKE, Q, 4, 512, 512, 1, 128, FAKE, 512, FAKE, STREAM), qd.QD_EUNSUPPORTED, "rotate_block"),
+    ]:
+        st, msg = _status(L.qd_quantize_rowwise_act, *args)
+        assert st == status and needle in msg, (args, st, msg)
+    # ReLU has no FP64 temporaries: long rows are fine (M == 0 stops before any launch)
+    assert L.qd_quantize_rowwise_act(FAKE, F16, 0, 65536, 65536, 4, 256, FAKE, 65536, FAKE, STREAM) == qd.QD_OK
+    # the layer
+    st, msg = _status(L.qd_int8_linear_act, FAKE, F32, 4, 512, 512, 3, FAKE, 8, 512, FAKE, NULL, 256,
+                      FAKE, 1 << 20, FAKE, 8, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "BF16 or FP16" in msg
+    # the elementwise entry
+    for args, status, needle in [
+        ((FAKE, F32, 16, 1, FAKE, STREAM), qd.QD_EUNSUPPORTED, "BF16 or FP16"),
+        ((FAKE, Q, -1, 1, FAKE, STREAM), qd.QD_EINVAL, "n >= 0"),
+        ((NULL, Q, 16, 1, FAKE, STREAM), qd.QD_EINVAL, "null"),
+        ((ctypes.c_void_p(0x100001), Q, 16, 1, FAKE, STREAM), qd.QD_EUNSUPPORTED, "2-byte"),
+        ((FAKE, Q, 16, 7, FAKE, STREAM), qd.QD_EUNSUPPORTED, "unknown activation"),
+    ]:
+        st, msg = _status(L.qd_input_act, *args)
+        assert st == status and needle in msg, (args, st, msg)
