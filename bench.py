@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
+PEAK_FP6_TFLOPS = 10100.0      # MI355X dense FP6/FP4 MFMA, published (10.1 PFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published (8 TB/s)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_traffic.json")
 GEMM_SRC = os.path.join(ROOT, "quantized_diffusion_amd", "csrc", "gemm_i8.hip")
@@ -70,7 +71,8 @@ def time_launches(fn, n, torch):
     return a.elapsed_time(b) / n
 
 
-def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float, act: int = 0):
+def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float, act: int = 0,
+                 codes: bool = False):
     """Time the oracle on the leading rows of the same workload; check those rows."""
     import numpy as np
 
@@ -78,7 +80,7 @@ def cpu_baseline(x_dev, y_dev, wq_dev, sw_dev, b_bits, w, torch, budget_s: float
     O = oracle.default()
     int4 = w.kind == "w4a4"
     wq = wq_dev.cpu().numpy()
-    if int4:
+    if int4 and not codes:
         wq = O.unpack_int4(wq, w.K)     # packed weights -> INT4 codes in INT8 storage
     sw = sw_dev.cpu().numpy()
 
@@ -133,6 +135,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="workload id (synth.WORKLOADS)")
     ap.add_argument("--act", choices=["none", "gelu_tanh", "gelu_erf", "silu", "relu"], default="none",
                     help="input activation folded into the quantizer (int8_linear(input_act=...))")
+    ap.add_argument("--fp6", action="store_true",
+                    help="W4A4 workload on the FP6 matrix path (convrot_w4a4_linear_fp6)")
     ap.add_argument("--op", choices=["linear", "tensorwise"], default="linear",
                     help="linear: the whole layer (default); tensorwise: quantize_int8_tensorwise on the "
                          "workload's activations")
@@ -167,6 +171,9 @@ def main():
     act = ["none", "gelu_tanh", "gelu_erf", "silu", "relu"].index(args.act)
     if act and int4:
         sys.exit("an input activation is measured on the INT8 layer only")
+    fp6 = args.fp6
+    if fp6 and not int4:
+        sys.exit("--fp6 applies to the W4A4 workload")
     M, K, N = w.M, w.K, w.N
     dev = torch.device("cuda:0")
     log(f"[bench] {w.name}: generating inputs")
@@ -179,14 +186,22 @@ def main():
     b_bits = make_bias(w)
     bias = torch.from_numpy(b_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     # offline weight preparation (not timed)
-    wq, sw = qd.prepare_weights_w4a4(Wf) if int4 else qd.prepare_weights(Wf)
+    w_codes = None
+    if fp6:
+        wq, sw = qd.prepare_weights_w4a4_fp6(Wf)
+        w_codes = qd.quantize_and_rotate_rowwise_int4(Wf)[0]    # the same codes, for the CPU baseline
+    else:
+        wq, sw = qd.prepare_weights_w4a4(Wf) if int4 else qd.prepare_weights(Wf)
     del Wf
-    ws = torch.empty(qd.workspace_size(M, K), dtype=torch.uint8, device=dev)
+    ws = torch.empty(qd.w4a4_fp6_workspace_size(M, K) if fp6 else qd.workspace_size(M, K), dtype=torch.uint8,
+                     device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     def step():
-        if int4:
+        if fp6:
+            qd.convrot_w4a4_linear_fp6(x, wq, sw, bias, 256, ws, y)
+        elif int4:
             qd.convrot_w4a4_linear(x, wq, sw, bias, 256, ws, y)
         elif act:
             qd.int8_linear_act(x, wq, sw, bias, act, 256, ws, y)
@@ -216,7 +231,13 @@ def main():
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     y2 = torch.empty_like(y)
     reps = max(5, args.steps)
-    if int4:
+    ms_p = None
+    if fp6:
+        a6 = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=dev)
+        ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_int4(x, 256, aq, sx), reps, torch)
+        ms_p = time_launches(lambda: qd.pack_fp6(aq, a6), reps, torch)
+        ms_g = time_launches(lambda: qd.fp6_scaled_mm(a6, sx, wq, sw, K, bias, y2), reps, torch)
+    elif int4:
         ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_int4(x, 256, aq, sx), reps, torch)
         ms_g = time_launches(lambda: qd.int4_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     elif act:
@@ -227,11 +248,14 @@ def main():
         ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     same = bool(torch.equal(y2, y))
     q_bytes = 3.0 * M * K + 4.0 * M
-    g_min_bytes = float(M * K + (N * K // 2 if int4 else N * K) + 2 * M * N + 4 * M + 4 * N + 2 * N)
+    g_min_bytes = float((M * K * 3 // 4 + N * K * 3 // 4) if fp6 else (M * K + (N * K // 2 if int4 else N * K))) \
+        + 2 * M * N + 4 * M + 4 * N + 2 * N
     gemm_tops = ops / (ms_g * 1e-3) / 1e12
     traffic = load_traffic(w.name)
     out = {
-        "metric": (f"W4A4 rotated linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}" if int4 else
+        "metric": (f"W4A4 rotated linear TOPS on the FP6 matrix path (incl. rotate+quant+pack) & % of INT8 MFMA "
+                   f"peak, M{M}/K{K}/N{N}" if fp6 else
+                   f"W4A4 rotated linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}" if int4 else
                    f"INT8 linear TOPS with input_act={args.act} (incl. act+rotate+quant) & % of INT8 MFMA peak, "
                    f"M{M}/K{K}/N{N}" if act else
                    f"INT8 linear TOPS (incl. rotate+quant) & % of INT8 MFMA peak, M{M}/K{K}/N{N}"),
@@ -244,7 +268,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tops / (ops / (PAGE_MS[w.cid] * 1e-3) / 1e12), 4) if w.cid in PAGE_MS else None,
-        "dtype": "i4 codes on i8 MFMA" if int4 else "i8",
+        "dtype": "i4 codes on fp6 (e2m3) MFMA" if fp6 else "i4 codes on i8 MFMA" if int4 else "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "input_act": args.act,
                    "rotation": "block-256 Walsh-Hadamard",
@@ -253,11 +277,13 @@ def main():
                                else "int8 per-channel fp32 scale"),
                    "bias": "bf16", "output": "bf16", "parallelism": "single GPU"},
         "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": ("gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4>" if int4 else
+        "roofline": {"bound": "mfma", "kernel": ("gemm_f6_w8_kernel<MODE_BF16>" if fp6 else
+                                                 "gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4>" if int4 else
                                                  "gemm_i8_w8_kernel<MODE_BF16, 4, WF_I8>") + " (fused bf16 epilogue)",
-                     "achieved": round(gemm_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                     "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
-                     "traffic": traffic},
+                     "achieved": round(gemm_tops, 2), "peak": PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS,
+                     "unit": "TFLOP/s" if fp6 else "TOP/s",
+                     "frac": round(gemm_tops / (PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS), 4),
+                     "traffic": None if fp6 else traffic},
         "kernels": {
             "rotquant": {"ms": round(ms_q, 5), "algorithmic_bytes": q_bytes,
                          "GB_per_s": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),
@@ -266,6 +292,7 @@ def main():
                      "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "min_hbm_bytes": g_min_bytes},
             "separate_launch_output_identical": same,
+            "pack_fp6_ms": None if ms_p is None else round(ms_p, 5),
         },
         "device": torch.cuda.get_device_name(0),
         "wall_s_timed_region": round(t_wall, 4),
@@ -274,7 +301,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle on host cores)")
-        out["cpu_baseline"] = cpu_baseline(x, y, wq, sw, b_bits, w, torch, args.cpu_budget, act)
+        out["cpu_baseline"] = cpu_baseline(x, y, wq if w_codes is None else w_codes, sw, b_bits, w, torch,
+                                           args.cpu_budget, act, codes=w_codes is not None)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -305,6 +305,58 @@ qd_status_t qd_convrot_w4a4_linear(const void* x, qd_dtype_t x_dtype, int64_t M,
                                    int32_t rotate_block, void* workspace, size_t workspace_bytes,
                                    void* y_bf16, int64_t ldy, hipStream_t stream);
 
+/*
+ * W4A4 on the FP6 matrix path (the "map INT4 codes to FP6 E2M3" option for
+ * convrot_w4a4_linear).  Every INT4 code in [-7, 7] is exact in FP6 E2M3
+ * (OCP MX: sign, 2 exponent bits with bias 1, 3 mantissa bits), and all
+ * partial sums are integers below K * 49 < 2^24, so the FP32 accumulation
+ * of gfx950's FP6 matrix instructions is exact and the results equal the
+ * INT8-path results bit for bit.
+ *
+ * FP6 operand format of an [R, K] matrix (K % 64 == 0): each row takes 3K/4
+ * bytes (row stride ld bytes, a multiple of 16).  Values 64j .. 64j+63 of a
+ * row fill the 48 bytes at 48j as two pieces of 32 values (piece p = values
+ * 64j + 32p .. +31, value i of a piece in bits 6i .. 6i+5 of its 24 bytes,
+ * least significant first):
+ *     bytes  0..15  piece 0 bytes 0..15
+ *     bytes 16..31  piece 1 bytes 0..15
+ *     bytes 32..47  piece 0 bytes 16..23 then piece 1 bytes 16..23, or the
+ *                   two swapped when bit 4 of the row index is set.
+ *
+ * qd_pack_fp6: codes q [R, K] INT8 in [-7, 7] (other values give undefined
+ * bytes) -> out [R, 3K/4] in that format.  K % 64 == 0; q/out 16-byte
+ * aligned; ldq, ldo multiples of 16; ldo >= 3K/4.
+ */
+qd_status_t qd_pack_fp6(const int8_t* q, int64_t R, int64_t K, int64_t ldq, uint8_t* out, int64_t ldo,
+                        hipStream_t stream);
+
+/*
+ * The GEMM on FP6 operands: a6 [M, 3K/4] (stride lda bytes) and w6
+ * [N, 3K/4] (stride ldw bytes) in the FP6 operand format, a_scale [M],
+ * w_scale [N], bias [N] BF16 or NULL, y [M, N] BF16:
+ *   y = bf16_rne(((float)sum_k a[m,k] w[n,k] * a_scale[m]) * w_scale[n] + bias[n]).
+ * K % 128 == 0, K <= QD_MAX_K_GEMM; otherwise as qd_int8_scaled_mm.
+ * qd_fp6_gemm_i32 writes the exact sums as INT32 (ldc a multiple of 4).
+ */
+qd_status_t qd_fp6_scaled_mm(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, const float* a_scale,
+                             const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale, const void* bias_bf16,
+                             void* y_bf16, int64_t ldy, hipStream_t stream);
+qd_status_t qd_fp6_gemm_i32(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, const uint8_t* w6, int64_t N,
+                            int64_t ldw, int32_t* acc, int64_t ldc, hipStream_t stream);
+
+/*
+ * convrot_w4a4_linear with FP6 weights w6 [N, 3K/4] (qd_quantize_and_rotate_rowwise_int4
+ * on W, then qd_pack_fp6): the rotating INT4 quantizer, qd_pack_fp6 of the
+ * activation codes, then the FP6 GEMM.  Same results as qd_convrot_w4a4_linear.
+ * K % 256 == 0; workspace of qd_w4a4_fp6_workspace_size(M, K) bytes,
+ * 256-byte aligned.
+ */
+size_t qd_w4a4_fp6_workspace_size(int64_t M, int64_t K);
+qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                       const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale,
+                                       const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                       size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -423,6 +423,47 @@ void oracle_unpack_int4(const uint8_t* packed, int64_t R, int64_t K, int8_t* q) 
         }
 }
 
+/* ---- FP6 operand format ------------------------------------------------- */
+
+/* FP6 E2M3 (OCP MX): sign bit 5, exponent bits 4..3 (bias 1), mantissa bits
+ * 2..0; value m/8 when the exponent field is 0, else 2^(e-1) (1 + m/8).  The
+ * fields of an integer code are found by trying every (e, m). */
+static unsigned e2m3_of_code(int c) {
+    int a = c < 0 ? -c : c;
+    for (unsigned e = 0; e < 4; e++)
+        for (unsigned m = 0; m < 8; m++) {
+            float v = e == 0 ? (float)m / 8.0f : ldexpf(1.0f + (float)m / 8.0f, (int)e - 1);
+            if (v == (float)a) return (c < 0 ? 32u : 0u) | (e << 3) | m;
+        }
+    return 0xFFu;   /* not representable */
+}
+
+/* The FP6 operand format (qdiff.h) of INT4 codes q [R, K] (K % 64 == 0):
+ * out [R, 3K/4] dense.  Returns the number of codes that are not exact. */
+int64_t oracle_pack_fp6(const int8_t* q, int64_t R, int64_t K, uint8_t* out) {
+    int64_t bad = 0;
+    const int64_t rb = K / 4 * 3;
+    for (int64_t r = 0; r < R; r++)
+        for (int64_t j = 0; j < K / 64; j++) {
+            uint8_t piece[2][24];
+            memset(piece, 0, sizeof(piece));
+            for (int p = 0; p < 2; p++)
+                for (int i = 0; i < 32; i++) {
+                    unsigned f = e2m3_of_code(q[r * K + 64 * j + 32 * p + i]);
+                    if (f > 63u) { bad++; f = 0; }
+                    for (int b = 0; b < 6; b++)
+                        if (f >> b & 1u) piece[p][(6 * i + b) / 8] |= (uint8_t)(1u << ((6 * i + b) % 8));
+                }
+            uint8_t* o = out + r * rb + 48 * j;
+            memcpy(o, piece[0], 16);
+            memcpy(o + 16, piece[1], 16);
+            int first = (int)((r >> 4) & 1);          /* which piece's tail comes first */
+            memcpy(o + 32, piece[first] + 16, 8);
+            memcpy(o + 40, piece[1 - first] + 16, 8);
+        }
+    return bad;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

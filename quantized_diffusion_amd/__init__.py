@@ -32,7 +32,8 @@ __all__ = [
     "prepare_weights", "workspace_size", "EXPORTED_SYMBOLS", "pack_int4", "prepare_weights_w4a4",
     "int4_scaled_mm", "int4_gemm_i32", "convrot_w4a4_linear", "quantize_int8_tensorwise",
     "tensorwise_workspace_size", "int8_scaled_mm_ex", "input_act", "quantize_rowwise_act", "int8_linear_act",
-    "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU",
+    "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU", "pack_fp6", "fp6_scaled_mm",
+    "fp6_gemm_i32", "w4a4_fp6_workspace_size", "convrot_w4a4_linear_fp6", "prepare_weights_w4a4_fp6",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -47,7 +48,8 @@ EXPORTED_SYMBOLS = (
     "qd_int8_linear_workspace_size", "qd_int8_linear", "qd_dequantize_int8", "qd_int8_gemm_i32",
     "qd_pack_int4", "qd_int4_scaled_mm", "qd_int4_gemm_i32", "qd_convrot_w4a4_linear",
     "qd_quantize_tensorwise_workspace_size", "qd_quantize_int8_tensorwise", "qd_int8_scaled_mm_ex",
-    "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act",
+    "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act", "qd_pack_fp6", "qd_fp6_scaled_mm",
+    "qd_fp6_gemm_i32", "qd_w4a4_fp6_workspace_size", "qd_convrot_w4a4_linear_fp6",
 )
 
 
@@ -108,6 +110,16 @@ def lib():
         L.qd_quantize_rowwise_act.argtypes = [P, St, I64, I64, I64, St, I32, P, I64, P, P]
         L.qd_input_act.restype = St
         L.qd_input_act.argtypes = [P, St, I64, St, P, P]
+        L.qd_pack_fp6.restype = St
+        L.qd_pack_fp6.argtypes = [P, I64, I64, I64, P, I64, P]
+        L.qd_fp6_scaled_mm.restype = St
+        L.qd_fp6_scaled_mm.argtypes = [P, I64, I64, I64, P, P, I64, I64, P, P, P, I64, P]
+        L.qd_fp6_gemm_i32.restype = St
+        L.qd_fp6_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
+        L.qd_w4a4_fp6_workspace_size.restype = SZ
+        L.qd_w4a4_fp6_workspace_size.argtypes = [I64, I64]
+        L.qd_convrot_w4a4_linear_fp6.restype = St
+        L.qd_convrot_w4a4_linear_fp6.argtypes = [P, St, I64, I64, I64, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
         _lib = L
     return _lib
 
@@ -399,6 +411,90 @@ def input_act(x, act: int, out=None):
     if out is None:
         out = torch.empty_like(x)
     _check(lib().qd_input_act(_ptr(x), _dtype_code(x), x.numel(), int(act), _ptr(out), _stream(dev)))
+    return out
+
+
+# ------------------------------------------------------------- FP6 operands
+
+def _f6_ld(K):
+    return (K // 4 * 3 + 15) // 16 * 16
+
+
+def pack_fp6(q, out=None):
+    """INT4 codes (int8 [R, K], values in [-7, 7]) -> the FP6 E2M3 operand format
+    (uint8 [R, 3K/4]), exact for every code."""
+    torch = _torch()
+    _mat(q, "q")
+    dev = _dev(q, out)
+    R, K = q.shape
+    if out is None:
+        out = torch.empty((R, _f6_ld(K)), dtype=torch.uint8, device=dev)[:, :K // 4 * 3]
+    _mat(out, "out")
+    _check(lib().qd_pack_fp6(_ptr(q), R, K, q.stride(0), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def prepare_weights_w4a4_fp6(w, block: int = 256):
+    """Offline W4A4 weights for the FP6 path: rotate, quantize per channel to INT4
+    codes, pack as FP6.  Returns (w6 uint8 [N, 3K/4], w_scale fp32 [N])."""
+    q, s = quantize_and_rotate_rowwise_int4(w, block)
+    return pack_fp6(q), s
+
+
+def fp6_scaled_mm(a6, a_scale, w6, w_scale, K: int, bias=None, out=None):
+    """The GEMM on FP6 operands (K values per row), BF16 out with the fused epilogue."""
+    torch = _torch()
+    _mat(a6, "a6"), _mat(w6, "w6")
+    dev = _dev(a6, a_scale, w6, w_scale, bias, out)
+    M, N = a6.shape[0], w6.shape[0]
+    _rows_vec(a_scale, M, torch.float32, "a_scale")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_fp6_scaled_mm(_ptr(a6), M, K, a6.stride(0), _ptr(a_scale), _ptr(w6), N, w6.stride(0),
+                                  _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def fp6_gemm_i32(a6, w6, K: int, out=None):
+    """Exact sums of the FP6 GEMM as int32 [M, N]."""
+    torch = _torch()
+    _mat(a6, "a6"), _mat(w6, "w6")
+    dev = _dev(a6, w6, out)
+    M, N = a6.shape[0], w6.shape[0]
+    if out is None:
+        out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
+    _check(lib().qd_fp6_gemm_i32(_ptr(a6), M, K, a6.stride(0), _ptr(w6), N, w6.stride(0), _ptr(out),
+                                 out.stride(0), _stream(dev)))
+    return out
+
+
+def w4a4_fp6_workspace_size(M: int, K: int) -> int:
+    return int(lib().qd_w4a4_fp6_workspace_size(M, K))
+
+
+def convrot_w4a4_linear_fp6(x, w6, w_scale, bias=None, rotate_block: int = 256, workspace=None, out=None):
+    """convrot_w4a4_linear with FP6 weights (prepare_weights_w4a4_fp6): same results, FP6 matrix path."""
+    torch = _torch()
+    _mat(x, "x"), _mat(w6, "w6")
+    dev = _dev(x, w6, w_scale, bias, workspace, out)
+    M, K = x.shape
+    N = w6.shape[0]
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if workspace is None:
+        workspace = torch.empty(max(w4a4_fp6_workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_convrot_w4a4_linear_fp6(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(w6), N, w6.stride(0),
+                                            _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
+                                            _stream(dev)))
     return out
 
 

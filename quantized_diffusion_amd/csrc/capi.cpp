@@ -389,4 +389,109 @@ qd_status_t qd_convrot_w4a4_linear(const void* x, qd_dtype_t x_dtype, int64_t M,
                                                   ldy, M, N, K, stream));
 }
 
+// ---------------------------------------------------------------- FP6 operands
+
+namespace {
+
+// FP6 operand matrices: [R, K] values in 3K/4 bytes per row (the operand format
+// of qdiff.h), row stride ld bytes.
+qd_status_t check_f6(const char* fn, const uint8_t* a6, int64_t M, int64_t K, int64_t lda, const uint8_t* w6,
+                     int64_t N, int64_t ldw, const void* out, int64_t ldo, int64_t ldo_multiple) {
+    if (M < 0 || N < 0 || K <= 0)
+        return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
+    if (M > 0 && N > 0 && (!a6 || !w6 || !out)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (K % 128 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 128 for FP6 operands", (long long)K);
+    if (K > QD_MAX_K_GEMM) return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds %d", (long long)K, QD_MAX_K_GEMM);
+    if (lda < K / 4 * 3 || ldw < K / 4 * 3) return fail(QD_EINVAL, fn, "lda/ldw must be >= 3K/4 bytes");
+    if (ldo < N) return fail(QD_EINVAL, fn, "output leading dimension (%lld) < N (%lld)", (long long)ldo, (long long)N);
+    if (M > INT32_MAX - 256 || N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "M or N too large");
+    if ((M + 255) / 256 * ((N + 255) / 256) > INT32_MAX) return fail(QD_EUNSUPPORTED, fn, "too many output tiles");
+    if (M > 0 && N > 0 && (!aligned16(a6) || !aligned16(w6) || !aligned16(out)))
+        return fail(QD_EUNSUPPORTED, fn, "operands and output must be 16-byte aligned");
+    if (lda % 16 != 0 || ldw % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "lda and ldw must be multiples of 16 bytes");
+    if (ldo % ldo_multiple != 0)
+        return fail(QD_EUNSUPPORTED, fn, "output leading dimension must be a multiple of %lld", (long long)ldo_multiple);
+    return QD_OK;
+}
+
+int64_t f6_ld(int64_t K) { return (int64_t)round_up((size_t)(K / 4 * 3), 16); }
+
+}  // namespace
+
+qd_status_t qd_pack_fp6(const int8_t* q, int64_t R, int64_t K, int64_t ldq, uint8_t* out, int64_t ldo,
+                        hipStream_t stream) {
+    const char* fn = "qd_pack_fp6";
+    if (R < 0 || K <= 0) return fail(QD_EINVAL, fn, "need R >= 0 and K > 0 (R=%lld, K=%lld)", (long long)R, (long long)K);
+    if (R > 0 && (!q || !out)) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 64", (long long)K);
+    if (ldq < K) return fail(QD_EINVAL, fn, "ldq (%lld) < K (%lld)", (long long)ldq, (long long)K);
+    if (ldo < K / 4 * 3) return fail(QD_EINVAL, fn, "ldo (%lld bytes) < 3K/4", (long long)ldo);
+    if (R > 0 && (!aligned16(q) || !aligned16(out))) return fail(QD_EUNSUPPORTED, fn, "q and out must be 16-byte aligned");
+    if (ldq % 16 != 0 || ldo % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "ldq and ldo must be multiples of 16 bytes");
+    if (R == 0) return ok();
+    return hip_status(fn, qd::launch_pack_fp6(q, ldq, out, ldo, R, K, stream));
+}
+
+qd_status_t qd_fp6_scaled_mm(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, const float* a_scale,
+                             const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale, const void* bias_bf16,
+                             void* y_bf16, int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_fp6_scaled_mm";
+    qd_status_t st = check_f6(fn, a6, M, K, lda, w6, N, ldw, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    return hip_status(fn, qd::launch_gemm_f6_bf16(a6, lda, a_scale, w6, ldw, w_scale, bias_bf16, y_bf16, ldy, M, N,
+                                                  K, stream));
+}
+
+qd_status_t qd_fp6_gemm_i32(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, const uint8_t* w6, int64_t N,
+                            int64_t ldw, int32_t* acc, int64_t ldc, hipStream_t stream) {
+    const char* fn = "qd_fp6_gemm_i32";
+    qd_status_t st = check_f6(fn, a6, M, K, lda, w6, N, ldw, acc, ldc, 4);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    return hip_status(fn, qd::launch_gemm_f6_i32(a6, lda, w6, ldw, acc, ldc, M, N, K, stream));
+}
+
+size_t qd_w4a4_fp6_workspace_size(int64_t M, int64_t K) {
+    if (M <= 0 || K <= 0) return 0;
+    return ws_codes_bytes(M, K) + round_up((size_t)M * (size_t)f6_ld(K), kAlign) + round_up((size_t)M * sizeof(float), kAlign);
+}
+
+qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                       const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale,
+                                       const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                       size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_convrot_w4a4_linear_fp6";
+    if (rotate_block != 256) return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 256 (got %d)", rotate_block);
+    if (M < 0 || N < 0 || K <= 0)
+        return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
+    if (M == 0 || N == 0) return ok();
+    if (!workspace) return fail(QD_EINVAL, fn, "null workspace");
+    if ((uintptr_t)workspace % kAlign) return fail(QD_EUNSUPPORTED, fn, "workspace must be 256-byte aligned");
+    if (workspace_bytes < qd_w4a4_fp6_workspace_size(M, K))
+        return fail(QD_EINVAL, fn, "workspace too small: %zu < %zu bytes", workspace_bytes, qd_w4a4_fp6_workspace_size(M, K));
+    const int64_t ldq = (int64_t)round_up((size_t)K, 16);
+    const int64_t lda6 = f6_ld(K);
+    char* ws = static_cast<char*>(workspace);
+    int8_t* aq = reinterpret_cast<int8_t*>(ws);
+    uint8_t* a6 = reinterpret_cast<uint8_t*>(ws + ws_codes_bytes(M, K));
+    float* sx = reinterpret_cast<float*>(ws + ws_codes_bytes(M, K) + round_up((size_t)M * (size_t)lda6, kAlign));
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, true, rotate_block, aq, ldq, sx);
+    if (st != QD_OK) return st;
+    st = check_f6(fn, a6, M, K, lda6, w6, N, ldw, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, true, 7, M, K, ldx, aq, ldq, sx, stream);
+    if (e != hipSuccess) return hip_status(fn, e);
+    e = qd::launch_pack_fp6(aq, ldq, a6, lda6, M, K, stream);
+    if (e != hipSuccess) return hip_status(fn, e);
+    return hip_status(fn, qd::launch_gemm_f6_bf16(a6, lda6, sx, w6, ldw, w_scale, bias_bf16, y_bf16, ldy, M, N, K,
+                                                  stream));
+}
+
 }  // extern "C"

@@ -72,7 +72,64 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const int8_t* __restrict
     *reinterpret_cast<u32x4*>(out + r * ldo + c * 16) = o;
 }
 
+// FP6 E2M3 bits of four INT4 codes (bytes of w, each in [-7, 7]), one per
+// byte: sign in bit 5, exponent (bias 1) in bits 4..3, mantissa in 2..0;
+// every integer of [-7, 7] is exact (1 = 1.0 x 2^0 ... 7 = 1.75 x 2^2).
+__device__ __forceinline__ uint32_t e2m3x4(uint32_t w) {
+    const uint32_t s = (w >> 7) & 0x01010101u;        // sign per byte
+    const uint32_t a = (w ^ (s * 0xFFu)) + s;          // |code| per byte (no carries: <= 7)
+    const uint32_t e = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, a);   // magnitudes 0,1,2,3 | 4,5,6,7
+    return e | (s << 5);
+}
+
+// Four 6-bit fields (one per byte) -> 24 bits, field i at bits 6i.
+__device__ __forceinline__ uint32_t pack6x4(uint32_t c) {
+    const uint32_t u = (c & 0x00FF00FFu) | (((c >> 8) & 0x00FF00FFu) << 6);
+    return (u & 0xFFFu) | ((u >> 16) << 12);
+}
+
+// One 64-value K block of one row per thread: codes -> the FP6 operand
+// format (see qdiff.h): [piece 0 bytes 0..15 | piece 1 bytes 0..15 | the
+// two 8-byte tails, piece 0's first unless bit 4 of the row index is set].
+__global__ __launch_bounds__(256) void pack_fp6_kernel(const int8_t* __restrict__ q, int64_t ldq,
+                                                       uint8_t* __restrict__ out, int64_t ldo, int64_t R,
+                                                       int64_t blocks_per_row) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= R * blocks_per_row) return;
+    const int64_t r = idx / blocks_per_row;
+    const int64_t b = idx - r * blocks_per_row;
+    const int8_t* src = q + r * ldq + b * 64;
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + 16 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = pack6x4(e2m3x4(w[j]));
+    }
+    uint32_t d[12];   // the 384-bit stream of 64 fields, 24 bits per group of four
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
+        d[3 * g] = v0 | (v1 << 24);
+        d[3 * g + 1] = (v1 >> 8) | (v2 << 16);
+        d[3 * g + 2] = (v2 >> 16) | (v3 << 8);
+    }
+    uint8_t* dst = out + r * ldo + b * 48;
+    const bool swp = (r >> 4) & 1;
+    *reinterpret_cast<u32x4*>(dst) = u32x4{d[0], d[1], d[2], d[3]};
+    *reinterpret_cast<u32x4*>(dst + 16) = u32x4{d[6], d[7], d[8], d[9]};
+    *reinterpret_cast<u32x4*>(dst + 32) = swp ? u32x4{d[10], d[11], d[4], d[5]} : u32x4{d[4], d[5], d[10], d[11]};
+}
+
 }  // namespace
+
+hipError_t launch_pack_fp6(const int8_t* q, int64_t ldq, uint8_t* out, int64_t ldo, int64_t R, int64_t K,
+                           hipStream_t stream) {
+    const int64_t bpr = K / 64;
+    const int64_t grid = (R * bpr + 255) / 256;
+    pack_fp6_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(q, ldq, out, ldo, R, bpr);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack_int4(const int8_t* q, int64_t ldq, uint8_t* out, int64_t ldo, int64_t R, int64_t K,
                             hipStream_t stream) {

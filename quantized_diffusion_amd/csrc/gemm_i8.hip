@@ -591,6 +591,282 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// FP6 operands (W4A4 codes on the FP6 matrix path).  Every INT4 code in
+// [-7, 7] is exact in FP6 E2M3, and v_mfma_scale_f32_32x32x64_f8f6f4 with
+// unit (E8M0 = 127) scales multiplies 32 x 64 by 64 x 32 FP6 blocks at twice
+// the INT8 rate, accumulating in FP32.  All partial sums are integers of
+// magnitude <= K * 49 < 2^24, so the FP32 accumulator holds the exact INT32
+// sum and the epilogue sees the same value as the INT8 path.
+//
+// The loop is the eight-wave kernel's (same stage protocol, barrier between
+// the two K halves of a slice) with a slice of 128 values: 96 bytes per row,
+// one MFMA K step (64 values, 48 bytes) per half.  Operands arrive in the FP6
+// operand format (qdiff.h): per 64-value block, [piece 0 bytes 0..15 |
+// piece 1 bytes 0..15 | tails], the tails swapped when bit 4 of the row is
+// set.  A lane (row r, K half h) takes piece h as one 16-byte read (slot h)
+// and one 8-byte read (tail half h ^ swap(r)); in LDS the six 16-byte slots
+// of a row are rotated by one when bit 3 of the row is set.  Together these
+// make both reads free of bank conflicts.  Three 48 KB stages.
+constexpr int F6_BK = 128;                 // values per slice
+constexpr int F6_RB = 96;                  // bytes per row per slice
+constexpr int F6_STG = (BM + BN) * F6_RB;  // 48 KB per stage
+constexpr int F6_NS = 3;
+constexpr int F6_PER = 6;                  // copies per slice per thread (3 activation + 3 weight)
+
+__device__ __forceinline__ int f6_rot(int r) { return (r >> 3) & 1; }
+__device__ __forceinline__ int f6_swp(int r) { return (r >> 4) & 1; }
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Four outputs from exact FP32 sums (same arithmetic as epi_bf16x4).
+__device__ __forceinline__ u32x2 epi_bf16x4_f(const float* a4, float sx, const f32x4& sw, const u32x2& bb,
+                                              bool has_bias) {
+#pragma clang fp contract(off)
+    const float b[4] = {bits_f(bb[0] << 16), bits_f(bb[0] & 0xFFFF0000u), bits_f(bb[1] << 16),
+                        bits_f(bb[1] & 0xFFFF0000u)};
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float tt = a4[e];
+        tt = tt * sx;
+        tt = tt * sw[e];
+        if (has_bias) tt = tt + b[e];
+        o[e] = tt;
+    }
+    u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    return pk;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __restrict__ A, int64_t lda,
+                                                           const uint8_t* __restrict__ W, int64_t ldw,
+                                                           int M, int N, int K, EpiArgs ep) {
+    constexpr int NS = F6_NS;
+    constexpr int STG = F6_STG;
+    constexpr int RING = NS * STG > 256 * 512 ? NS * STG : 256 * 512;
+    __shared__ __attribute__((aligned(1024))) int8_t smem[RING + EPI_LDS];
+    float* l_sx = reinterpret_cast<float*>(smem + RING);
+    float* l_sw = l_sx + 256;
+    uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + 256);
+
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const int T = tiles_m * tiles_n;
+    const int g = blockIdx.x;
+    const int xcd = g % NXCD;
+    const int q8 = T / NXCD, rem = T % NXCD;
+    const int t_lin = xcd * q8 + min(xcd, rem) + g / NXCD;
+    const int per_group = GROUP_M * tiles_n;
+    const int group = t_lin / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsz = min(tiles_m - first_m, GROUP_M);
+    const int tg = t_lin - group * per_group;
+    const int m0 = (first_m + tg % gsz) * BM;
+    const int n0 = (tg / gsz) * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+
+    if (MODE == MODE_BF16) {
+        if (tid < 256) {
+            const int m = min(m0 + tid, M - 1);
+            l_sx[tid] = ep.a_scale[m * ep.a_step];
+        } else {
+            const int c = tid - 256;
+            const int n = min(n0 + c, N - 1);
+            l_sw[c] = ep.w_scale[n * ep.w_step];
+            l_b[c] = ep.bias ? ep.bias[n] : (uint16_t)0;
+        }
+    }
+
+    // copies: instruction i (0..2) of wave w fills the 16-byte LDS slots
+    // (3w + i) * 64 + lane of an operand's 24 KB stage part; slot q holds
+    // row q / 6, physical slot q % 6 = logical slot rotated by f6_rot(row)
+    const uint8_t* ga[3];
+    const uint8_t* gw[3];
+    uint32_t lslot[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int q = (3 * wave + i) * 64 + lane;
+        const int row = q / 6;
+        const int phys = q - 6 * row;
+        int logical = phys - f6_rot(row);
+        logical += logical < 0 ? 6 : 0;
+        ga[i] = A + (int64_t)min(m0 + row, M - 1) * lda + 16 * logical;
+        gw[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 16 * logical;
+        lslot[i] = (uint32_t)((3 * wave + i) * 1024);
+    }
+    const uint32_t lds0 = lds_addr(smem);
+    auto copy_part = [&](int u, int part, int i) {
+        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
+        if (part == 0) dma16(sb + lslot[i], reinterpret_cast<const int8_t*>(ga[i] + (int64_t)u * F6_RB));
+        else dma16(sb + BM * F6_RB + lslot[i], reinterpret_cast<const int8_t*>(gw[i] + (int64_t)u * F6_RB));
+    };
+    auto issue = [&](int u) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) copy_part(u, 0, i);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) copy_part(u, 1, i);
+    };
+
+    const int fr = lane & 31;
+    const int fk = lane >> 5;
+    // LDS byte offsets of a lane's piece in K half kk: 16-byte head, 8-byte tail
+    int a_h[4][2], a_t[4][2], w_h[2][2], w_t[2][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int r = wm * 128 + b * 32 + fr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            a_h[b][kk] = r * F6_RB + 16 * ((3 * kk + fk + f6_rot(r)) % 6);
+            a_t[b][kk] = r * F6_RB + 16 * ((3 * kk + 2 + f6_rot(r)) % 6) + 8 * (fk ^ f6_swp(r));
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int r = wn * 64 + b * 32 + fr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            w_h[b][kk] = BM * F6_RB + r * F6_RB + 16 * ((3 * kk + fk + f6_rot(r)) % 6);
+            w_t[b][kk] = BM * F6_RB + r * F6_RB + 16 * ((3 * kk + 2 + f6_rot(r)) % 6) + 8 * (fk ^ f6_swp(r));
+        }
+    }
+    auto rd = [&](int u, int head, int tail) {
+        const int8_t* base = smem + (u % NS) * STG;
+        const i32x4 h = *reinterpret_cast<const i32x4*>(base + head);
+        const u32x2 t = *reinterpret_cast<const u32x2*>(base + tail);
+        return i32x8{h[0], h[1], h[2], h[3], (int32_t)t[0], (int32_t)t[1], 0, 0};
+    };
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = K / F6_BK;
+#pragma unroll
+    for (int u = 0; u < NS - 1; ++u)
+        if (u < nk) issue(u);
+    wait_groups<F6_PER>(min(nk, NS - 1) - 1);
+    __syncthreads();
+    if (NS - 1 < nk) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) copy_part(NS - 1, 0, i);
+    }
+
+    i32x8 a0[4], w0[2], a1[4], w1[2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) a0[b] = rd(0, a_h[b][0], a_t[b][0]);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) w0[b] = rd(0, w_h[b][0], w_t[b][0]);
+    for (int t = 0; t < nk; ++t) {
+        const bool late = t + NS - 1 < nk;
+        // first half of slice t; reads of its second half; weight copies of slice t+NS-1
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            w1[q] = rd(t, w_h[q][1], w_t[q][1]);
+            a1[2 * q] = rd(t, a_h[2 * q][1], a_t[2 * q][1]);
+            a1[2 * q + 1] = rd(t, a_h[2 * q + 1][1], a_t[2 * q + 1][1]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[q], a0[j], acc[q][j], 2, 2, 0, 127,
+                                                                            0, 127);
+            if (late) {
+                copy_part(t + NS - 1, 1, q);
+                if (q == 1) copy_part(t + NS - 1, 1, 2);
+            }
+        }
+        acc[0][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[0], a1[0], acc[0][0], 2, 2, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        wait_groups<F6_PER>(min(nk - 1, t + NS - 1) - (t + 1));
+        __builtin_amdgcn_s_barrier();
+        const bool early = t + NS < nk;
+        // second half of slice t; reads of slice t+1's first half; activation copies of slice t+NS
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            w0[q] = rd(t + 1, w_h[q][0], w_t[q][0]);
+            a0[2 * q] = rd(t + 1, a_h[2 * q][0], a_t[2 * q][0]);
+            a0[2 * q + 1] = rd(t + 1, a_h[2 * q + 1][0], a_t[2 * q + 1][0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (q != 0 || j > 0)
+                    acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[q], a1[j], acc[q][j], 2, 2, 0,
+                                                                                127, 0, 127);
+            if (early) {
+                copy_part(t + NS, 0, q);
+                if (q == 1) copy_part(t + NS, 0, 2);
+            }
+        }
+    }
+
+    if (MODE == MODE_BF16) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = wm * 128 + 32 * j + fr;
+            const float sx = l_sx[r];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c = wn * 64 + 32 * i + 8 * g4 + 4 * fk;
+                    const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
+                    const u32x2 bb = *reinterpret_cast<const u32x2*>(l_b + c);
+                    const float a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
+                                         acc[i][j][4 * g4 + 3]};
+                    const u32x2 pk = epi_bf16x4_f(a4, sx, sw, bb, ep.bias != nullptr);
+                    const int off = r * 512 + (((c >> 3) ^ (r & 31)) << 4) + ((c & 7) << 1);
+                    *reinterpret_cast<u32x2*>(smem + off) = pk;
+                }
+            }
+        }
+        __syncthreads();
+        uint16_t* out = static_cast<uint16_t*>(ep.out);
+#pragma unroll 4
+        for (int it = 0; it < 16; ++it) {
+            const int q = it * NT8 + tid;
+            const int r = q >> 5, c = q & 31;
+            const int m = m0 + r;
+            const int n = n0 + c * 8;
+            if (m >= M || n >= N) continue;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
+            uint16_t* dst = out + (int64_t)m * ep.ldo + n;
+            if (n + 7 < N) {
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+            } else {
+                for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int m = m0 + wm * 128 + 32 * j + fr;
+            if (m >= M) continue;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int n = n0 + wn * 64 + 32 * i + 8 * g4 + 4 * fk;
+                    if (n >= N) continue;
+                    const int32_t a4[4] = {(int32_t)acc[i][j][4 * g4], (int32_t)acc[i][j][4 * g4 + 1],
+                                           (int32_t)acc[i][j][4 * g4 + 2], (int32_t)acc[i][j][4 * g4 + 3]};
+                    store_i32x4(a4, n, N, m, ep);
+                }
+            }
+        }
+    }
+}
+
 template <int MODE>
 hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, int64_t M,
                   int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
@@ -630,6 +906,25 @@ hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_sca
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
         aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_f6_bf16(const uint8_t* a6, int64_t lda, const float* a_scale, const uint8_t* w6,
+                               int64_t ldw, const float* w_scale, const void* bias, void* y, int64_t ldy,
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, 1, 1};
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_f6_w8_kernel<MODE_BF16><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(a6, lda, w6, ldw, (int)M, (int)N,
+                                                                                  (int)K, ep);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_f6_i32(const uint8_t* a6, int64_t lda, const uint8_t* w6, int64_t ldw, int32_t* acc,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    gemm_f6_w8_kernel<MODE_I32><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(a6, lda, w6, ldw, (int)M, (int)N,
+                                                                                 (int)K, ep);
     return hipGetLastError();
 }
 

@@ -48,6 +48,18 @@ hipError_t launch_gemm_w4_i32(const int8_t* aq, int64_t lda, const uint8_t* wp, 
 hipError_t launch_pack_int4(const int8_t* q, int64_t ldq, uint8_t* out, int64_t ldo, int64_t R, int64_t K,
                             hipStream_t stream);
 
+// INT4 codes [R, K] (K % 64 == 0) -> the FP6 E2M3 operand format, 3K/4 bytes per row.
+hipError_t launch_pack_fp6(const int8_t* q, int64_t ldq, uint8_t* out, int64_t ldo, int64_t R, int64_t K,
+                           hipStream_t stream);
+
+// FP6-operand GEMM (K % 128 == 0): a6 [M, 3K/4] and w6 [N, 3K/4] bytes in the FP6
+// operand format; BF16 output with the usual epilogue, or exact INT32 sums.
+hipError_t launch_gemm_f6_bf16(const uint8_t* a6, int64_t lda, const float* a_scale, const uint8_t* w6,
+                               int64_t ldw, const float* w_scale, const void* bias, void* y, int64_t ldy,
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_f6_i32(const uint8_t* a6, int64_t lda, const uint8_t* w6, int64_t ldw, int32_t* acc,
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // out = q * scale (per row or per tensor) as FP32 (out_bf16 = false) or BF16.
 hipError_t launch_dequant(const int8_t* q, int64_t ldq, const float* scale, bool per_row,
                           bool out_bf16, void* out, int64_t ldo, int64_t M, int64_t K,
