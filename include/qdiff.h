@@ -321,7 +321,7 @@ qd_status_t qd_convrot_w4a4_linear(const void* x, qd_dtype_t x_dtype, int64_t M,
  *     bytes  0..15  piece 0 bytes 0..15
  *     bytes 16..31  piece 1 bytes 0..15
  *     bytes 32..47  piece 0 bytes 16..23 then piece 1 bytes 16..23, or the
- *                   two swapped when bit 4 of the row index is set.
+ *                   two swapped when bits 3 and 4 of the row index differ.
  *
  * qd_pack_fp6: codes q [R, K] INT8 in [-7, 7] (other values give undefined
  * bytes) -> out [R, 3K/4] in that format.  K % 64 == 0; q/out 16-byte

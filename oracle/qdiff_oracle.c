@@ -457,7 +457,7 @@ int64_t oracle_pack_fp6(const int8_t* q, int64_t R, int64_t K, uint8_t* out) {
             uint8_t* o = out + r * rb + 48 * j;
             memcpy(o, piece[0], 16);
             memcpy(o + 16, piece[1], 16);
-            int first = (int)((r >> 4) & 1);          /* which piece's tail comes first */
+            int first = (int)(((r >> 3) ^ (r >> 4)) & 1);   /* which piece's tail comes first */
             memcpy(o + 32, piece[first] + 16, 8);
             memcpy(o + 40, piece[1 - first] + 16, 8);
         }

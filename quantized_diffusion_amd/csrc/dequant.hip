@@ -90,7 +90,7 @@ __device__ __forceinline__ uint32_t pack6x4(uint32_t c) {
 
 // One 64-value K block of one row per thread: codes -> the FP6 operand
 // format (see qdiff.h): [piece 0 bytes 0..15 | piece 1 bytes 0..15 | the
-// two 8-byte tails, piece 0's first unless bit 4 of the row index is set].
+// two 8-byte tails, piece 0's first unless bits 3 and 4 of the row index differ].
 __global__ __launch_bounds__(256) void pack_fp6_kernel(const int8_t* __restrict__ q, int64_t ldq,
                                                        uint8_t* __restrict__ out, int64_t ldo, int64_t R,
                                                        int64_t blocks_per_row) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void pack_fp6_kernel(const int8_t* __restrict_
         d[3 * g + 2] = (v2 >> 16) | (v3 << 8);
     }
     uint8_t* dst = out + r * ldo + b * 48;
-    const bool swp = (r >> 4) & 1;
+    const bool swp = ((r >> 3) ^ (r >> 4)) & 1;
     *reinterpret_cast<u32x4*>(dst) = u32x4{d[0], d[1], d[2], d[3]};
     *reinterpret_cast<u32x4*>(dst + 16) = u32x4{d[6], d[7], d[8], d[9]};
     *reinterpret_cast<u32x4*>(dst + 32) = swp ? u32x4{d[10], d[11], d[4], d[5]} : u32x4{d[4], d[5], d[10], d[11]};

@@ -603,19 +603,22 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
 // the two K halves of a slice) with a slice of 128 values: 96 bytes per row,
 // one MFMA K step (64 values, 48 bytes) per half.  Operands arrive in the FP6
 // operand format (qdiff.h): per 64-value block, [piece 0 bytes 0..15 |
-// piece 1 bytes 0..15 | tails], the tails swapped when bit 4 of the row is
-// set.  A lane (row r, K half h) takes piece h as one 16-byte read (slot h)
-// and one 8-byte read (tail half h ^ swap(r)); in LDS the six 16-byte slots
-// of a row are rotated by one when bit 3 of the row is set.  Together these
-// make both reads free of bank conflicts.  Three 48 KB stages.
+// piece 1 bytes 0..15 | tails], the tails swapped when bits 3 and 4 of the
+// row differ.  In LDS a row's slice is six 16-byte slots (96 bytes, so one
+// copy instruction moves ~11 whole row slices), with the two K steps' slot
+// groups exchanged when bits 2 and 3 of the row differ.  A lane (row r, K
+// half h) takes piece h as one 16-byte read (its head slot) and one 8-byte
+// read (tail half h ^ swap(r)).  The exchange and the swap together put the
+// rows of every read phase on distinct banks (for 32 or 64 banks), so both
+// reads are free of bank conflicts.  Three 48 KB stages.
 constexpr int F6_BK = 128;                 // values per slice
 constexpr int F6_RB = 96;                  // bytes per row per slice
 constexpr int F6_STG = (BM + BN) * F6_RB;  // 48 KB per stage
 constexpr int F6_NS = 3;
 constexpr int F6_PER = 6;                  // copies per slice per thread (3 activation + 3 weight)
 
-__device__ __forceinline__ int f6_rot(int r) { return (r >> 3) & 1; }
-__device__ __forceinline__ int f6_swp(int r) { return (r >> 4) & 1; }
+__device__ __forceinline__ int f6_rot(int r) { return 3 * (((r >> 2) ^ (r >> 3)) & 1); }   // slots
+__device__ __forceinline__ int f6_swp(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
 
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -686,7 +689,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
 
     // copies: instruction i (0..2) of wave w fills the 16-byte LDS slots
     // (3w + i) * 64 + lane of an operand's 24 KB stage part; slot q holds
-    // row q / 6, physical slot q % 6 = logical slot rotated by f6_rot(row)
+    // row q / 6, physical slot q % 6 = logical slot + f6_rot(row) (mod 6)
     const uint8_t* ga[3];
     const uint8_t* gw[3];
     uint32_t lslot[3];
@@ -695,8 +698,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
         const int q = (3 * wave + i) * 64 + lane;
         const int row = q / 6;
         const int phys = q - 6 * row;
-        int logical = phys - f6_rot(row);
-        logical += logical < 0 ? 6 : 0;
+        const int logical = (phys + f6_rot(row)) % 6;   // rot is 0 or 3: its own inverse
         ga[i] = A + (int64_t)min(m0 + row, M - 1) * lda + 16 * logical;
         gw[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 16 * logical;
         lslot[i] = (uint32_t)((3 * wave + i) * 1024);
@@ -779,6 +781,13 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
             for (int j = 0; j < 4; ++j)
                 acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[q], a0[j], acc[q][j], 2, 2, 0, 127,
                                                                             0, 127);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (late) {
                 copy_part(t + NS - 1, 1, q);
                 if (q == 1) copy_part(t + NS - 1, 1, 2);
@@ -801,6 +810,13 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
                 if (q != 0 || j > 0)
                     acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[q], a1[j], acc[q][j], 2, 2, 0,
                                                                                 127, 0, 127);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (early) {
                 copy_part(t + NS, 0, q);
                 if (q == 1) copy_part(t + NS, 0, 2);

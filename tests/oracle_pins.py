@@ -417,13 +417,13 @@ def check_linear_accuracy(O):
 def _decode_fp6_rows(packed: np.ndarray, K: int) -> list:
     """Values of the FP6 operand format, decoded from its description: per 64
     values, [piece 0 head 16 B | piece 1 head 16 B | tails (swapped when row
-    bit 4 is set)], value i of a piece in bits 6i.., E2M3 fields."""
+    bits 3 and 4 differ)], value i of a piece in bits 6i.., E2M3 fields."""
     rows = []
     for r, row in enumerate(packed):
         vals = []
         for j in range(K // 64):
             blk = bytes(row[48 * j:48 * j + 48])
-            t0, t1 = (blk[32:40], blk[40:48]) if (r >> 4) & 1 == 0 else (blk[40:48], blk[32:40])
+            t0, t1 = (blk[32:40], blk[40:48]) if ((r >> 3) ^ (r >> 4)) & 1 == 0 else (blk[40:48], blk[32:40])
             for piece in (blk[0:16] + t0, blk[16:32] + t1):
                 bits = int.from_bytes(piece, "little")
                 for i in range(32):
@@ -437,7 +437,7 @@ def _decode_fp6_rows(packed: np.ndarray, K: int) -> list:
 
 def check_fp6_pack(O):
     g = np.random.Generator(np.random.PCG64(40))
-    q = g.integers(-7, 8, (40, 192), dtype=np.int64).astype(np.int8)     # rows 16..31 have bit 4 set
+    q = g.integers(-7, 8, (40, 192), dtype=np.int64).astype(np.int8)     # rows with every (bit 3, bit 4)
     q[0, :15] = np.arange(-7, 8)
     packed = O.pack_fp6(q)
     assert packed.shape == (40, 144)
