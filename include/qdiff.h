@@ -331,6 +331,16 @@ qd_status_t qd_pack_fp6(const int8_t* q, int64_t R, int64_t K, int64_t ldq, uint
                         hipStream_t stream);
 
 /*
+ * The rotating INT4 quantizer (as qd_quantize_and_rotate_rowwise_int4) writing
+ * the codes straight into the FP6 operand format: q6 [M, 3K/4] bytes, row
+ * stride ld6 bytes (>= 3K/4, a multiple of 16), row_scale [M].  BF16 or FP16
+ * input; block 256, K % 256 == 0.
+ */
+qd_status_t qd_quantize_and_rotate_rowwise_fp6(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                               int64_t ldx, int32_t block, uint8_t* q6, int64_t ld6,
+                                               float* row_scale, hipStream_t stream);
+
+/*
  * The GEMM on FP6 operands: a6 [M, 3K/4] (stride lda bytes) and w6
  * [N, 3K/4] (stride ldw bytes) in the FP6 operand format, a_scale [M],
  * w_scale [N], bias [N] BF16 or NULL, y [M, N] BF16:
@@ -346,8 +356,9 @@ qd_status_t qd_fp6_gemm_i32(const uint8_t* a6, int64_t M, int64_t K, int64_t lda
 
 /*
  * convrot_w4a4_linear with FP6 weights w6 [N, 3K/4] (qd_quantize_and_rotate_rowwise_int4
- * on W, then qd_pack_fp6): the rotating INT4 quantizer, qd_pack_fp6 of the
- * activation codes, then the FP6 GEMM.  Same results as qd_convrot_w4a4_linear.
+ * on W, then qd_pack_fp6): the rotating INT4 quantizer writing FP6 (BF16 or
+ * FP16 x; FP32 x: INT4 codes, then qd_pack_fp6), then the FP6 GEMM.  Same
+ * results as qd_convrot_w4a4_linear.
  * K % 256 == 0; workspace of qd_w4a4_fp6_workspace_size(M, K) bytes,
  * 256-byte aligned.
  */

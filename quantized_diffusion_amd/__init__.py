@@ -34,6 +34,7 @@ __all__ = [
     "tensorwise_workspace_size", "int8_scaled_mm_ex", "input_act", "quantize_rowwise_act", "int8_linear_act",
     "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU", "pack_fp6", "fp6_scaled_mm",
     "fp6_gemm_i32", "w4a4_fp6_workspace_size", "convrot_w4a4_linear_fp6", "prepare_weights_w4a4_fp6",
+    "quantize_and_rotate_rowwise_fp6",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -50,6 +51,7 @@ EXPORTED_SYMBOLS = (
     "qd_quantize_tensorwise_workspace_size", "qd_quantize_int8_tensorwise", "qd_int8_scaled_mm_ex",
     "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act", "qd_pack_fp6", "qd_fp6_scaled_mm",
     "qd_fp6_gemm_i32", "qd_w4a4_fp6_workspace_size", "qd_convrot_w4a4_linear_fp6",
+    "qd_quantize_and_rotate_rowwise_fp6",
 )
 
 
@@ -118,6 +120,8 @@ def lib():
         L.qd_fp6_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
         L.qd_w4a4_fp6_workspace_size.restype = SZ
         L.qd_w4a4_fp6_workspace_size.argtypes = [I64, I64]
+        L.qd_quantize_and_rotate_rowwise_fp6.restype = St
+        L.qd_quantize_and_rotate_rowwise_fp6.argtypes = [P, St, I64, I64, I64, I32, P, I64, P, P]
         L.qd_convrot_w4a4_linear_fp6.restype = St
         L.qd_convrot_w4a4_linear_fp6.argtypes = [P, St, I64, I64, I64, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
         _lib = L
@@ -432,6 +436,23 @@ def pack_fp6(q, out=None):
     _mat(out, "out")
     _check(lib().qd_pack_fp6(_ptr(q), R, K, q.stride(0), _ptr(out), out.stride(0), _stream(dev)))
     return out
+
+
+def quantize_and_rotate_rowwise_fp6(x, block: int = 256, out_q6=None, out_scale=None):
+    """Rotating INT4 quantizer writing the FP6 operand format (BF16/FP16 x):
+    returns (q6 uint8 [M, 3K/4], row scales fp32 [M])."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, out_q6, out_scale)
+    M, K = x.shape
+    if out_q6 is None:
+        out_q6 = torch.empty((M, _f6_ld(K)), dtype=torch.uint8, device=dev)[:, :K // 4 * 3]
+    if out_scale is None:
+        out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _mat(out_q6, "q6")
+    _check(lib().qd_quantize_and_rotate_rowwise_fp6(_ptr(x), _dtype_code(x), M, K, x.stride(0), block,
+                                                    _ptr(out_q6), out_q6.stride(0), _ptr(out_scale), _stream(dev)))
+    return out_q6, out_scale
 
 
 def prepare_weights_w4a4_fp6(w, block: int = 256):

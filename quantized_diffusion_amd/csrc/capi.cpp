@@ -40,14 +40,16 @@ int dtype_size(qd_dtype_t dt) { return dt == QD_F32 ? 4 : 2; }
 bool dtype_ok(qd_dtype_t dt) { return dt == QD_F32 || dt == QD_BF16 || dt == QD_F16; }
 
 // Shared checks of the quantizers.
+// min_ldq: smallest row stride of q in bytes (K for one code per byte).
 qd_status_t check_quant(const char* fn, const void* x, qd_dtype_t dt, int64_t M, int64_t K,
                         int64_t ldx, bool rotate, int32_t block, const int8_t* q, int64_t ldq,
-                        const float* scale) {
+                        const float* scale, int64_t min_ldq = -1) {
     if (M < 0 || K <= 0) return fail(QD_EINVAL, fn, "need M >= 0 and K > 0 (M=%lld, K=%lld)", (long long)M, (long long)K);
     if (M > 0 && (!x || !q || !scale)) return fail(QD_EINVAL, fn, "null pointer argument");
     if (!dtype_ok(dt)) return fail(QD_EUNSUPPORTED, fn, "unknown input dtype %d", (int)dt);
     if (ldx < K) return fail(QD_EINVAL, fn, "ldx (%lld) < K (%lld)", (long long)ldx, (long long)K);
-    if (ldq < K) return fail(QD_EINVAL, fn, "ldq (%lld) < K (%lld)", (long long)ldq, (long long)K);
+    if (min_ldq < 0) min_ldq = K;
+    if (ldq < min_ldq) return fail(QD_EINVAL, fn, "ldq (%lld) < %lld", (long long)ldq, (long long)min_ldq);
     if (rotate && block != 256) return fail(QD_EUNSUPPORTED, fn, "rotation block must be 256 (got %d)", block);
     if (rotate && K % 256 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of the 256-wide rotation block", (long long)K);
     if (K % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 16", (long long)K);
@@ -455,6 +457,19 @@ qd_status_t qd_fp6_gemm_i32(const uint8_t* a6, int64_t M, int64_t K, int64_t lda
     return hip_status(fn, qd::launch_gemm_f6_i32(a6, lda, w6, ldw, acc, ldc, M, N, K, stream));
 }
 
+qd_status_t qd_quantize_and_rotate_rowwise_fp6(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                               int64_t ldx, int32_t block, uint8_t* q6, int64_t ld6,
+                                               float* row_scale, hipStream_t stream) {
+    const char* fn = "qd_quantize_and_rotate_rowwise_fp6";
+    if (x_dtype != QD_BF16 && x_dtype != QD_F16)
+        return fail(QD_EUNSUPPORTED, fn, "FP6 output needs a BF16 or FP16 input");
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, true, block, reinterpret_cast<int8_t*>(q6), ld6,
+                                 row_scale, K / 4 * 3);
+    if (st != QD_OK) return st;
+    if (M == 0) return ok();
+    return hip_status(fn, qd::launch_rotquant_fp6(x, (int)x_dtype, M, K, ldx, q6, ld6, row_scale, stream));
+}
+
 size_t qd_w4a4_fp6_workspace_size(int64_t M, int64_t K) {
     if (M <= 0 || K <= 0) return 0;
     return ws_codes_bytes(M, K) + round_up((size_t)M * (size_t)f6_ld(K), kAlign) + round_up((size_t)M * sizeof(float), kAlign);
@@ -486,9 +501,14 @@ qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_
     if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
     if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
         return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
-    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, true, 7, M, K, ldx, aq, ldq, sx, stream);
-    if (e != hipSuccess) return hip_status(fn, e);
-    e = qd::launch_pack_fp6(aq, ldq, a6, lda6, M, K, stream);
+    hipError_t e;
+    if (x_dtype == QD_BF16 || x_dtype == QD_F16) {
+        // 16-bit inputs: the quantizer writes the FP6 operand format itself
+        e = qd::launch_rotquant_fp6(x, (int)x_dtype, M, K, ldx, a6, lda6, sx, stream);
+    } else {
+        e = qd::launch_rotquant(x, (int)x_dtype, true, 7, M, K, ldx, aq, ldq, sx, stream);
+        if (e == hipSuccess) e = qd::launch_pack_fp6(aq, ldq, a6, lda6, M, K, stream);
+    }
     if (e != hipSuccess) return hip_status(fn, e);
     return hip_status(fn, qd::launch_gemm_f6_bf16(a6, lda6, sx, w6, ldw, w_scale, bias_bf16, y_bf16, ldy, M, N, K,
                                                   stream));

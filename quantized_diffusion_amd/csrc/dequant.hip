@@ -8,6 +8,7 @@
 
 #include "qd_device.h"
 #include "qd_launch.h"
+#include "qd_quant.h"
 
 namespace qd {
 namespace {
@@ -70,22 +71,6 @@ __global__ __launch_bounds__(256) void pack_int4_kernel(const int8_t* __restrict
     }
     u32x4 o = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
     *reinterpret_cast<u32x4*>(out + r * ldo + c * 16) = o;
-}
-
-// FP6 E2M3 bits of four INT4 codes (bytes of w, each in [-7, 7]), one per
-// byte: sign in bit 5, exponent (bias 1) in bits 4..3, mantissa in 2..0;
-// every integer of [-7, 7] is exact (1 = 1.0 x 2^0 ... 7 = 1.75 x 2^2).
-__device__ __forceinline__ uint32_t e2m3x4(uint32_t w) {
-    const uint32_t s = (w >> 7) & 0x01010101u;        // sign per byte
-    const uint32_t a = (w ^ (s * 0xFFu)) + s;          // |code| per byte (no carries: <= 7)
-    const uint32_t e = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, a);   // magnitudes 0,1,2,3 | 4,5,6,7
-    return e | (s << 5);
-}
-
-// Four 6-bit fields (one per byte) -> 24 bits, field i at bits 6i.
-__device__ __forceinline__ uint32_t pack6x4(uint32_t c) {
-    const uint32_t u = (c & 0x00FF00FFu) | (((c >> 8) & 0x00FF00FFu) << 6);
-    return (u & 0xFFFu) | ((u >> 16) << 12);
 }
 
 // One 64-value K block of one row per thread: codes -> the FP6 operand

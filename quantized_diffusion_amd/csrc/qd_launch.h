@@ -14,6 +14,11 @@ hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int6
                            int64_t ldx, int8_t* q, int64_t ldq, float* scale, hipStream_t stream,
                            int act = 0);
 
+// Rotating INT4 quantizer writing the FP6 operand format directly (16-bit
+// inputs, dtype 1 or 2): q6 [M, 3K/4] bytes, row stride ld6 (multiple of 16).
+hipError_t launch_rotquant_fp6(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q6,
+                               int64_t ld6, float* scale, hipStream_t stream);
+
 // out[i] = act(x[i]) rounded to the 16-bit input type (dtype 1 BF16, 2 FP16).
 hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* out, hipStream_t stream);
 

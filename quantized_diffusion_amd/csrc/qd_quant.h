@@ -65,4 +65,20 @@ __device__ __forceinline__ uint32_t pack4(uint32_t a, uint32_t b, uint32_t c, ui
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
+// FP6 E2M3 bits of four INT4 codes (bytes of w, each in [-7, 7]), one per
+// byte: sign in bit 5, exponent (bias 1) in bits 4..3, mantissa in 2..0;
+// every integer of [-7, 7] is exact (1 = 1.0 x 2^0 ... 7 = 1.75 x 2^2).
+__device__ __forceinline__ uint32_t e2m3x4(uint32_t w) {
+    const uint32_t s = (w >> 7) & 0x01010101u;        // sign per byte
+    const uint32_t a = (w ^ (s * 0xFFu)) + s;          // |code| per byte (no carries: <= 7)
+    const uint32_t e = __builtin_amdgcn_perm(0x1E1C1A18u, 0x14100800u, a);   // magnitudes 0,1,2,3 | 4,5,6,7
+    return e | (s << 5);
+}
+
+// Four 6-bit fields (one per byte) -> 24 bits, field i at bits 6i.
+__device__ __forceinline__ uint32_t pack6x4(uint32_t c) {
+    const uint32_t u = (c & 0x00FF00FFu) | (((c >> 8) & 0x00FF00FFu) << 6);
+    return (u & 0xFFFu) | ((u >> 16) << 12);
+}
+
 }  // namespace qd

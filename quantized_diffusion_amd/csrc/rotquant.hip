@@ -45,8 +45,9 @@
 // rotated path are staged through LDS per wave: each lane writes its chunks
 // into its quad's 256-byte block image, then lane l stores bytes
 // [16 l, 16 l + 16) of four consecutive block images, so one store
-// instruction writes four whole blocks (1 KB, whole 128-byte lines) and the
-// stores can bypass the caches.
+// instruction writes four whole blocks (1 KB, whole 128-byte lines).  The
+// stores keep the default cache policy: the GEMM reads the codes next, and a
+// whole step measured faster that way than with streaming stores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,6 +89,16 @@ template <int ACT> struct kMaxThreads { static constexpr int value = (ACT == 0 |
 
 constexpr int kStageStride = 288;                 // bytes per block image in LDS (256 + 32: spreads banks)
 constexpr int kStageWave = 16 * kStageStride;     // per wave: 16 quads
+// Whole-line code stores.  The codes are read again by the GEMM that follows
+// (and fit the Infinity Cache at the sizes used), so they are stored with the
+// default policy unless kStreamCodes is set.
+constexpr bool kStreamCodes = false;
+__device__ __forceinline__ void store_codes(const u32x4& v, int8_t* dst) {
+    if (kStreamCodes) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+    else *reinterpret_cast<u32x4*>(dst) = v;
+}
+constexpr int kF6Stride = 208;                    // FP6 block image: 192 bytes (+16: an odd count of 16-byte slots)
+constexpr int kF6Wave = 16 * kF6Stride;
 
 // One cross-lane butterfly stage for one value: own + sign * partner, the
 // partner read through DPP inside the FMA (a separate v_mov_b32_dpp would
@@ -104,14 +115,19 @@ __device__ __forceinline__ float fmac_quad_xor2(float own, float sign) {
     return own;
 }
 
-template <class In, bool ROT, int QMAX, bool STAGE>
+template <class In, bool ROT, int QMAX, bool STAGE, bool F6>
 __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bits, int row, int blk,
                                                int ql, int K, int8_t* __restrict__ q, int64_t ldq,
                                                float* __restrict__ scale, uint8_t* img);
 
 // STAGE (rotated path only): codes leave through the LDS block images.
 // ACT: input activation applied to each widened element (16-bit inputs).
-template <class In, bool ROT, int QMAX, bool STAGE, int ACT>
+// F6 (INT4 codes, 16-bit inputs, STAGE): the codes are written as FP6 E2M3
+// fields straight into the FP6 operand format (q is then the FP6 matrix,
+// ldq its row stride in bytes, 3K/4 bytes per row): each 8-code chunk is
+// 48 bits, three 2-byte pieces placed in the block's 192-byte image at their
+// head / tail positions.
+template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false>
 __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const uint8_t* __restrict__ x,
                                                         int64_t ldx_bytes, int M, int K, int nb,
                                                         int R, int8_t* __restrict__ q,
@@ -217,9 +233,36 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
     __syncthreads();
     if (active && ql == 0) atomicMax(&row_amax[rl], f_bits(am));
     __syncthreads();
-    if (active) quantize_store<In, ROT, QMAX, STAGE>(v, row_amax[rl], row, blk, ql, K, q, ldq, scale,
-                                                     stage + (tid >> 6) * kStageWave + ((tid >> 2) & 15) * kStageStride);
-    if (STAGE) {
+    if (active) {
+        uint8_t* img = F6 ? stage + (tid >> 6) * kF6Wave + ((tid >> 2) & 15) * kF6Stride
+                          : stage + (tid >> 6) * kStageWave + ((tid >> 2) & 15) * kStageStride;
+        quantize_store<In, ROT, QMAX, STAGE, F6>(v, row_amax[rl], row, blk, ql, K, q, ldq, scale, img);
+    }
+    if (F6) {
+        // twelve 16-byte slots per block image; lane l stores slots l, l+64, l+128 of the wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int lane = tid & 63;
+        const uint8_t* imgs = stage + (tid >> 6) * kF6Wave;
+        u32x4 val[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int sl = lane + 64 * j;
+            val[j] = *reinterpret_cast<const u32x4*>(imgs + (sl / 12) * kF6Stride + 16 * (sl % 12));
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int sl = lane + 64 * j;
+            const int qq = (tid >> 6) * 16 + sl / 12;
+            const int rl2 = (int)(__umul24((uint32_t)qq, nb_inv) >> 20);
+            const int row2 = blockIdx.x * R + rl2;
+            if (rl2 < R && row2 < M) {
+                int8_t* dst = q + (int64_t)row2 * ldq + (qq - rl2 * nb) * 192 + 16 * (sl % 12);
+                store_codes(val[j], dst);
+            }
+        }
+    } else if (STAGE) {
         // Whole-block stores of the wave's 16 block images (see the header).
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -236,7 +279,7 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
             const int row2 = blockIdx.x * R + rl2;
             if (rl2 < R && row2 < M) {
                 int8_t* dst = q + (int64_t)row2 * ldq + (qq - rl2 * nb) * 256 + 16 * (lane & 15);
-                __builtin_nontemporal_store(val[j], reinterpret_cast<u32x4*>(dst));
+                store_codes(val[j], dst);
             }
         }
     }
@@ -244,7 +287,7 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
 
 // Scale and codes of one quad's values (see the header).  Rotated path: the
 // codes go to the quad's block image `img` in LDS; otherwise straight to q.
-template <class In, bool ROT, int QMAX, bool STAGE>
+template <class In, bool ROT, int QMAX, bool STAGE, bool F6>
 __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bits, int row, int blk,
                                                int ql, int K, int8_t* __restrict__ q, int64_t ldq,
                                                float* __restrict__ scale, uint8_t* img) {
@@ -290,6 +333,24 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
                     code[e] = mode == 0 ? 0u : exact_code<ROT, QMAX>(w, tau, s);
             }
         }
+        if (F6 && E == 8) {
+            // 8 codes -> 48 bits of E2M3 fields; piece p = (c % 8) / 4 of K block
+            // c / 8, piece bytes 6 (c % 4) .. +5, each 2-byte part at its head
+            // (bytes < 16) or tail position
+            const uint32_t g0 = pack6x4(e2m3x4(pack4(code[0], code[1], code[2], code[3])));
+            const uint32_t g1 = pack6x4(e2m3x4(pack4(code[4 % E], code[5 % E], code[6 % E], code[7 % E])));
+            const uint32_t lo = g0 | (g1 << 24), hi = g1 >> 8;
+            const uint32_t part[3] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu};
+            const int kb = c >> 3, p = (c >> 2) & 1, o = 6 * (c & 3);
+            const int swp = ((row >> 3) ^ (row >> 4)) & 1;
+#pragma unroll
+            for (int h = 0; h < 3; ++h) {
+                const int x = o + 2 * h;
+                const int pos = kb * 48 + (x < 16 ? 16 * p + x : 32 + 8 * (p ^ swp) + (x - 16));
+                *reinterpret_cast<uint16_t*>(img + pos) = (uint16_t)part[h];
+            }
+            continue;
+        }
         uint8_t* out = STAGE ? img + c * E : reinterpret_cast<uint8_t*>(dst) + c * E;
         if (E == 8) {
             u32x2 p;
@@ -303,19 +364,19 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
     }
 }
 
-template <class In, bool ROT, int QMAX, bool STAGE, int ACT>
+template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false>
 hipError_t launch_staged(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                          float* scale, hipStream_t stream, int R, int threads) {
     constexpr int ESZ = 16 / In::E;
     const int nb = (int)((K + 255) / 256);
     const int64_t grid = (M + R - 1) / R;
-    const size_t lds = STAGE ? (size_t)(threads / 64) * kStageWave : 0;
-    rotquant_kernel<In, ROT, QMAX, STAGE, ACT><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
+    const size_t lds = F6 ? (size_t)(threads / 64) * kF6Wave : STAGE ? (size_t)(threads / 64) * kStageWave : 0;
+    rotquant_kernel<In, ROT, QMAX, STAGE, ACT, F6><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
         static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
     return hipGetLastError();
 }
 
-template <class In, bool ROT, int QMAX, int ACT = ACT_NONE>
+template <class In, bool ROT, int QMAX, int ACT = ACT_NONE, bool F6 = false>
 hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                         float* scale, hipStream_t stream) {
     const int nb = (int)((K + 255) / 256);
@@ -333,6 +394,8 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
     if (best_threads > MAXT) return hipErrorInvalidValue;   // rows longer than the caller's checks allow
+    if (F6)
+        return launch_staged<In, ROT, QMAX, true, ACT, true>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
     if (ROT)
         return launch_staged<In, ROT, QMAX, true, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
     return launch_staged<In, ROT, QMAX, false, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
@@ -405,6 +468,13 @@ hipError_t launch_act16(const void* x, int64_t n, int act, void* out, hipStream_
 }
 
 }  // namespace
+
+hipError_t launch_rotquant_fp6(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q6,
+                               int64_t ld6, float* scale, hipStream_t stream) {
+    int8_t* q = reinterpret_cast<int8_t*>(q6);
+    if (dtype == 1) return launch_typed<InBF16, true, 7, ACT_NONE, true>(x, M, K, ldx, q, ld6, scale, stream);
+    return launch_typed<InF16, true, 7, ACT_NONE, true>(x, M, K, ldx, q, ld6, scale, stream);
+}
 
 hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* out, hipStream_t stream) {
     return dtype == 1 ? launch_act16<1>(x, n, act, out, stream) : launch_act16<2>(x, n, act, out, stream);

@@ -238,3 +238,28 @@ def test_act_validation():
     ]:
         st, msg = _status(L.qd_input_act, *args)
         assert st == status and needle in msg, (args, st, msg)
+
+
+def test_fp6_validation():
+    L = qd.lib()
+    # fused FP6 quantizer: 16-bit input only, ld6 >= 3K/4 and a multiple of 16
+    for args, status, needle in [
+        ((FAKE, qd.QD_F32, 4, 512, 512, 256, FAKE, 384, FAKE, STREAM), qd.QD_EUNSUPPORTED, "BF16 or FP16"),
+        ((FAKE, Q, 4, 512, 512, 256, FAKE, 368, FAKE, STREAM), qd.QD_EINVAL, "ldq"),
+        ((FAKE, Q, 4, 512, 512, 256, FAKE, 392, FAKE, STREAM), qd.QD_EUNSUPPORTED, "multiples of 16"),
+        ((FAKE, Q, 4, 640, 640, 256, FAKE, 480, FAKE, STREAM), qd.QD_EUNSUPPORTED, "256"),
+    ]:
+        st, msg = _status(L.qd_quantize_and_rotate_rowwise_fp6, *args)
+        assert st == status and needle in msg, (args, st, msg)
+    assert L.qd_quantize_and_rotate_rowwise_fp6(FAKE, Q, 0, 512, 512, 256, FAKE, 384, FAKE, STREAM) == qd.QD_OK
+    # packing and the FP6 GEMM
+    st, msg = _status(L.qd_pack_fp6, FAKE, 4, 96, 96, FAKE, 80, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 64" in msg
+    st, msg = _status(L.qd_pack_fp6, FAKE, 4, 128, 128, FAKE, 80, STREAM)
+    assert st == qd.QD_EINVAL and "3K/4" in msg
+    st, msg = _status(L.qd_fp6_scaled_mm, FAKE, 8, 192, 144, FAKE, FAKE, 8, 144, FAKE, NULL, FAKE, 8, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 128" in msg
+    st, msg = _status(L.qd_fp6_scaled_mm, FAKE, 8, 256, 176, FAKE, FAKE, 8, 192, FAKE, NULL, FAKE, 8, STREAM)
+    assert st == qd.QD_EINVAL and "3K/4" in msg
+    st, msg = _status(L.qd_fp6_gemm_i32, FAKE, 8, 256, 192, FAKE, 8, 192, FAKE, 10, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "multiple of 4" in msg

@@ -135,3 +135,40 @@ def test_w4a4_fp6_full_size(qd, O):
     ci = torch.from_numpy(cols).to(dev)
     n = assert_bf16_within_1ulp(bf16_bits(y[ri, ci]), yo, "w4a4 fp6 full size")
     say(f"  {n} of {yo.size} sampled outputs not bit-identical")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M,K", [(1, 256), (33, 1280), (300, 28672), (2, 65536)])
+def test_quantize_fp6_direct(qd, O, dtype, M, K):
+    """The rotating INT4 quantizer writing FP6 directly equals the oracle's
+    codes packed into the FP6 operand format, byte for byte."""
+    say(f"quantize fp6 direct {dtype} M={M} K={K}")
+    g = np.random.Generator(np.random.PCG64(840 + M + K))
+    xf = g.standard_normal((M, K), dtype=np.float32)
+    xf[:, g.choice(K, size=max(1, K // 100), replace=False)] *= 20
+    if dtype == "bf16":
+        from synth import f32_to_bf16_bits
+        x = f32_to_bf16_bits(xf)
+        xd = to_dev_bf16(x)
+    else:
+        x = xf.astype(np.float16)
+        xd = to_dev(x)
+    q6, s = qd.quantize_and_rotate_rowwise_fp6(xd)
+    qo, so = O.quantize_rowwise(x, dtype, 256, qmax=7)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q6), O.pack_fp6(qo))
+
+
+def test_convrot_w4a4_linear_fp6_f32_input(qd, O):
+    """FP32 activations take the two-step route (INT4 codes, then packing)."""
+    say("convrot_w4a4_linear_fp6 f32 input")
+    g = np.random.Generator(np.random.PCG64(850))
+    M, K, N = 70, 512, 136
+    x = g.standard_normal((M, K)).astype(np.float32)
+    wf = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w6, sw = qd.prepare_weights_w4a4_fp6(to_dev(wf))
+    y = qd.convrot_w4a4_linear_fp6(to_dev(x), w6, sw)
+    wq_o, sw_o = O.prepare_weights(wf, 256, qmax=7)
+    yo = O.linear(x, wq_o, sw_o, None, "f32", 256, qmax=7)
+    n = assert_bf16_within_1ulp(bf16_bits(y), yo, "w4a4 fp6 f32 input")
+    say(f"  {n} of {yo.size} outputs differ from the oracle (allowed: 1 ulp)")
