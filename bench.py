@@ -44,7 +44,11 @@ def log(*a):
 
 
 def kernel_hash(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code (comments and blank lines dropped)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    code = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+    return hashlib.sha256("\n".join(ln for ln in code if ln).encode()).hexdigest()[:16]
 
 
 def load_traffic(workload_name: str):
@@ -249,7 +253,7 @@ def main():
     g_min_bytes = float((M * K * 3 // 4 + N * K * 3 // 4) if fp6 else (M * K + (N * K // 2 if int4 else N * K))) \
         + 2 * M * N + 4 * M + 4 * N + 2 * N
     gemm_tops = ops / (ms_g * 1e-3) / 1e12
-    traffic = load_traffic(w.name)
+    traffic = load_traffic(w.name + (" (FP6)" if fp6 else ""))
     out = {
         "metric": (f"W4A4 rotated linear TOPS on the FP6 matrix path (incl. rotate+quant) & % of INT8 MFMA "
                    f"peak, M{M}/K{K}/N{N}" if fp6 else
@@ -277,11 +281,14 @@ def main():
         "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
         "roofline": {"bound": "mfma", "kernel": ("gemm_f6_w8_kernel<MODE_BF16>" if fp6 else
                                                  "gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4>" if int4 else
-                                                 "gemm_i8_w8_kernel<MODE_BF16, 4, WF_I8>") + " (fused bf16 epilogue)",
+                                                 "gemm_i8_w12_kernel<MODE_BF16> (256x384 tiles)"
+                                                 if qd.int8_gemm_tiles(M, N, K) == qd.GEMM_TILES_256x384 else
+                                                 "gemm_i8_w8_kernel<MODE_BF16, 4, WF_I8> (256x256 tiles)")
+                     + " (fused bf16 epilogue)",
                      "achieved": round(gemm_tops, 2), "peak": PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS,
                      "unit": "TFLOP/s" if fp6 else "TOP/s",
                      "frac": round(gemm_tops / (PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS), 4),
-                     "traffic": None if fp6 else traffic},
+                     "traffic": traffic},
         "kernels": {
             "rotquant": {"ms": round(ms_q, 5), "algorithmic_bytes": q_bytes,
                          "GB_per_s": round(q_bytes / (ms_q * 1e-3) / 1e9, 1),

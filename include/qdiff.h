@@ -226,6 +226,23 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
                              int64_t ldc, hipStream_t stream);
 
 /*
+ * Output tile of the INT8-weight GEMM kernels (K % 64 == 0) behind
+ * qd_int8_linear, qd_int8_linear_act, qd_int8_scaled_mm, qd_int8_scaled_mm_ex
+ * and qd_int8_gemm_i32.  QD_GEMM_TILES_AUTO (the default) chooses 256 x 256
+ * or 256 x 384 tiles by shape (the wide tile moves 17 % fewer bytes from L2
+ * into LDS per MAC; the narrow one wastes less on small or ragged grids); the
+ * other values fix one tile for every later launch in the process, for
+ * tuning and for testing both kernels on the same shapes.  Results are
+ * identical either way.  The setting is process-wide (not per stream) and
+ * read when a GEMM is enqueued.  QD_EINVAL for any other value.
+ */
+typedef enum { QD_GEMM_TILES_AUTO = 0, QD_GEMM_TILES_256x256 = 1, QD_GEMM_TILES_256x384 = 2 } qd_gemm_tiles_t;
+qd_status_t qd_set_gemm_tiles(qd_gemm_tiles_t tiles);
+/* The tile (QD_GEMM_TILES_256x256 or QD_GEMM_TILES_256x384) an INT8-weight
+ * GEMM of this shape would use under the current setting. */
+qd_gemm_tiles_t qd_int8_gemm_tiles(int64_t M, int64_t N, int64_t K);
+
+/*
  * Tensor-wise scaling (comfy-kitchen 0.2.40, "Huawei Ascend backend":
  * quantize_int8_tensorwise; "HIP backend": tensor-wise is the scaling its
  * GEMMs take).

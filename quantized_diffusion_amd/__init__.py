@@ -34,7 +34,8 @@ __all__ = [
     "tensorwise_workspace_size", "int8_scaled_mm_ex", "input_act", "quantize_rowwise_act", "int8_linear_act",
     "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU", "pack_fp6", "fp6_scaled_mm",
     "fp6_gemm_i32", "w4a4_fp6_workspace_size", "convrot_w4a4_linear_fp6", "prepare_weights_w4a4_fp6",
-    "quantize_and_rotate_rowwise_fp6",
+    "quantize_and_rotate_rowwise_fp6", "set_gemm_tiles", "int8_gemm_tiles", "GEMM_TILES_AUTO", "GEMM_TILES_256x256",
+    "GEMM_TILES_256x384",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -42,6 +43,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so
 QD_OK, QD_EINVAL, QD_EUNSUPPORTED, QD_EHIP = 0, 1, 2, 3
 QD_F32, QD_BF16, QD_F16 = 0, 1, 2
 ACT_NONE, ACT_GELU_TANH, ACT_GELU_ERF, ACT_SILU, ACT_RELU = 0, 1, 2, 3, 4
+GEMM_TILES_AUTO, GEMM_TILES_256x256, GEMM_TILES_256x384 = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "qd_last_error", "qd_version", "qd_quantize_and_rotate_rowwise",
@@ -51,7 +53,7 @@ EXPORTED_SYMBOLS = (
     "qd_quantize_tensorwise_workspace_size", "qd_quantize_int8_tensorwise", "qd_int8_scaled_mm_ex",
     "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act", "qd_pack_fp6", "qd_fp6_scaled_mm",
     "qd_fp6_gemm_i32", "qd_w4a4_fp6_workspace_size", "qd_convrot_w4a4_linear_fp6",
-    "qd_quantize_and_rotate_rowwise_fp6",
+    "qd_quantize_and_rotate_rowwise_fp6", "qd_set_gemm_tiles", "qd_int8_gemm_tiles",
 )
 
 
@@ -91,6 +93,10 @@ def lib():
         L.qd_dequantize_int8.restype = St
         L.qd_dequantize_int8.argtypes = [P, I64, I64, I64, P, I32, St, P, I64, P]
         L.qd_int8_gemm_i32.restype = St
+        L.qd_set_gemm_tiles.restype = St
+        L.qd_set_gemm_tiles.argtypes = [St]
+        L.qd_int8_gemm_tiles.restype = St
+        L.qd_int8_gemm_tiles.argtypes = [I64, I64, I64]
         L.qd_int8_gemm_i32.argtypes = [P, I64, I64, I64, P, I64, I64, P, I64, P]
         L.qd_pack_int4.restype = St
         L.qd_pack_int4.argtypes = [P, I64, I64, I64, P, I64, P]
@@ -330,6 +336,19 @@ def int8_gemm_i32(aq, wq, out=None):
     _check(lib().qd_int8_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wq), N, wq.stride(0), _ptr(out),
                                   out.stride(0), _stream(dev)))
     return out
+
+
+def set_gemm_tiles(tiles: int) -> None:
+    """Output tile of the INT8-weight GEMM kernels for every later launch in
+    the process: GEMM_TILES_AUTO (chosen by shape, the default),
+    GEMM_TILES_256x256 or GEMM_TILES_256x384.  Results are identical."""
+    _check(lib().qd_set_gemm_tiles(int(tiles)))
+
+
+def int8_gemm_tiles(M: int, N: int, K: int) -> int:
+    """GEMM_TILES_256x256 or GEMM_TILES_256x384: the tile an INT8-weight GEMM
+    of this shape uses under the current setting."""
+    return int(lib().qd_int8_gemm_tiles(M, N, K))
 
 
 def workspace_size(M: int, K: int) -> int:

@@ -308,6 +308,21 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
     return hip_status(fn, qd::launch_gemm_i32(aq, lda, wq, ldw, acc, ldc, M, N, K, stream));
 }
 
+qd_status_t qd_set_gemm_tiles(qd_gemm_tiles_t tiles) {
+    const int t = (int)tiles;
+    if (t != QD_GEMM_TILES_AUTO && t != QD_GEMM_TILES_256x256 && t != QD_GEMM_TILES_256x384)
+        return fail(QD_EINVAL, "qd_set_gemm_tiles", "unknown tile setting %d", t);
+    static_assert((int)QD_GEMM_TILES_AUTO == qd::GEMM_TILES_AUTO && (int)QD_GEMM_TILES_256x256 == qd::GEMM_TILES_256x256 &&
+                      (int)QD_GEMM_TILES_256x384 == qd::GEMM_TILES_256x384,
+                  "tile settings");
+    qd::set_gemm_tile_policy(t);
+    return ok();
+}
+
+qd_gemm_tiles_t qd_int8_gemm_tiles(int64_t M, int64_t N, int64_t K) {
+    return qd::gemm_uses_wide_tiles(M, N, K) ? QD_GEMM_TILES_256x384 : QD_GEMM_TILES_256x256;
+}
+
 qd_status_t qd_pack_int4(const int8_t* q, int64_t R, int64_t K, int64_t ldq, uint8_t* packed,
                          int64_t ldp, hipStream_t stream) {
     const char* fn = "qd_pack_int4";

@@ -28,6 +28,12 @@ constexpr int kTensorwisePartials = 1024;
 hipError_t launch_quant_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                    int64_t ldq, float* scale, float* partial, hipStream_t stream);
 
+// Output tile of the INT8-weight GEMM kernels (K % 64 == 0): chosen by shape,
+// or fixed (process-wide) for tuning and tests.
+enum { GEMM_TILES_AUTO = 0, GEMM_TILES_256x256 = 1, GEMM_TILES_256x384 = 2 };
+void set_gemm_tile_policy(int policy);
+bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K);
+
 // y (BF16) = epilogue(aq . wq^T); bias may be null.  a_step / w_step: 1 for a
 // scale per row / per output channel, 0 for one scale for the whole operand.
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,

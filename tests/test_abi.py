@@ -263,3 +263,27 @@ def test_fp6_validation():
     assert st == qd.QD_EINVAL and "3K/4" in msg
     st, msg = _status(L.qd_fp6_gemm_i32, FAKE, 8, 256, 192, FAKE, 8, 192, FAKE, 10, STREAM)
     assert st == qd.QD_EUNSUPPORTED and "multiple of 4" in msg
+
+
+def test_gemm_tiles_setting():
+    L = qd.lib()
+    for bad in (-1, 3, 99):
+        assert L.qd_set_gemm_tiles(bad) == qd.QD_EINVAL
+        assert b"tile setting" in L.qd_last_error()
+    for good in (qd.GEMM_TILES_256x384, qd.GEMM_TILES_256x256, qd.GEMM_TILES_AUTO):
+        assert L.qd_set_gemm_tiles(good) == qd.QD_OK
+    with pytest.raises(qd.QDiffError):
+        qd.set_gemm_tiles(7)
+    qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
+
+
+def test_gemm_tiles_choice():
+    """The shape rule: rounds of 256 workgroups, a wide round costing 1.41x."""
+    qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
+    assert qd.int8_gemm_tiles(32700, 16128, 5376) == qd.GEMM_TILES_256x384   # 32 vs 21 rounds
+    assert qd.int8_gemm_tiles(14850, 28672, 7168) == qd.GEMM_TILES_256x384   # 26 vs 18
+    assert qd.int8_gemm_tiles(1000, 1000, 320) == qd.GEMM_TILES_256x256      # one round either way
+    assert qd.int8_gemm_tiles(32700, 16128, 5392) == qd.GEMM_TILES_256x256   # K % 64 != 0: general kernel
+    qd.set_gemm_tiles(qd.GEMM_TILES_256x384)
+    assert qd.int8_gemm_tiles(1000, 1000, 320) == qd.GEMM_TILES_256x384
+    qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)

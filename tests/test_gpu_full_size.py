@@ -70,7 +70,13 @@ def test_full_size_workload(O, cid):
     n = assert_bf16_within_1ulp(yg, yo, f"workload {cid}")
     say(f"  {n} of {yo.size} sampled outputs not bit-identical")
 
-    say("  int32 accumulators at the sampled points")
     aq = ws[: M * K].view(M, K).view(torch.int8)
-    acc = qd.int8_gemm_i32(aq, wq)
-    assert np.array_equal(host(acc[ri, ci]), acco)
+    for tiles in (qd.GEMM_TILES_256x256, qd.GEMM_TILES_256x384):
+        say(f"  int32 accumulators at the sampled points, tile setting {tiles}")
+        qd.set_gemm_tiles(tiles)
+        try:
+            acc = qd.int8_gemm_i32(aq, wq)
+        finally:
+            qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
+        assert np.array_equal(host(acc[ri, ci]), acco)
+        del acc

@@ -128,13 +128,22 @@ def test_quantize_strided_rows(qd, O):
 
 # ---------------------------------------------------------------------- GEMM
 
-GEMM_SHAPES = [(1, 1, 16), (256, 256, 64), (257, 255, 80), (300, 520, 512), (513, 1000, 5376),
-               (64, 4100, 1024), (1024, 1024, 7168)]
+GEMM_SHAPES = [(1, 1, 16), (1, 1, 64), (256, 256, 64), (257, 255, 80), (70, 130, 128), (300, 520, 512),
+               (513, 1000, 5376), (64, 4100, 1024), (1024, 1024, 7168)]
+
+
+@pytest.fixture(params=[1, 2], ids=["tiles256x256", "tiles256x384"])
+def tiles(request, qd):
+    """Both INT8 GEMM output tiles on every shape (K % 64 == 0; the general
+    kernel otherwise)."""
+    qd.set_gemm_tiles(request.param)
+    yield request.param
+    qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
-def test_gemm_i32_exact(qd, O, M, N, K):
-    say(f"gemm i32 M={M} N={N} K={K}")
+def test_gemm_i32_exact(qd, O, tiles, M, N, K):
+    say(f"gemm i32 M={M} N={N} K={K} tiles={tiles}")
     g = np.random.Generator(np.random.PCG64(M * 7 + N * 3 + K))
     a = g.integers(-128, 128, (M, K), dtype=np.int64).astype(np.int8)
     w = g.integers(-128, 128, (N, K), dtype=np.int64).astype(np.int8)
@@ -142,8 +151,8 @@ def test_gemm_i32_exact(qd, O, M, N, K):
     assert np.array_equal(host(acc), O.gemm_i32(a, w))
 
 
-def test_gemm_i32_extremes(qd, O):
-    say("gemm i32 extremes")
+def test_gemm_i32_extremes(qd, O, tiles):
+    say(f"gemm i32 extremes tiles={tiles}")
     K = 5376
     a = np.full((300, K), 127, np.int8)
     a[1::2] = -127
@@ -155,8 +164,8 @@ def test_gemm_i32_extremes(qd, O):
 
 @pytest.mark.parametrize("M,N,K,with_bias", [(256, 512, 512, True), (257, 264, 5376, True),
                                               (77, 1000, 768, False), (1, 8, 16, True)])
-def test_scaled_mm_bf16(qd, O, M, N, K, with_bias):
-    say(f"scaled_mm M={M} N={N} K={K} bias={with_bias}")
+def test_scaled_mm_bf16(qd, O, tiles, M, N, K, with_bias):
+    say(f"scaled_mm M={M} N={N} K={K} bias={with_bias} tiles={tiles}")
     import torch
     g = np.random.Generator(np.random.PCG64(M + N + K))
     a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
@@ -194,8 +203,8 @@ def test_int8_linear_tiny_config(qd, O):
 
 
 @pytest.mark.parametrize("M", [1, 2, 255, 257, 511])
-def test_int8_linear_ragged_rows(qd, O, M):
-    say(f"int8_linear ragged M={M}")
+def test_int8_linear_ragged_rows(qd, O, tiles, M):
+    say(f"int8_linear ragged M={M} tiles={tiles}")
     from synth import make_bias, make_w, workload
     w = workload(1)
     W, b = make_w(w), make_bias(w)

@@ -101,8 +101,10 @@ def test_tensorwise_strided_and_reused_workspace(qd, O):
 
 @pytest.mark.parametrize("a_tensor,w_tensor", [(True, True), (True, False), (False, True), (False, False)])
 @pytest.mark.parametrize("M,N,K", [(257, 1000, 5376), (70, 264, 528)])
-def test_scaled_mm_ex(qd, O, a_tensor, w_tensor, M, N, K):
-    say(f"scaled_mm_ex M={M} N={N} K={K} a_tensor={a_tensor} w_tensor={w_tensor}")
+@pytest.mark.parametrize("tiles", [1, 2])
+def test_scaled_mm_ex(qd, O, a_tensor, w_tensor, M, N, K, tiles):
+    say(f"scaled_mm_ex M={M} N={N} K={K} a_tensor={a_tensor} w_tensor={w_tensor} tiles={tiles}")
+    qd.set_gemm_tiles(tiles)
     g = np.random.Generator(np.random.PCG64(M * 3 + N + K + 2 * a_tensor + w_tensor))
     a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
     w = g.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
@@ -111,6 +113,7 @@ def test_scaled_mm_ex(qd, O, a_tensor, w_tensor, M, N, K):
     from synth import random_bf16
     b = random_bf16(N, seed=K + 1, scale=0.1)
     y = qd.int8_scaled_mm_ex(to_dev(a), to_dev(sx), to_dev(w), to_dev(sw), to_dev_bf16(b))
+    qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
     yo = O.epilogue(O.gemm_i32(a, w), np.broadcast_to(sx, (M,)), np.broadcast_to(sw, (N,)), b)
     n = assert_bf16_within_1ulp(bf16_bits(y), yo, "scaled_mm_ex")
     say(f"  {n} of {yo.size} outputs differ from the oracle (allowed: 1 ulp)")
