@@ -64,4 +64,41 @@ __device__ __forceinline__ float input_act(float x) {
     return IN16 == 1 ? round_to_grid<7, -126>(a) : round_to_grid<10, -14>(a);
 }
 
+// BF16 inputs of the smooth activations (GELU tanh / erf, SiLU): a BF16
+// input has 65536 values, and act(x) rounded to BF16 is x itself for
+// x >= 2^8, -0 for x <= -2^8, and x/2 rounded for |x| < 2^-12 (act(x) =
+// x/2 + c x^2 + ..., c > 0, and the positive term is far below half an ulp,
+// so only a tie moves the result: it goes up).  The 5120 inputs in between,
+// 2^-12 <= |x| < 2^8, take a table built by input_act above (same values).
+constexpr int kLutEmin = 115;                 // biased BF16 exponent of 2^-12
+constexpr int kLutExps = 20;                  // exponents of 2^-12 .. 2^7
+constexpr int kLutHalf = kLutExps * 128;      // entries per sign
+constexpr int kLutN = 2 * kLutHalf;           // 5120
+constexpr int kLutBytes = kLutN * 2;          // 10 KB
+template <int ACT, int IN16>
+struct UsesLut {
+    static constexpr bool value = IN16 == 1 && (ACT == ACT_GELU_TANH || ACT == ACT_GELU_ERF || ACT == ACT_SILU);
+};
+
+// BF16 bits of the input behind table entry i (sign-major, then exponent, then mantissa).
+__device__ __forceinline__ uint32_t lut_input_bits(int i) {
+    const uint32_t sg = (uint32_t)(i >= kLutHalf);
+    return (sg << 15) | (uint32_t)((kLutEmin << 7) + i - (int)sg * kLutHalf);
+}
+
+// act(x) as BF16 bits for BF16 bits b.
+__device__ __forceinline__ uint32_t act_bf16_lut(uint32_t b, const uint16_t* lut) {
+    const uint32_t e = (b >> 7) & 0xFFu;
+    const uint32_t sign = b & 0x8000u;
+    if (e - (uint32_t)kLutEmin < (uint32_t)kLutExps)
+        return lut[(b & 0x7FFFu) - (uint32_t)(kLutEmin << 7) + (sign >> 15) * (uint32_t)kLutHalf];
+    if (e >= (uint32_t)(kLutEmin + kLutExps)) {
+        if (e == 0xFFu && (b & 0x7Fu)) return b | 0x40u;    // NaN stays a (quiet) NaN
+        return sign ? 0x8000u : b;                          // x (or +inf); -0 (also for -inf)
+    }
+    if (e >= 2u) return b - 0x80u;                          // x/2 is a normal BF16 value
+    const uint32_t full = e ? (0x80u | (b & 0x7Fu)) : (b & 0x7Fu);   // |x| in units of 2^-133
+    return sign | ((full >> 1) + (full & 1u & ((sign >> 15) ^ 1u)));
+}
+
 }  // namespace qd

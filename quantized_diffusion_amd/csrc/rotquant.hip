@@ -63,9 +63,10 @@ template <class In> struct In16 { static constexpr int value = 0; };
 template <> struct In16<InBF16> { static constexpr int value = 1; };
 template <> struct In16<InF16> { static constexpr int value = 2; };
 
-// act() on the eight 16-bit values of a chunk, results in the same type.
+// act() on the eight 16-bit values of a chunk, results in the same type
+// (BF16 with a smooth activation: the table lut; otherwise FP64 evaluation).
 template <int ACT, int IN16>
-__device__ __forceinline__ u32x4 act_chunk(u32x4 d) {
+__device__ __forceinline__ u32x4 act_chunk(u32x4 d, const uint16_t* lut) {
     if (IN16 == 0) return d;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -73,9 +74,14 @@ __device__ __forceinline__ u32x4 act_chunk(u32x4 d) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t b = (d[w] >> (16 * h)) & 0xFFFFu;
-            const float f = IN16 == 1 ? bits_f(b << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)b);
-            const float a = input_act<ACT, IN16>(f);
-            const uint32_t r = IN16 == 1 ? f_bits(a) >> 16 : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a);
+            uint32_t r;
+            if (UsesLut<ACT, IN16>::value) {
+                r = act_bf16_lut(b, lut);   // chunks with an input outside the table
+            } else {
+                const float f = IN16 == 1 ? bits_f(b << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+                const float a = input_act<ACT, IN16>(f);
+                r = IN16 == 1 ? f_bits(a) >> 16 : (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a);
+            }
             out |= r << (16 * h);
         }
         d[w] = out;
@@ -83,9 +89,61 @@ __device__ __forceinline__ u32x4 act_chunk(u32x4 d) {
     return d;
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// act() on a BF16 chunk through the table: indices two at a time in 16-bit
+// lanes (entry = |x| bits - 2^-12's bits, + kLutHalf for negative x), one
+// range test for the chunk, the general path only for a chunk with an input
+// outside the table.
+template <int ACT>
+__device__ __forceinline__ u32x4 act_chunk_lut(u32x4 d, const uint16_t* lut) {
+    u16x2 t[4], idx[4];
+    const u16x2 base = {(unsigned short)(kLutEmin << 7), (unsigned short)(kLutEmin << 7)};
+    const u16x2 half = {(unsigned short)kLutHalf, (unsigned short)kLutHalf};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        t[w] = __builtin_bit_cast(u16x2, d[w] & 0x7FFF7FFFu) - base;
+        const u16x2 sg = __builtin_bit_cast(u16x2, (d[w] >> 15) & 0x00010001u);
+        idx[w] = sg * half + t[w];
+    }
+    const u16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(t[0], t[1]),
+                                               __builtin_elementwise_max(t[2], t[3]));
+    if (__builtin_expect(mx[0] < (unsigned short)kLutHalf && mx[1] < (unsigned short)kLutHalf, 1)) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) d[w] = (uint32_t)lut[idx[w][0]] | ((uint32_t)lut[idx[w][1]] << 16);
+        return d;
+    }
+    return act_chunk<ACT, 1>(d, lut);
+}
+
+// Tables of the smooth activations for BF16 inputs (entry i: input
+// lut_input_bits(i)), rebuilt by act_lut_kernel on the stream of every
+// launch that reads them.  The values never change, so launches on other
+// streams that rebuild a table concurrently only rewrite the same bits.
+__device__ uint16_t g_act_lut[3][kLutN];
+
+template <int ACT>
+__global__ __launch_bounds__(256) void act_lut_kernel() {
+    const int i = blockIdx.x * 256 + (int)threadIdx.x;
+    if (i < kLutN) {
+        const float x = bits_f(lut_input_bits(i) << 16);
+        g_act_lut[ACT - 1][i] = (uint16_t)(f_bits(input_act<ACT, 1>(x)) >> 16);
+    }
+}
+
+template <int ACT, int IN16>
+hipError_t build_lut(hipStream_t stream) {
+    if (!UsesLut<ACT, IN16>::value) return hipSuccess;
+    act_lut_kernel<UsesLut<ACT, IN16>::value ? ACT : ACT_SILU><<<dim3((kLutN + 255) / 256), dim3(256), 0, stream>>>();
+    return hipGetLastError();
+}
+
 // Largest workgroup: 1024 threads (4 waves per SIMD, 128 VGPRs); 512 with an
 // FP64 activation, whose temporaries need more registers.
-template <int ACT> struct kMaxThreads { static constexpr int value = (ACT == 0 || ACT == 4) ? 1024 : 512; };
+template <int ACT, int IN16>
+struct kMaxThreads {
+    static constexpr int value = (ACT == 0 || ACT == 4 || UsesLut<ACT, IN16>::value) ? 1024 : 512;
+};
 
 constexpr int kStageStride = 288;                 // bytes per block image in LDS (256 + 32: spreads banks)
 constexpr int kStageWave = 16 * kStageStride;     // per wave: 16 quads
@@ -128,7 +186,7 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
 // 48 bits, three 2-byte pieces placed in the block's 192-byte image at their
 // head / tail positions.
 template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false>
-__global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const uint8_t* __restrict__ x,
+__global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void rotquant_kernel(const uint8_t* __restrict__ x,
                                                         int64_t ldx_bytes, int M, int K, int nb,
                                                         int R, int8_t* __restrict__ q,
                                                         int64_t ldq, float* __restrict__ scale) {
@@ -137,7 +195,19 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
     constexpr int NV = NI * E;           // 64 values per lane
     constexpr int ESZ = 16 / E;          // bytes per input element
     __shared__ uint32_t row_amax[256];
-    extern __shared__ __attribute__((aligned(16))) uint8_t stage[];   // kStageWave per wave (rotated path)
+    // dynamic LDS: [activation table (LUT) | kStageWave per wave (rotated path)]
+    constexpr bool LUT = UsesLut<ACT, In16<In>::value>::value;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    uint8_t* const stage = lds_dyn + (LUT ? kLutBytes : 0);
+    const uint16_t* lut = reinterpret_cast<const uint16_t*>(lds_dyn);
+    auto load_lut = [&]() {
+        if (LUT) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(g_act_lut[(ACT > 0 && ACT < 4) ? ACT - 1 : 0]);
+            for (int c = threadIdx.x; c < kLutBytes / 16; c += blockDim.x)
+                reinterpret_cast<u32x4*>(lds_dyn)[c] = src[c];
+            __syncthreads();
+        }
+    };
 
     const int tid = threadIdx.x;
     const int quad = tid >> 2;
@@ -162,10 +232,11 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
 #pragma unroll
         for (int i = 0; i < NI; ++i) d[i] = *reinterpret_cast<const u32x4*>(src + (i * 4 + ql) * 16);
         if (ACT != ACT_NONE) {
+            load_lut();
             // on the raw 16-bit words, before widening: fewer live registers
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                d[i] = act_chunk<ACT, In16<In>::value>(d[i]);
+                d[i] = LUT ? act_chunk_lut<ACT>(d[i], lut) : act_chunk<ACT, In16<In>::value>(d[i], lut);
                 __builtin_amdgcn_sched_barrier(0);   // one chunk at a time: bounded FP64 temporaries
             }
         }
@@ -174,6 +245,7 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
     } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) v[j] = 0.0f;
+        if (ACT != ACT_NONE) load_lut();
         if (active) {
             const uint8_t* src = x + (int64_t)row * ldx_bytes + (int64_t)blk * 256 * ESZ;
 #pragma unroll
@@ -181,7 +253,8 @@ __global__ __launch_bounds__(kMaxThreads<ACT>::value) void rotquant_kernel(const
                 const int c = i * 4 + ql;
                 if (blk * 256 + c * E < K) {
                     u32x4 d = *reinterpret_cast<const u32x4*>(src + c * 16);
-                    if (ACT != ACT_NONE) d = act_chunk<ACT, In16<In>::value>(d);
+                    if (ACT != ACT_NONE)
+                        d = LUT ? act_chunk_lut<ACT>(d, lut) : act_chunk<ACT, In16<In>::value>(d, lut);
                     widen(In{}, d, &v[i * E]);
                 }
             }
@@ -370,7 +443,10 @@ hipError_t launch_staged(const void* x, int64_t M, int64_t K, int64_t ldx, int8_
     constexpr int ESZ = 16 / In::E;
     const int nb = (int)((K + 255) / 256);
     const int64_t grid = (M + R - 1) / R;
-    const size_t lds = F6 ? (size_t)(threads / 64) * kF6Wave : STAGE ? (size_t)(threads / 64) * kStageWave : 0;
+    const size_t lds = (F6 ? (size_t)(threads / 64) * kF6Wave : STAGE ? (size_t)(threads / 64) * kStageWave : 0) +
+                       (UsesLut<ACT, In16<In>::value>::value ? (size_t)kLutBytes : 0);
+    const hipError_t e = build_lut<ACT, In16<In>::value>(stream);
+    if (e != hipSuccess) return e;
     rotquant_kernel<In, ROT, QMAX, STAGE, ACT, F6><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
         static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
     return hipGetLastError();
@@ -384,7 +460,7 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     // leaves the fewest idle lanes in whole waves, preferring ~256 threads.
     int R = 1, best_threads = 0;
     double best_waste = 2.0;
-    constexpr int MAXT = kMaxThreads<ACT>::value;
+    constexpr int MAXT = kMaxThreads<ACT, In16<In>::value>::value;
     const int r0 = nb >= 64 ? 1 : 64 / nb;
     for (int r = r0; r <= 2 * r0 && 4 * r * nb <= MAXT; ++r) {
         const int th = (4 * r * nb + 63) / 64 * 64;
@@ -438,14 +514,20 @@ hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int6
 
 namespace {
 
+// The activation alone, by the quantizer's code path (table or FP64).
 template <int ACT, int IN16>
 __global__ __launch_bounds__(256) void act_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                   uint16_t* __restrict__ out) {
+    const uint16_t* lut = g_act_lut[(ACT > 0 && ACT < 4) ? ACT - 1 : 0];
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const uint16_t b = x[i];
+        const uint32_t b = x[i];
+        if (UsesLut<ACT, IN16>::value) {
+            out[i] = (uint16_t)act_bf16_lut(b, lut);
+            continue;
+        }
         float f;
-        if (IN16 == 1) f = bits_f((uint32_t)b << 16);
-        else f = (float)__builtin_bit_cast(_Float16, b);
+        if (IN16 == 1) f = bits_f(b << 16);
+        else f = (float)__builtin_bit_cast(_Float16, (uint16_t)b);
         const float a = input_act<ACT, IN16>(f);
         // a is exactly representable in the 16-bit type
         out[i] = IN16 == 1 ? (uint16_t)(f_bits(a) >> 16) : __builtin_bit_cast(uint16_t, (_Float16)a);
@@ -457,6 +539,14 @@ hipError_t launch_act16(const void* x, int64_t n, int act, void* out, hipStream_
     const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
     const uint16_t* xi = static_cast<const uint16_t*>(x);
     uint16_t* o = static_cast<uint16_t*>(out);
+    hipError_t e = hipSuccess;
+    switch (act) {
+        case ACT_GELU_TANH: e = build_lut<ACT_GELU_TANH, IN16>(stream); break;
+        case ACT_GELU_ERF: e = build_lut<ACT_GELU_ERF, IN16>(stream); break;
+        case ACT_SILU: e = build_lut<ACT_SILU, IN16>(stream); break;
+        default: break;
+    }
+    if (e != hipSuccess) return e;
     switch (act) {
         case ACT_GELU_TANH: act_kernel<ACT_GELU_TANH, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
         case ACT_GELU_ERF: act_kernel<ACT_GELU_ERF, IN16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(xi, n, o); break;
