@@ -1,4 +1,4 @@
-"""Oracle for the rotated, dynamically quantized INT8/INT4 linear layer.
+"""Oracle for the rotated, dynamically quantized INT8/INT4 linear layer (and INT8 attention).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The GPU library
@@ -54,6 +54,8 @@ def _p(a):
 
 def _bind(L):
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.oracle_attention_i8.restype = None
+    L.oracle_attention_i8.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
     L.oracle_bf16_rne.restype = ctypes.c_uint16
     L.oracle_bf16_rne.argtypes = [ctypes.c_float]
     L.oracle_hadamard256.argtypes = [P]
@@ -243,6 +245,36 @@ class Oracle:
         self.L.oracle_linear_points(_p(aq), K, _p(sx), _p(aq_rows), _p(wq), _p(sw), _p(b),
                                     _p(cols), n, _p(y), _p(acc))
         return y, acc
+
+    def attention_codes(self, qc, sq, kc, sk, vc, sv, scale=None) -> np.ndarray:
+        """INT8 attention on per-token codes: qc [BH, Lq, D], kc / vc [BH, Lk, D],
+        scales [BH, L]; float64 [BH, Lq, D] (the reading in qdiff_oracle.c)."""
+        qc, kc, vc = (np.ascontiguousarray(a, dtype=np.int8) for a in (qc, kc, vc))
+        sq, sk, sv = (np.ascontiguousarray(a, dtype=np.float32) for a in (sq, sk, sv))
+        BH, Lq, D = qc.shape
+        Lk = kc.shape[1]
+        if kc.shape != (BH, Lk, D) or vc.shape != (BH, Lk, D) or sq.shape != (BH, Lq) or sk.shape != (BH, Lk) \
+                or sv.shape != (BH, Lk):
+            raise ValueError("attention shapes disagree")
+        out = np.empty((BH, Lq, D), np.float64)
+        self.L.oracle_attention_i8(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), BH, Lq, Lk, D,
+                                   float(1.0 / np.sqrt(D) if scale is None else scale), _p(out))
+        return out
+
+    def quantize_tokens(self, x, dtype: str = "bf16"):
+        """Per-token INT8 codes and scales of x [BH, L, D] (the unrotated row rule)."""
+        x = np.asarray(x)
+        BH, L, D = x.shape
+        q, s = self.quantize_rowwise(x.reshape(BH * L, D), dtype, 0)
+        return q.reshape(BH, L, D), s.reshape(BH, L)
+
+    def attention(self, q, k, v, dtype: str = "bf16", scale=None) -> np.ndarray:
+        """int8_attention of q [BH, Lq, D], k / v [BH, Lk, D] (16-bit bits or float32):
+        per-token quantization of all three, then attention_codes."""
+        qc, sq = self.quantize_tokens(q, dtype)
+        kc, sk = self.quantize_tokens(k, dtype)
+        vc, sv = self.quantize_tokens(v, dtype)
+        return self.attention_codes(qc, sq, kc, sk, vc, sv, scale)
 
     def dequantize(self, q, scale, per_row: bool = True, out: str = "f32") -> np.ndarray:
         q = np.ascontiguousarray(q, dtype=np.int8)

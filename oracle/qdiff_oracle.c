@@ -47,6 +47,16 @@
  *    the layer then proceeds on those values.  GELU (tanh form
  *    with 0.044715), GELU (erf form), SiLU and ReLU, evaluated in long
  *    double.
+ *  - INT8 attention (int8_attention: comfy-kitchen's INT8-quantized
+ *    attention kernel behind ComfyUI's --use-ck-attention, per the
+ *    ai-jitan-hub article on ComfyUI v0.32.0; the article gives no formula,
+ *    only that q, k and v are quantized to INT8).  Reading: q, k and v are
+ *    each quantized per token (one row of D values per head) by the row rule
+ *    above; scores S[i][j] = acc(i, j) * sq[i] * sk[j] * scale with the exact
+ *    integer dot product acc of the codes and scale = 1/sqrt(D) unless given;
+ *    softmax over j; out[i] = sum_j p[i][j] * (sv[j] * v[j]) / sum_j p[i][j].
+ *    Evaluated in double precision (the GPU result is compared within a
+ *    bound derived from its own rounding steps).
  */
 #include <math.h>
 #include <stdint.h>
@@ -475,4 +485,38 @@ int oracle_num_threads(void) {
 /* Array form of oracle_bf16_rne. */
 void oracle_bf16_rne_array(const float* f, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; i++) out[i] = oracle_bf16_rne(f[i]);
+}
+
+/* INT8 attention on codes (reading in the header).  qc [BH*Lq, D], kc and vc
+ * [BH*Lk, D] INT8 codes with one FP32 scale per row; out [BH*Lq, D] double. */
+void oracle_attention_i8(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                         const int8_t* vc, const float* sv, int64_t BH, int64_t Lq, int64_t Lk,
+                         int64_t D, double scale, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t qi = 0; qi < BH * Lq; qi++) {
+        const int64_t bh = qi / Lq;
+        double* sc = (double*)malloc((size_t)Lk * sizeof(double));
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < Lk; j++) {
+            const int64_t kr = bh * Lk + j;
+            int64_t acc = 0;
+            for (int64_t d = 0; d < D; d++) acc += (int64_t)qc[qi * D + d] * (int64_t)kc[kr * D + d];
+            sc[j] = (double)acc * (double)sq[qi] * (double)sk[kr] * scale;
+            if (sc[j] > mx) mx = sc[j];
+        }
+        double den = 0.0;
+        for (int64_t j = 0; j < Lk; j++) {
+            sc[j] = exp(sc[j] - mx);
+            den += sc[j];
+        }
+        for (int64_t d = 0; d < D; d++) {
+            double num = 0.0;
+            for (int64_t j = 0; j < Lk; j++) {
+                const int64_t vr = bh * Lk + j;
+                num += sc[j] * ((double)sv[vr] * (double)vc[vr * D + d]);
+            }
+            out[qi * D + d] = num / den;
+        }
+        free(sc);
+    }
 }

@@ -551,6 +551,70 @@ def slowcheck_act_all_inputs(O):
             _check_act(O, act, dtype, _finite_patterns(dtype))
 
 
+# ------------------------------------------------------------ INT8 attention
+
+def _lossless_rows(g, shape, exp2):
+    """float32 rows that per-token quantization reproduces exactly: integers in
+    [-127, 127] with a +-127 in every row, times 2^exp2 (s = 2^exp2 exactly)."""
+    c = g.integers(-127, 128, shape).astype(np.float64)
+    c[..., 0] = np.where(g.integers(0, 2, shape[:-1]) == 1, 127.0, -127.0)
+    return (c * 2.0 ** exp2).astype(np.float32)
+
+
+def check_attention_single_key(O):
+    """One key: the softmax is 1, the output is that key's dequantized value row."""
+    g = np.random.default_rng(31)
+    q = g.standard_normal((3, 5, 64)).astype(np.float32)
+    k = g.standard_normal((3, 1, 64)).astype(np.float32)
+    v = (g.standard_normal((3, 1, 64)) * 3).astype(np.float32)
+    out = O.attention(q, k, v, "f32")
+    vc, sv = O.quantize_tokens(v, "f32")
+    want = sv[:, :, None].astype(np.float64) * vc.astype(np.float64)
+    assert np.array_equal(out, np.broadcast_to(want, out.shape))
+
+
+def check_attention_zero_queries(O):
+    """All-zero queries: every score is 0, the output is the mean of the
+    dequantized value rows (per head)."""
+    g = np.random.default_rng(32)
+    q = np.zeros((2, 4, 128), np.float32)
+    k = g.standard_normal((2, 37, 128)).astype(np.float32)
+    v = g.standard_normal((2, 37, 128)).astype(np.float32)
+    out = O.attention(q, k, v, "f32")
+    vc, sv = O.quantize_tokens(v, "f32")
+    want = (sv[:, :, None].astype(np.float64) * vc).mean(axis=1)
+    assert np.allclose(out, want[:, None, :], rtol=1e-13, atol=1e-15)
+
+
+def check_attention_against_sdpa(O):
+    """Inputs that quantize losslessly: the oracle equals the float64 scaled
+    dot-product attention of torch on the same values (an independent
+    implementation), several heads, both default and explicit scales."""
+    import torch
+    g = np.random.default_rng(33)
+    for BH, Lq, Lk, D, scale in ((2, 9, 50, 64, None), (3, 4, 17, 128, 0.3)):
+        q = _lossless_rows(g, (BH, Lq, D), -9)
+        k = _lossless_rows(g, (BH, Lk, D), -8)
+        v = _lossless_rows(g, (BH, Lk, D), -5)
+        out = O.attention(q, k, v, "f32", scale)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q.astype(np.float64)), torch.from_numpy(k.astype(np.float64)),
+            torch.from_numpy(v.astype(np.float64)), scale=scale).numpy()
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-14), (BH, Lq, Lk, D, np.abs(out - ref).max())
+
+
+def check_attention_key_permutation(O):
+    """Permuting the keys together with their values leaves the output unchanged."""
+    g = np.random.default_rng(34)
+    q = g.standard_normal((1, 6, 64)).astype(np.float32) * 4
+    k = g.standard_normal((1, 40, 64)).astype(np.float32)
+    v = g.standard_normal((1, 40, 64)).astype(np.float32)
+    p = g.permutation(40)
+    a = O.attention(q, k, v, "f32")
+    b = O.attention(q, k[:, p], v[:, p], "f32")
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]
 # Slow exhaustive checks run after the quick ones.
 CHECKS += [v for k, v in sorted(globals().items()) if k.startswith("slowcheck_")]

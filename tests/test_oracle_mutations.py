@@ -33,6 +33,12 @@ MUTATIONS = {
     "fp6_tail_swap_on_bit4_only": ("int first = (int)(((r >> 3) ^ (r >> 4)) & 1);", "int first = (int)((r >> 4) & 1);"),
     "fp6_exponent_bias_zero": ("ldexpf(1.0f + (float)m / 8.0f, (int)e - 1)", "ldexpf(1.0f + (float)m / 8.0f, (int)e)"),
     "relu_passes_negatives": ("case ORACLE_ACT_RELU: return x > 0.0L ? x : 0.0L;", "case ORACLE_ACT_RELU: return x;"),
+    "attention_scale_missing": ("(double)sk[kr] * scale;", "(double)sk[kr];"),
+    "attention_value_scale_dropped": ("num += sc[j] * ((double)sv[vr] * (double)vc[vr * D + d]);",
+                                      "num += sc[j] * (double)vc[vr * D + d];"),
+    "attention_not_normalised": ("out[qi * D + d] = num / den;", "out[qi * D + d] = num;"),
+    "attention_keys_of_head0": ("const int64_t kr = bh * Lk + j;", "const int64_t kr = j;"),
+    "attention_key_scale_of_query": ("(double)sq[qi] * (double)sk[kr]", "(double)sq[qi] * (double)sq[qi]"),
 }
 
 
