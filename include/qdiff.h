@@ -226,6 +226,37 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
                              int64_t ldc, hipStream_t stream);
 
 /*
+ * INT8 attention (int8_attention: comfy-kitchen's INT8-quantized attention
+ * behind ComfyUI's --use-ck-attention, per the ai-jitan-hub article on
+ * ComfyUI v0.32.0, which names the operation and says q, k and v are
+ * quantized to INT8, without a formula).  This library's reading:
+ *   q, k, v are quantized per token (each row of D values, per batch and
+ *   head) exactly as qd_quantize_int8_rowwise does: s = amax / 127,
+ *   codes clamp(rne(fl(x / s)), -127, 127);
+ *   S[i][j] = (sum_d qc[i][d] * kc[j][d]) * sq[i] * sk[j] * scale (the
+ *   integer sum exact, the rest FP32), softmax over j,
+ *   out[i][d] = sum_j p[i][j] * sv[j] * vc[j][d] / sum_j p[i][j], BF16.
+ * Layout: q [BH, Lq, D], k and v [BH, Lk, D] (BH = batch x heads), rows of
+ * D contiguous, in x_dtype (QD_F32, QD_BF16 or QD_F16); out [BH, Lq, D]
+ * BF16, contiguous.  scale <= 0 selects 1/sqrt(D).
+ * Accuracy: the probabilities times the value scale enter the value product
+ * rounded to BF16 and the output is rounded to BF16, so each output differs
+ * from the exact value of the reading (float64 softmax of the same codes) by
+ * at most about 2^-9 * max_j |sv[j] * vc[j][d]| + 2^-8 * |out| (the test
+ * bound is twice that).
+ * workspace: qd_int8_attention_workspace_size(BH, Lq, Lk, D) bytes, 256-byte
+ * aligned; on return it holds, in order and each part 256-byte aligned, the
+ * q, k, v codes ([BH*L, D] INT8) and then their FP32 row scales.
+ * Requires D == 64 or D == 128, BH >= 1, Lk >= 1 (Lq == 0 does nothing),
+ * BH <= 65535, BH * max(Lq, Lk) <= 2^31 - 1, all pointers 16-byte aligned.
+ * Enqueues four kernels (three quantizer launches and the attention).
+ */
+size_t qd_int8_attention_workspace_size(int64_t BH, int64_t Lq, int64_t Lk, int64_t D);
+qd_status_t qd_int8_attention(const void* q, const void* k, const void* v, qd_dtype_t x_dtype, int64_t BH,
+                              int64_t Lq, int64_t Lk, int64_t D, float scale, void* workspace,
+                              size_t workspace_bytes, void* out_bf16, hipStream_t stream);
+
+/*
  * Output tile of the INT8-weight GEMM kernels (K % 64 == 0) behind
  * qd_int8_linear, qd_int8_linear_act, qd_int8_scaled_mm, qd_int8_scaled_mm_ex
  * and qd_int8_gemm_i32.  QD_GEMM_TILES_AUTO (the default) chooses 256 x 256

@@ -35,7 +35,7 @@ __all__ = [
     "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU", "pack_fp6", "fp6_scaled_mm",
     "fp6_gemm_i32", "w4a4_fp6_workspace_size", "convrot_w4a4_linear_fp6", "prepare_weights_w4a4_fp6",
     "quantize_and_rotate_rowwise_fp6", "set_gemm_tiles", "int8_gemm_tiles", "GEMM_TILES_AUTO", "GEMM_TILES_256x256",
-    "GEMM_TILES_256x384",
+    "GEMM_TILES_256x384", "int8_attention", "attention_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -54,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act", "qd_pack_fp6", "qd_fp6_scaled_mm",
     "qd_fp6_gemm_i32", "qd_w4a4_fp6_workspace_size", "qd_convrot_w4a4_linear_fp6",
     "qd_quantize_and_rotate_rowwise_fp6", "qd_set_gemm_tiles", "qd_int8_gemm_tiles",
+    "qd_int8_attention_workspace_size", "qd_int8_attention",
 )
 
 
@@ -93,6 +94,10 @@ def lib():
         L.qd_dequantize_int8.restype = St
         L.qd_dequantize_int8.argtypes = [P, I64, I64, I64, P, I32, St, P, I64, P]
         L.qd_int8_gemm_i32.restype = St
+        L.qd_int8_attention_workspace_size.restype = SZ
+        L.qd_int8_attention_workspace_size.argtypes = [I64, I64, I64, I64]
+        L.qd_int8_attention.restype = St
+        L.qd_int8_attention.argtypes = [P, P, P, St, I64, I64, I64, I64, ctypes.c_float, P, SZ, P, P]
         L.qd_set_gemm_tiles.restype = St
         L.qd_set_gemm_tiles.argtypes = [St]
         L.qd_int8_gemm_tiles.restype = St
@@ -335,6 +340,37 @@ def int8_gemm_i32(aq, wq, out=None):
     _mat(out, "out")
     _check(lib().qd_int8_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wq), N, wq.stride(0), _ptr(out),
                                   out.stride(0), _stream(dev)))
+    return out
+
+
+def attention_workspace_size(BH: int, Lq: int, Lk: int, D: int) -> int:
+    return int(lib().qd_int8_attention_workspace_size(BH, Lq, Lk, D))
+
+
+def int8_attention(q, k, v, scale: float = 0.0, workspace=None, out=None):
+    """INT8 attention of q [BH, Lq, D], k / v [BH, Lk, D] (contiguous, same
+    dtype: float32, bfloat16 or float16; D = 64 or 128) -> BF16 [BH, Lq, D].
+    scale <= 0: 1/sqrt(D).  The workspace (optional) ends up holding the
+    per-token codes and scales (qdiff.h gives the layout)."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [BH, L, D]")
+    BH, Lq, D = q.shape
+    Lk = k.shape[1]
+    if k.shape != (BH, Lk, D) or v.shape != (BH, Lk, D):
+        raise ValueError("q, k, v shapes disagree")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    dev = _dev(q, k, v, out)
+    if workspace is None:
+        workspace = torch.empty(max(1, attention_workspace_size(BH, Lq, Lk, D)), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((BH, Lq, D), dtype=torch.bfloat16, device=dev)
+    _check(lib().qd_int8_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), BH, Lq, Lk, D, float(scale),
+                                   _ptr(workspace), workspace.numel(), _ptr(out), _stream(dev)))
     return out
 
 

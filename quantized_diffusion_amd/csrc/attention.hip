@@ -1,0 +1,256 @@
+// INT8 attention for gfx950 (CDNA4).
+//
+// int8_attention (comfy-kitchen's INT8-quantized attention behind ComfyUI's
+// --use-ck-attention; the ai-jitan-hub article on ComfyUI v0.32.0 says that
+// q, k and v are quantized to INT8 and that only the CUDA and HIP backends
+// implement it, and gives no formula).  This library's reading: q, k and v
+// are quantized per token (one row of D values per head) by the unrotated
+// row quantizer of the linear layer; scores are the exact INT32 dot products
+// of the codes scaled by sq[i] * sk[j] * scale; softmax over the keys; the
+// output row is sum_j p[i][j] * sv[j] * v[j] / sum_j p[i][j], stored as BF16.
+//
+// attn_i8_kernel: a workgroup of 4 waves takes 128 queries of one (batch,
+// head), each wave 32 queries, and walks the keys in blocks of 64 through
+// two LDS stages (flash-attention style: running maximum and sum, the
+// output accumulators rescaled when the maximum grows).
+//  * Scores are computed transposed, S^T = K Q^T, with
+//    v_mfma_i32_32x32x32_i8 (K from LDS as the "A" operand, the wave's Q
+//    codes in registers as "B"), so a lane holds 16 keys of ONE query: the
+//    row maximum and sum need one exchange between the two half-waves.
+//  * The probabilities p[i][j] * sv[j] (the key's value scale folded in) are
+//    rounded to BF16 in registers and are directly the "B" operand of
+//    v_mfma_f32_32x32x16_bf16 computing O^T = V^T P^T: the key order inside
+//    each 16-key step is the one the score layout leaves in the lanes, and
+//    the V^T operand is read in the same order from a transposed BF16 copy
+//    of the value codes in LDS (codes |v| <= 127 are exact in BF16).
+//  * Exponentials are base 2 with log2(e) folded into the score scale.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qd_device.h"
+#include "qd_launch.h"
+
+namespace qd {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int AQ = 128;              // queries per workgroup (4 waves x 32)
+constexpr int AK = 64;               // keys per block
+constexpr int VT_STRIDE = AK + 4;    // BF16 per row of the transposed value tile (136 bytes)
+constexpr int ATT_THREADS = 256;
+
+template <int D>
+struct AttnStage {
+    int8_t k[AK * D];                // key codes, 16-byte chunks of row r XOR-swizzled by r % (D / 16)
+    uint16_t vt[D * VT_STRIDE];      // value codes as BF16, transposed: vt[d][key]
+    float sk[AK];
+    float sv[AK];
+};
+
+template <int D>
+__global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __restrict__ qc,
+                                                              const float* __restrict__ sq,
+                                                              const int8_t* __restrict__ kc,
+                                                              const float* __restrict__ sk,
+                                                              const int8_t* __restrict__ vc,
+                                                              const float* __restrict__ sv,
+                                                              uint16_t* __restrict__ out, int Lq, int Lk,
+                                                              float c) {
+    constexpr int NS = D / 32;                   // 32-element steps along D (score MFMA K, output tiles)
+    constexpr int CPR = D / 16;                  // 16-byte chunks per key row
+    constexpr int KCH = AK * CPR / ATT_THREADS;  // key chunks staged per thread
+    constexpr int VCH = D / 4 / 16;              // value chunks staged per thread (a quarter of a row)
+    static_assert(KCH >= 1 && VCH >= 1, "head dim");
+    __shared__ AttnStage<D> st[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int fr = lane & 31;
+    const int h = lane >> 5;
+    const int64_t qbase = (int64_t)blockIdx.y * Lq;
+    const int64_t kbase = (int64_t)blockIdx.y * Lk;
+    const int q_row = blockIdx.x * AQ + wave * 32 + fr;   // this lane's query
+    const int qr = min(q_row, Lq - 1);
+
+    i32x4 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        qf[s] = *reinterpret_cast<const i32x4*>(qc + (qbase + qr) * D + 32 * s + 16 * h);
+    const float sqc = sq[qbase + qr] * c;
+
+    // staging of key block kb: registers first (loads in flight during the
+    // previous block's math), then LDS
+    u32x4 kreg[KCH], vreg[VCH];
+    float sreg = 0.0f;
+    auto gload = [&](int kb) {
+        const int k0 = kb * AK;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int ch = tid + ATT_THREADS * i;
+            const int key = min(k0 + ch / CPR, Lk - 1);
+            kreg[i] = *reinterpret_cast<const u32x4*>(kc + (kbase + key) * D + (ch % CPR) * 16);
+        }
+        const int vkey = min(k0 + (tid & (AK - 1)), Lk - 1);
+#pragma unroll
+        for (int i = 0; i < VCH; ++i)
+            vreg[i] = *reinterpret_cast<const u32x4*>(vc + (kbase + vkey) * D + (tid / AK) * (D / 4) + 16 * i);
+        if (tid < AK) sreg = sk[kbase + min(k0 + tid, Lk - 1)];
+        else if (tid < 2 * AK) sreg = sv[kbase + min(k0 + tid - AK, Lk - 1)];
+    };
+    auto sstore = [&](AttnStage<D>& S) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int ch = tid + ATT_THREADS * i;
+            const int row = ch / CPR;
+            *reinterpret_cast<u32x4*>(S.k + row * D + (((ch % CPR) ^ (row % CPR)) << 4)) = kreg[i];
+        }
+        const int key = tid & (AK - 1);
+        const int d0 = (tid / AK) * (D / 4);
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+#pragma unroll
+            for (int b = 0; b < 16; ++b) {
+                const int8_t code = (int8_t)((vreg[i][b >> 2] >> (8 * (b & 3))) & 0xFFu);
+                S.vt[(d0 + 16 * i + b) * VT_STRIDE + key] = (uint16_t)(f_bits((float)code) >> 16);
+            }
+        }
+        if (tid < AK) S.sk[tid] = sreg;
+        else if (tid < 2 * AK) S.sv[tid - AK] = sreg;
+    };
+
+    f32x16 o[NS];
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
+    float m_run = -__builtin_inff();
+    float l_run = 0.0f;
+
+    const int nkb = (Lk + AK - 1) / AK;
+    gload(0);
+    sstore(st[0]);
+    __syncthreads();
+    for (int kb = 0; kb < nkb; ++kb) {
+        const AttnStage<D>& S = st[kb & 1];
+        if (kb + 1 < nkb) gload(kb + 1);
+
+        // S^T tiles: keys kt*32 + 8g + 4h + e (element 4g + e), query fr
+        i32x16 sacc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kt][r] = 0;
+            const int row = kt * 32 + fr;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const i32x4 kf =
+                    *reinterpret_cast<const i32x4*>(S.k + row * D + ((((2 * s + h) ^ (row % CPR))) << 4));
+                sacc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], sacc[kt], 0, 0, 0);
+            }
+        }
+
+        float t[2][16];
+        float bm = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 skv = *reinterpret_cast<const f32x4*>(S.sk + kt * 32 + 8 * g + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = kb * AK + kt * 32 + 8 * g + 4 * h + e;
+                    const float x = ((float)sacc[kt][4 * g + e] * sqc) * skv[e];
+                    t[kt][4 * g + e] = key < Lk ? x : -__builtin_inff();
+                    bm = __builtin_fmaxf(bm, t[kt][4 * g + e]);
+                }
+            }
+        }
+        bm = __builtin_fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = __builtin_fmaxf(m_run, bm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+
+        // p * sv as BF16: 16-key step s16 = 2 kt + g / 2 holds keys 16 s16 + 8 (g % 2) + 4h + e
+        // at element 4 (g % 2) + e
+        u32x4 pb[4];
+        float ls = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 svv = *reinterpret_cast<const f32x4*>(S.sv + kt * 32 + 8 * g + 4 * h);
+                float pv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(t[kt][4 * g + e] - m_new);
+                    ls += p;
+                    pv[e] = p * svv[e];
+                }
+                pb[2 * kt + g / 2][2 * (g % 2)] = pack_bf16x2(pv[0], pv[1]);
+                pb[2 * kt + g / 2][2 * (g % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
+            }
+        }
+        l_run = l_run * alpha + ls;
+#pragma unroll
+        for (int dt = 0; dt < NS; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+        // O^T tiles: dims dt*32 + 8g + 4h + e (element 4g + e), query fr
+#pragma unroll
+        for (int s16 = 0; s16 < 4; ++s16) {
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, pb[s16]);
+#pragma unroll
+            for (int dt = 0; dt < NS; ++dt) {
+                const uint16_t* vrow = S.vt + (dt * 32 + fr) * VT_STRIDE + 16 * s16 + 4 * h;
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+                const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bop, o[dt], 0, 0, 0);
+            }
+        }
+
+        if (kb + 1 < nkb) sstore(st[(kb + 1) & 1]);
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float inv = 1.0f / l_tot;
+    if (q_row < Lq) {
+        uint16_t* orow = out + (qbase + q_row) * D;
+#pragma unroll
+        for (int dt = 0; dt < NS; ++dt) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x2 pk = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                                  pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+                *reinterpret_cast<u32x2*>(orow + dt * 32 + 8 * g + 4 * h) = pk;
+            }
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_attn(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk, const int8_t* vc,
+                       const float* sv, uint16_t* out, int64_t BH, int64_t Lq, int64_t Lk, float c,
+                       hipStream_t stream) {
+    const dim3 grid((unsigned)((Lq + AQ - 1) / AQ), (unsigned)BH);
+    attn_i8_kernel<D><<<grid, dim3(ATT_THREADS), 0, stream>>>(qc, sq, kc, sk, vc, sv, out, (int)Lq, (int)Lk, c);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attention_i8(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                               const int8_t* vc, const float* sv, void* out, int64_t BH, int64_t Lq, int64_t Lk,
+                               int64_t D, float scale, hipStream_t stream) {
+    const float c = scale * 1.4426950408889634f;   // log2(e): the kernel exponentiates in base 2
+    uint16_t* o = static_cast<uint16_t*>(out);
+    if (D == 64) return launch_attn<64>(qc, sq, kc, sk, vc, sv, o, BH, Lq, Lk, c, stream);
+    return launch_attn<128>(qc, sq, kc, sk, vc, sv, o, BH, Lq, Lk, c, stream);
+}
+
+}  // namespace qd

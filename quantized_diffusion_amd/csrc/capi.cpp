@@ -3,6 +3,7 @@
 // allocates, frees or synchronises, and no C++ exception crosses the ABI.
 #include <hip/hip_runtime.h>
 #include <stdarg.h>
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 
@@ -306,6 +307,52 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
     if (st != QD_OK) return st;
     if (M == 0 || N == 0) return ok();
     return hip_status(fn, qd::launch_gemm_i32(aq, lda, wq, ldw, acc, ldc, M, N, K, stream));
+}
+
+size_t qd_int8_attention_workspace_size(int64_t BH, int64_t Lq, int64_t Lk, int64_t D) {
+    if (BH <= 0 || Lq < 0 || Lk <= 0 || D <= 0) return 0;
+    const size_t rq = (size_t)BH * (size_t)Lq, rk = (size_t)BH * (size_t)Lk;
+    return round_up(rq * (size_t)D, kAlign) + 2 * round_up(rk * (size_t)D, kAlign) +
+           round_up(rq * sizeof(float), kAlign) + 2 * round_up(rk * sizeof(float), kAlign);
+}
+
+qd_status_t qd_int8_attention(const void* q, const void* k, const void* v, qd_dtype_t x_dtype, int64_t BH,
+                              int64_t Lq, int64_t Lk, int64_t D, float scale, void* workspace,
+                              size_t workspace_bytes, void* out_bf16, hipStream_t stream) {
+    const char* fn = "qd_int8_attention";
+    if (BH <= 0 || Lq < 0 || Lk <= 0)
+        return fail(QD_EINVAL, fn, "need BH >= 1, Lq >= 0, Lk >= 1 (BH=%lld, Lq=%lld, Lk=%lld)", (long long)BH,
+                    (long long)Lq, (long long)Lk);
+    if (D != 64 && D != 128) return fail(QD_EUNSUPPORTED, fn, "head dim D must be 64 or 128 (got %lld)", (long long)D);
+    if (!dtype_ok(x_dtype)) return fail(QD_EUNSUPPORTED, fn, "unknown input dtype %d", (int)x_dtype);
+    if (BH > 65535) return fail(QD_EUNSUPPORTED, fn, "BH (%lld) exceeds 65535", (long long)BH);
+    if (BH * (Lq > Lk ? Lq : Lk) > INT32_MAX) return fail(QD_EUNSUPPORTED, fn, "BH * L exceeds INT32_MAX");
+    if (Lq == 0) return ok();
+    if (!q || !k || !v || !workspace || !out_bf16) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out_bf16) & 15u)
+        return fail(QD_EUNSUPPORTED, fn, "q, k, v and out must be 16-byte aligned");
+    if ((uintptr_t)workspace & (kAlign - 1)) return fail(QD_EUNSUPPORTED, fn, "workspace must be 256-byte aligned");
+    const size_t need = qd_int8_attention_workspace_size(BH, Lq, Lk, D);
+    if (workspace_bytes < need) return fail(QD_EINVAL, fn, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    const int64_t rq = BH * Lq, rk = BH * Lk;
+    char* w = static_cast<char*>(workspace);
+    int8_t* qc = reinterpret_cast<int8_t*>(w);
+    w += round_up((size_t)rq * (size_t)D, kAlign);
+    int8_t* kc = reinterpret_cast<int8_t*>(w);
+    w += round_up((size_t)rk * (size_t)D, kAlign);
+    int8_t* vc = reinterpret_cast<int8_t*>(w);
+    w += round_up((size_t)rk * (size_t)D, kAlign);
+    float* sq = reinterpret_cast<float*>(w);
+    w += round_up((size_t)rq * sizeof(float), kAlign);
+    float* sk = reinterpret_cast<float*>(w);
+    w += round_up((size_t)rk * sizeof(float), kAlign);
+    float* sv = reinterpret_cast<float*>(w);
+    hipError_t e = qd::launch_rotquant(q, (int)x_dtype, false, 127, rq, D, D, qc, D, sq, stream, 0);
+    if (e == hipSuccess) e = qd::launch_rotquant(k, (int)x_dtype, false, 127, rk, D, D, kc, D, sk, stream, 0);
+    if (e == hipSuccess) e = qd::launch_rotquant(v, (int)x_dtype, false, 127, rk, D, D, vc, D, sv, stream, 0);
+    if (e != hipSuccess) return hip_status(fn, e);
+    const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)D));
+    return hip_status(fn, qd::launch_attention_i8(qc, sq, kc, sk, vc, sv, out_bf16, BH, Lq, Lk, D, sc, stream));
 }
 
 qd_status_t qd_set_gemm_tiles(qd_gemm_tiles_t tiles) {

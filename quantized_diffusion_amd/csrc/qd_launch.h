@@ -28,6 +28,12 @@ constexpr int kTensorwisePartials = 1024;
 hipError_t launch_quant_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                    int64_t ldq, float* scale, float* partial, hipStream_t stream);
 
+// INT8 attention on per-token codes: qc [BH*Lq, D], kc / vc [BH*Lk, D] with
+// FP32 scales per row; out [BH*Lq, D] BF16; D = 64 or 128.
+hipError_t launch_attention_i8(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                               const int8_t* vc, const float* sv, void* out, int64_t BH, int64_t Lq, int64_t Lk,
+                               int64_t D, float scale, hipStream_t stream);
+
 // Output tile of the INT8-weight GEMM kernels (K % 64 == 0): chosen by shape,
 // or fixed (process-wide) for tuning and tests.
 enum { GEMM_TILES_AUTO = 0, GEMM_TILES_256x256 = 1, GEMM_TILES_256x384 = 2 };

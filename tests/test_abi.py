@@ -287,3 +287,25 @@ def test_gemm_tiles_choice():
     qd.set_gemm_tiles(qd.GEMM_TILES_256x384)
     assert qd.int8_gemm_tiles(1000, 1000, 320) == qd.GEMM_TILES_256x384
     qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
+
+
+def test_attention_validation():
+    L = qd.lib()
+    ws = qd.attention_workspace_size(2, 100, 70, 128)
+    assert ws >= 2 * 100 * 128 + 2 * 2 * 70 * 128 + 4 * 2 * (100 + 2 * 70)
+    assert qd.attention_workspace_size(0, 1, 1, 64) == 0
+    A = ctypes.c_void_p(0x100000)
+    big = ctypes.c_size_t(1 << 40)
+    args = lambda BH, Lq, Lk, D, ws_ptr=A, n=big, q=A: (q, A, A, qd.QD_BF16, BH, Lq, Lk, D, ctypes.c_float(0.0),
+                                                        ws_ptr, n, A, STREAM)
+    assert L.qd_int8_attention(*args(1, 4, 4, 96)) == qd.QD_EUNSUPPORTED
+    assert b"head dim" in L.qd_last_error()
+    assert L.qd_int8_attention(*args(0, 4, 4, 64)) == qd.QD_EINVAL
+    assert L.qd_int8_attention(*args(1, 4, 0, 64)) == qd.QD_EINVAL
+    assert L.qd_int8_attention(*args(70000, 4, 4, 64)) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_attention(*args(1, 0, 4, 64)) == qd.QD_OK          # nothing to do
+    assert L.qd_int8_attention(*args(1, 4, 4, 64, n=ctypes.c_size_t(16))) == qd.QD_EINVAL
+    assert b"workspace too small" in L.qd_last_error()
+    assert L.qd_int8_attention(*args(1, 4, 4, 64, ws_ptr=ctypes.c_void_p(0x100010))) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_attention(*args(1, 4, 4, 64, q=FAKE_ODD)) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_attention(*args(1, 4, 4, 64, q=NULL)) == qd.QD_EINVAL
