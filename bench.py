@@ -31,6 +31,12 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, published (5.0 POP/s)
 PEAK_FP6_TFLOPS = 10100.0      # MI355X dense FP6/FP4 MFMA, published (10.1 PFLOP/s)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published (8 TB/s)
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA, published (2.5 PFLOP/s)
+# int8_attention: half its operations on the INT8 matrix cores (Q K^T), half on
+# the BF16 ones (P V): the combined dense peak is 1 / (0.5 / 5000 + 0.5 / 2500)
+PEAK_ATTN_TOPS = 1.0 / (0.5 / PEAK_INT8_TOPS + 0.5 / PEAK_BF16_TFLOPS)
+# attention workload: 40 heads of dimension 128 (a 14B-class video DiT block), one 16384-token sequence
+ATTN_BH, ATTN_L, ATTN_D = 40, 16384, 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_i8_traffic.json")
 GEMM_SRC = os.path.join(ROOT, "quantized_diffusion_amd", "csrc", "gemm_i8.hip")
 # The pages' single-call figure for M32700/K5376/N16128 on an RTX 5090 D v2
@@ -141,9 +147,9 @@ def main():
                     help="input activation folded into the quantizer (int8_linear(input_act=...))")
     ap.add_argument("--fp6", action="store_true",
                     help="W4A4 workload on the FP6 matrix path (convrot_w4a4_linear_fp6)")
-    ap.add_argument("--op", choices=["linear", "tensorwise"], default="linear",
+    ap.add_argument("--op", choices=["linear", "tensorwise", "attention"], default="linear",
                     help="linear: the whole layer (default); tensorwise: quantize_int8_tensorwise on the "
-                         "workload's activations")
+                         "workload's activations; attention: int8_attention on 40 heads x 16384 tokens x 128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -171,6 +177,8 @@ def main():
     w = workload(args.workload)
     if args.op == "tensorwise":
         return bench_tensorwise(args, w)
+    if args.op == "attention":
+        return bench_attention(args)
     int4 = w.kind == "w4a4"
     act = ["none", "gelu_tanh", "gelu_erf", "silu", "relu"].index(args.act)
     if act and int4:
@@ -364,6 +372,86 @@ def bench_tensorwise(args, w):
         out["cpu_baseline"] = {"value": round(alg / t / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(),
                                "kind": "oracle", "sample": f"the whole {M}x{K} tensor", "seconds": round(t, 3),
                                "sample_parity": {"codes_and_scale_identical": same}}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_attention(args):
+    """int8_attention (per-token quantization of q, k, v + the attention
+    kernel) on BF16 q, k, v [40, 16384, 128]; 4 BH L^2 D operations per step."""
+    import numpy as np
+    import torch
+
+    import quantized_diffusion_amd as qd
+
+    BH, L, D = ATTN_BH, ATTN_L, ATTN_D
+    dev = torch.device("cuda:0")
+    log(f"[bench] int8_attention BH{BH}/L{L}/D{D}: generating inputs")
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    q, k, v = (torch.randn((BH, L, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(3))
+    ws = torch.empty(qd.attention_workspace_size(BH, L, L, D), dtype=torch.uint8, device=dev)
+    y = torch.empty((BH, L, D), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        qd.int8_attention(q, k, v, workspace=ws, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = time_launches(step, args.steps, torch)
+    t_wall = time.perf_counter() - t0
+    al = lambda n: (n + 255) // 256 * 256
+    offs = np.cumsum([0, al(BH * L * D), al(BH * L * D), al(BH * L * D), al(4 * BH * L), al(4 * BH * L)])
+    qc, kc, vc = (ws[offs[i]:offs[i] + BH * L * D].view(BH, L, D).view(torch.int8) for i in range(3))
+    sq, sk, sv = (ws[offs[3 + i]:offs[3 + i] + 4 * BH * L].view(torch.float32).view(BH, L) for i in range(3))
+    y2 = torch.empty_like(y)
+    ms_k = time_launches(lambda: qd.int8_attention_codes(qc, sq, kc, sk, vc, sv, out=y2), max(5, args.steps), torch)
+    same = bool(torch.equal(y, y2))
+    ops = 4.0 * BH * L * L * D
+    tops = ops / (ms * 1e-3) / 1e12
+    k_tops = ops / (ms_k * 1e-3) / 1e12
+    out = {
+        "metric": f"int8_attention TOPS (Q K^T on INT8, P V on BF16 matrix cores, incl. per-token quantization), "
+                  f"BH{BH}/L{L}/D{D}",
+        "value": round(tops, 2), "unit": "TOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8 (scores), bf16 (probabilities x values)", "data": "synthetic",
+        "config": {"workload": f"int8_attention BH{BH}/Lq{L}/Lk{L}/D{D}", "BH": BH, "Lq": L, "Lk": L, "D": D,
+                   "inputs": "bf16 N(0,1)", "output": "bf16", "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": f"attn_i8_kernel<{D}>", "achieved": round(k_tops, 2),
+                     "peak": round(PEAK_ATTN_TOPS, 1), "unit": "TOP/s", "frac": round(k_tops / PEAK_ATTN_TOPS, 4),
+                     "traffic": None,
+                     "note": "peak = dense INT8 and BF16 matrix peaks combined for equal operation counts"},
+        "kernels": {"attention": {"ms": round(ms_k, 5), "TOP_per_s": round(k_tops, 2)},
+                    "quantizers": {"ms": round(ms - ms_k, 5)},
+                    "codes_entry_output_identical": same},
+        "device": torch.cuda.get_device_name(0),
+        "wall_s_timed_region": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        O = oracle.default()
+        h = lambda t: t.cpu().numpy()
+        kch, skh, vch, svh = h(kc[:1]), h(sk[:1]), h(vc[:1]), h(sv[:1])
+        n, t = 16, 0.0
+        while True:       # grow the sample of head-0 queries until it takes a few seconds
+            t0 = time.perf_counter()
+            want = O.attention_codes(h(qc[:1, :n]), h(sq[:1, :n]), kch, skh, vch, svh)
+            t = time.perf_counter() - t0
+            if t > args.cpu_budget / 4 or n >= L:
+                break
+            n = min(L, n * 4)
+        got = (y[:1, :n].contiguous().view(torch.int16).cpu().numpy().astype(np.uint32) << 16).view(np.float32)
+        vmax = np.abs(svh[:, :, None].astype(np.float64) * vch).max(axis=1)
+        bound = 2.0 ** -7 * vmax[:, None, :] + 2.0 ** -7 * np.abs(want)
+        out["cpu_baseline"] = {"value": round(4.0 * n * L * D / t / 1e12, 6), "unit": "TOP/s",
+                               "cores": O.num_threads(), "kind": "oracle",
+                               "sample": f"{n} queries of head 0 against all {L} keys (float64 oracle on the codes)",
+                               "seconds": round(t, 3),
+                               "sample_parity": {"outputs": int(want.size),
+                                                 "within_bound": bool(np.all(np.abs(got - want) <= bound))}}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -239,11 +239,11 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
  * Layout: q [BH, Lq, D], k and v [BH, Lk, D] (BH = batch x heads), rows of
  * D contiguous, in x_dtype (QD_F32, QD_BF16 or QD_F16); out [BH, Lq, D]
  * BF16, contiguous.  scale <= 0 selects 1/sqrt(D).
- * Accuracy: the probabilities times the value scale enter the value product
- * rounded to BF16 and the output is rounded to BF16, so each output differs
- * from the exact value of the reading (float64 softmax of the same codes) by
- * at most about 2^-9 * max_j |sv[j] * vc[j][d]| + 2^-8 * |out| (the test
- * bound is twice that).
+ * Accuracy: the probabilities and the dequantized values sv[j] * vc[j][d]
+ * enter the value product rounded to BF16 (relative error 2^-9 each), and
+ * the output is rounded to BF16, so each output differs from the exact value
+ * of the reading (float64 softmax of the same codes) by at most about
+ * 2^-8 * max_j |sv[j] * vc[j][d]| + 2^-8 * |out| (the tests allow twice that).
  * workspace: qd_int8_attention_workspace_size(BH, Lq, Lk, D) bytes, 256-byte
  * aligned; on return it holds, in order and each part 256-byte aligned, the
  * q, k, v codes ([BH*L, D] INT8) and then their FP32 row scales.
@@ -252,6 +252,13 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
  * Enqueues four kernels (three quantizer launches and the attention).
  */
 size_t qd_int8_attention_workspace_size(int64_t BH, int64_t Lq, int64_t Lk, int64_t D);
+/* The attention step alone, on codes already quantized per token (for
+ * example a cached K and V): qc [BH*Lq, D], kc / vc [BH*Lk, D] INT8, 16-byte
+ * aligned; sq [BH*Lq], sk / sv [BH*Lk] FP32 row scales; out as above.
+ * One kernel.  Same requirements as qd_int8_attention. */
+qd_status_t qd_int8_attention_codes(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                                    const int8_t* vc, const float* sv, int64_t BH, int64_t Lq, int64_t Lk,
+                                    int64_t D, float scale, void* out_bf16, hipStream_t stream);
 qd_status_t qd_int8_attention(const void* q, const void* k, const void* v, qd_dtype_t x_dtype, int64_t BH,
                               int64_t Lq, int64_t Lk, int64_t D, float scale, void* workspace,
                               size_t workspace_bytes, void* out_bf16, hipStream_t stream);

@@ -9,21 +9,22 @@
 // of the codes scaled by sq[i] * sk[j] * scale; softmax over the keys; the
 // output row is sum_j p[i][j] * sv[j] * v[j] / sum_j p[i][j], stored as BF16.
 //
-// attn_i8_kernel: a workgroup of 4 waves takes 128 queries of one (batch,
-// head), each wave 32 queries, and walks the keys in blocks of 64 through
-// two LDS stages (flash-attention style: running maximum and sum, the
-// output accumulators rescaled when the maximum grows).
+// attn_i8_kernel: a workgroup of 8 waves (two per SIMD) takes 256 queries of
+// one (batch, head), each wave 32 queries, and walks the keys in blocks of 64
+// through two LDS stages (flash-attention style: running maximum and sum,
+// the output accumulators rescaled only when some query's maximum grew).
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_i32_32x32x32_i8 (K from LDS as the "A" operand, the wave's Q
 //    codes in registers as "B"), so a lane holds 16 keys of ONE query: the
-//    row maximum and sum need one exchange between the two half-waves.
-//  * The probabilities p[i][j] * sv[j] (the key's value scale folded in) are
-//    rounded to BF16 in registers and are directly the "B" operand of
-//    v_mfma_f32_32x32x16_bf16 computing O^T = V^T P^T: the key order inside
-//    each 16-key step is the one the score layout leaves in the lanes, and
-//    the V^T operand is read in the same order from a transposed BF16 copy
-//    of the value codes in LDS (codes |v| <= 127 are exact in BF16).
-//  * Exponentials are base 2 with log2(e) folded into the score scale.
+//    row maximum and sum need one exchange between the two half-waves.  The
+//    key scale is applied to the scores, the query scale (>= 0, with the
+//    softmax scale and log2(e)) inside the base-2 exponent's FMA.
+//  * The probabilities are rounded to BF16 in registers and are directly the
+//    "B" operand of v_mfma_f32_32x32x16_bf16 computing O^T = V^T P^T: the
+//    key order inside each 16-key step is the one the score layout leaves in
+//    the lanes, and the V^T operand is read in the same order from a
+//    transposed tile of dequantized values sv[key] * vc[key][d] rounded to
+//    BF16, written into LDS 4 keys x 4 dims per thread.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,17 +37,17 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int AQ = 128;              // queries per workgroup (4 waves x 32)
+constexpr int AW = 8;                // waves per workgroup, 32 queries each
+constexpr int AQ = 32 * AW;          // queries per workgroup
 constexpr int AK = 64;               // keys per block
 constexpr int VT_STRIDE = AK + 4;    // BF16 per row of the transposed value tile (136 bytes)
-constexpr int ATT_THREADS = 256;
+constexpr int ATT_THREADS = 64 * AW;
 
 template <int D>
 struct AttnStage {
     int8_t k[AK * D];                // key codes, 16-byte chunks of row r XOR-swizzled by r % (D / 16)
-    uint16_t vt[D * VT_STRIDE];      // value codes as BF16, transposed: vt[d][key]
+    uint16_t vt[D * VT_STRIDE];      // dequantized values sv[key] * vc[key][d] as BF16, transposed: vt[d][key]
     float sk[AK];
-    float sv[AK];
 };
 
 template <int D>
@@ -60,9 +61,9 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
                                                               float c) {
     constexpr int NS = D / 32;                   // 32-element steps along D (score MFMA K, output tiles)
     constexpr int CPR = D / 16;                  // 16-byte chunks per key row
-    constexpr int KCH = AK * CPR / ATT_THREADS;  // key chunks staged per thread
-    constexpr int VCH = D / 4 / 16;              // value chunks staged per thread (a quarter of a row)
-    static_assert(KCH >= 1 && VCH >= 1, "head dim");
+    constexpr int KCH = (AK * CPR + ATT_THREADS - 1) / ATT_THREADS;   // key chunks staged per thread
+    constexpr int VG = AK / 4 * D / 4;           // value groups of 4 keys x 4 dims
+    static_assert(VG == ATT_THREADS || VG * 2 == ATT_THREADS, "value staging");
     __shared__ AttnStage<D> st[2];
 
     const int tid = threadIdx.x;
@@ -79,46 +80,57 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
 #pragma unroll
     for (int s = 0; s < NS; ++s)
         qf[s] = *reinterpret_cast<const i32x4*>(qc + (qbase + qr) * D + 32 * s + 16 * h);
-    const float sqc = sq[qbase + qr] * c;
+    const float sqc = sq[qbase + qr] * c;   // >= 0: applied inside the exponent
 
     // staging of key block kb: registers first (loads in flight during the
-    // previous block's math), then LDS
-    u32x4 kreg[KCH], vreg[VCH];
-    float sreg = 0.0f;
+    // previous block's math), then LDS.  Value group vg: keys 4 (vg % 16) + 0..3,
+    // dims 4 (vg / 16) + 0..3.
+    u32x4 kreg[KCH];
+    uint32_t vreg[4];
+    float vscale[4];
+    float skr = 0.0f;
+    const bool vthread = tid < VG;
+    const int vkq = tid & 15, vdg = tid >> 4;
     auto gload = [&](int kb) {
         const int k0 = kb * AK;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int ch = tid + ATT_THREADS * i;
-            const int key = min(k0 + ch / CPR, Lk - 1);
-            kreg[i] = *reinterpret_cast<const u32x4*>(kc + (kbase + key) * D + (ch % CPR) * 16);
+            if (ch < AK * CPR) {
+                const int key = min(k0 + ch / CPR, Lk - 1);
+                kreg[i] = *reinterpret_cast<const u32x4*>(kc + (kbase + key) * D + (ch % CPR) * 16);
+            }
         }
-        const int vkey = min(k0 + (tid & (AK - 1)), Lk - 1);
+        if (vthread) {
 #pragma unroll
-        for (int i = 0; i < VCH; ++i)
-            vreg[i] = *reinterpret_cast<const u32x4*>(vc + (kbase + vkey) * D + (tid / AK) * (D / 4) + 16 * i);
-        if (tid < AK) sreg = sk[kbase + min(k0 + tid, Lk - 1)];
-        else if (tid < 2 * AK) sreg = sv[kbase + min(k0 + tid - AK, Lk - 1)];
+            for (int j = 0; j < 4; ++j) {
+                const int key = min(k0 + 4 * vkq + j, Lk - 1);
+                vreg[j] = *reinterpret_cast<const uint32_t*>(vc + (kbase + key) * D + 4 * vdg);
+                vscale[j] = sv[kbase + key];
+            }
+        }
+        if (tid < AK) skr = sk[kbase + min(k0 + tid, Lk - 1)];
     };
     auto sstore = [&](AttnStage<D>& S) {
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int ch = tid + ATT_THREADS * i;
-            const int row = ch / CPR;
-            *reinterpret_cast<u32x4*>(S.k + row * D + (((ch % CPR) ^ (row % CPR)) << 4)) = kreg[i];
-        }
-        const int key = tid & (AK - 1);
-        const int d0 = (tid / AK) * (D / 4);
-#pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-#pragma unroll
-            for (int b = 0; b < 16; ++b) {
-                const int8_t code = (int8_t)((vreg[i][b >> 2] >> (8 * (b & 3))) & 0xFFu);
-                S.vt[(d0 + 16 * i + b) * VT_STRIDE + key] = (uint16_t)(f_bits((float)code) >> 16);
+            if (ch < AK * CPR) {
+                const int row = ch / CPR;
+                *reinterpret_cast<u32x4*>(S.k + row * D + (((ch % CPR) ^ (row % CPR)) << 4)) = kreg[i];
             }
         }
-        if (tid < AK) S.sk[tid] = sreg;
-        else if (tid < 2 * AK) S.sv[tid - AK] = sreg;
+        if (vthread) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {      // dim 4 vdg + e: keys 4 vkq .. +3
+                float f[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[j] = (float)(int8_t)((vreg[j] >> (8 * e)) & 0xFFu) * vscale[j];
+                const u32x2 pk = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+                *reinterpret_cast<u32x2*>(S.vt + (4 * vdg + e) * VT_STRIDE + 4 * vkq) = pk;
+            }
+        }
+        if (tid < AK) S.sk[tid] = skr;
     };
 
     f32x16 o[NS];
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
-    float m_run = -__builtin_inff();
+    float m_run = -__builtin_inff();   // running maximum of acc * sk (the query's scale applied later)
     float l_run = 0.0f;
 
     const int nkb = (Lk + AK - 1) / AK;
@@ -137,15 +149,18 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
         const AttnStage<D>& S = st[kb & 1];
         if (kb + 1 < nkb) gload(kb + 1);
 
-        // S^T tiles: keys kt*32 + 8g + 4h + e (element 4g + e), query fr
+        // S^T tiles: keys kt*32 + 8g + 4h + e (element 4g + e), query fr; the
+        // two tiles' MFMAs alternate (independent accumulators)
         i32x16 sacc[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kt][r] = 0;
-            const int row = kt * 32 + fr;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const int row = kt * 32 + fr;
                 const i32x4 kf =
                     *reinterpret_cast<const i32x4*>(S.k + row * D + ((((2 * s + h) ^ (row % CPR))) << 4));
                 sacc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], sacc[kt], 0, 0, 0);
@@ -154,6 +169,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
 
         float t[2][16];
         float bm = -__builtin_inff();
+        const bool tail = (kb + 1) * AK > Lk;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -161,19 +177,28 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
                 const f32x4 skv = *reinterpret_cast<const f32x4*>(S.sk + kt * 32 + 8 * g + 4 * h);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int key = kb * AK + kt * 32 + 8 * g + 4 * h + e;
-                    const float x = ((float)sacc[kt][4 * g + e] * sqc) * skv[e];
-                    t[kt][4 * g + e] = key < Lk ? x : -__builtin_inff();
-                    bm = __builtin_fmaxf(bm, t[kt][4 * g + e]);
+                    float x = (float)sacc[kt][4 * g + e] * skv[e];
+                    if (tail) x = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? x : -__builtin_inff();
+                    t[kt][4 * g + e] = x;
+                    bm = __builtin_fmaxf(bm, x);
                 }
             }
         }
         bm = __builtin_fmaxf(bm, __shfl_xor(bm, 32));
         const float m_new = __builtin_fmaxf(m_run, bm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float nm = -m_new * sqc;
+        if (__any(m_new != m_run)) {       // the output and the sum only need rescaling when a maximum grew
+            // (the first block: nothing accumulated yet; also avoids -inf * 0 for a zero query)
+            const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, sqc, nm));
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NS; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        }
         m_run = m_new;
 
-        // p * sv as BF16: 16-key step s16 = 2 kt + g / 2 holds keys 16 s16 + 8 (g % 2) + 4h + e
+        // p as BF16: 16-key step s16 = 2 kt + g / 2 holds keys 16 s16 + 8 (g % 2) + 4h + e
         // at element 4 (g % 2) + e
         u32x4 pb[4];
         float ls = 0.0f;
@@ -181,23 +206,19 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 svv = *reinterpret_cast<const f32x4*>(S.sv + kt * 32 + 8 * g + 4 * h);
                 float pv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(t[kt][4 * g + e] - m_new);
-                    ls += p;
-                    pv[e] = p * svv[e];
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kt][4 * g + e], sqc, nm));
+                    // keys past Lk (tail block only): p = 0, also for a zero query (-inf * 0)
+                    if (tail) pv[e] = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? pv[e] : 0.0f;
+                    ls += pv[e];
                 }
                 pb[2 * kt + g / 2][2 * (g % 2)] = pack_bf16x2(pv[0], pv[1]);
                 pb[2 * kt + g / 2][2 * (g % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
             }
         }
-        l_run = l_run * alpha + ls;
-#pragma unroll
-        for (int dt = 0; dt < NS; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        l_run += ls;
 
         // O^T tiles: dims dt*32 + 8g + 4h + e (element 4g + e), query fr
 #pragma unroll

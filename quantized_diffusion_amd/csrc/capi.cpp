@@ -316,17 +316,39 @@ size_t qd_int8_attention_workspace_size(int64_t BH, int64_t Lq, int64_t Lk, int6
            round_up(rq * sizeof(float), kAlign) + 2 * round_up(rk * sizeof(float), kAlign);
 }
 
-qd_status_t qd_int8_attention(const void* q, const void* k, const void* v, qd_dtype_t x_dtype, int64_t BH,
-                              int64_t Lq, int64_t Lk, int64_t D, float scale, void* workspace,
-                              size_t workspace_bytes, void* out_bf16, hipStream_t stream) {
-    const char* fn = "qd_int8_attention";
+static qd_status_t check_attention(const char* fn, int64_t BH, int64_t Lq, int64_t Lk, int64_t D) {
     if (BH <= 0 || Lq < 0 || Lk <= 0)
         return fail(QD_EINVAL, fn, "need BH >= 1, Lq >= 0, Lk >= 1 (BH=%lld, Lq=%lld, Lk=%lld)", (long long)BH,
                     (long long)Lq, (long long)Lk);
     if (D != 64 && D != 128) return fail(QD_EUNSUPPORTED, fn, "head dim D must be 64 or 128 (got %lld)", (long long)D);
-    if (!dtype_ok(x_dtype)) return fail(QD_EUNSUPPORTED, fn, "unknown input dtype %d", (int)x_dtype);
     if (BH > 65535) return fail(QD_EUNSUPPORTED, fn, "BH (%lld) exceeds 65535", (long long)BH);
     if (BH * (Lq > Lk ? Lq : Lk) > INT32_MAX) return fail(QD_EUNSUPPORTED, fn, "BH * L exceeds INT32_MAX");
+    return QD_OK;
+}
+
+qd_status_t qd_int8_attention_codes(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                                    const int8_t* vc, const float* sv, int64_t BH, int64_t Lq, int64_t Lk,
+                                    int64_t D, float scale, void* out_bf16, hipStream_t stream) {
+    const char* fn = "qd_int8_attention_codes";
+    qd_status_t st = check_attention(fn, BH, Lq, Lk, D);
+    if (st != QD_OK) return st;
+    if (Lq == 0) return ok();
+    if (!qc || !sq || !kc || !sk || !vc || !sv || !out_bf16) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (((uintptr_t)qc | (uintptr_t)kc | (uintptr_t)vc | (uintptr_t)out_bf16) & 15u)
+        return fail(QD_EUNSUPPORTED, fn, "codes and out must be 16-byte aligned");
+    if (((uintptr_t)sq | (uintptr_t)sk | (uintptr_t)sv) & 3u)
+        return fail(QD_EUNSUPPORTED, fn, "scales must be 4-byte aligned");
+    const float sc = scale > 0.0f ? scale : (float)(1.0 / sqrt((double)D));
+    return hip_status(fn, qd::launch_attention_i8(qc, sq, kc, sk, vc, sv, out_bf16, BH, Lq, Lk, D, sc, stream));
+}
+
+qd_status_t qd_int8_attention(const void* q, const void* k, const void* v, qd_dtype_t x_dtype, int64_t BH,
+                              int64_t Lq, int64_t Lk, int64_t D, float scale, void* workspace,
+                              size_t workspace_bytes, void* out_bf16, hipStream_t stream) {
+    const char* fn = "qd_int8_attention";
+    qd_status_t st0 = check_attention(fn, BH, Lq, Lk, D);
+    if (st0 != QD_OK) return st0;
+    if (!dtype_ok(x_dtype)) return fail(QD_EUNSUPPORTED, fn, "unknown input dtype %d", (int)x_dtype);
     if (Lq == 0) return ok();
     if (!q || !k || !v || !workspace || !out_bf16) return fail(QD_EINVAL, fn, "null pointer argument");
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out_bf16) & 15u)

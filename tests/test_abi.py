@@ -309,3 +309,16 @@ def test_attention_validation():
     assert L.qd_int8_attention(*args(1, 4, 4, 64, ws_ptr=ctypes.c_void_p(0x100010))) == qd.QD_EUNSUPPORTED
     assert L.qd_int8_attention(*args(1, 4, 4, 64, q=FAKE_ODD)) == qd.QD_EUNSUPPORTED
     assert L.qd_int8_attention(*args(1, 4, 4, 64, q=NULL)) == qd.QD_EINVAL
+
+
+def test_attention_codes_validation():
+    L = qd.lib()
+    A = ctypes.c_void_p(0x100000)
+    f = lambda BH, Lq, Lk, D, qc=A, s=A: L.qd_int8_attention_codes(qc, s, A, A, A, A, BH, Lq, Lk, D,
+                                                                   ctypes.c_float(0.0), A, STREAM)
+    assert f(1, 4, 4, 32) == qd.QD_EUNSUPPORTED
+    assert f(1, 4, 0, 64) == qd.QD_EINVAL
+    assert f(1, 0, 4, 64) == qd.QD_OK
+    assert f(1, 4, 4, 64, qc=FAKE_ODD) == qd.QD_EUNSUPPORTED
+    assert f(1, 4, 4, 64, s=ctypes.c_void_p(0x100002)) == qd.QD_EUNSUPPORTED
+    assert f(1, 4, 4, 64, qc=NULL) == qd.QD_EINVAL
