@@ -28,6 +28,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qd_device.h"
 #include "qd_launch.h"
 
@@ -145,7 +147,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     gload(0);
     sstore(st[0]);
     __syncthreads();
-    for (int kb = 0; kb < nkb; ++kb) {
+    // key blocks: the full ones, then the partial last one (keys past Lk
+    // masked) as a separate instance so that the full blocks carry no masking
+    auto block = [&](int kb, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
         const AttnStage<D>& S = st[kb & 1];
         if (kb + 1 < nkb) gload(kb + 1);
 
@@ -169,7 +174,6 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
 
         float t[2][16];
         float bm = -__builtin_inff();
-        const bool tail = (kb + 1) * AK > Lk;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float x = (float)sacc[kt][4 * g + e] * skv[e];
-                    if (tail) x = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? x : -__builtin_inff();
+                    if (TAIL) x = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? x : -__builtin_inff();
                     t[kt][4 * g + e] = x;
                     bm = __builtin_fmaxf(bm, x);
                 }
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
                 for (int e = 0; e < 4; ++e) {
                     pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kt][4 * g + e], sqc, nm));
                     // keys past Lk (tail block only): p = 0, also for a zero query (-inf * 0)
-                    if (tail) pv[e] = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? pv[e] : 0.0f;
+                    if (TAIL) pv[e] = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? pv[e] : 0.0f;
                     ls += pv[e];
                 }
                 pb[2 * kt + g / 2][2 * (g % 2)] = pack_bf16x2(pv[0], pv[1]);
@@ -236,7 +240,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
 
         if (kb + 1 < nkb) sstore(st[(kb + 1) & 1]);
         __syncthreads();
-    }
+    };
+    const int nfull = Lk / AK;
+    for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
+    if (nfull < nkb) block(nfull, std::true_type{});
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const float inv = 1.0f / l_tot;
