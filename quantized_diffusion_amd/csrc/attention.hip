@@ -9,7 +9,7 @@
 // of the codes scaled by sq[i] * sk[j] * scale; softmax over the keys; the
 // output row is sum_j p[i][j] * sv[j] * v[j] / sum_j p[i][j], stored as BF16.
 //
-// attn_i8_kernel: a workgroup of 8 waves (two per SIMD) takes 256 queries of
+// attn_i8_kernel: a workgroup of 12 waves (three per SIMD) takes 384 queries of
 // one (batch, head), each wave 32 queries, and walks the keys in blocks of 64
 // through two LDS stages (flash-attention style: running maximum and sum,
 // the output accumulators rescaled only when some query's maximum grew).
@@ -39,7 +39,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int AW = 8;                // waves per workgroup, 32 queries each
+constexpr int AW = 12;               // waves per workgroup, 32 queries each
 constexpr int AQ = 32 * AW;          // queries per workgroup
 constexpr int AK = 64;               // keys per block
 constexpr int VT_STRIDE = AK + 4;    // BF16 per row of the transposed value tile (136 bytes)
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     constexpr int CPR = D / 16;                  // 16-byte chunks per key row
     constexpr int KCH = (AK * CPR + ATT_THREADS - 1) / ATT_THREADS;   // key chunks staged per thread
     constexpr int VG = AK / 4 * D / 4;           // value groups of 4 keys x 4 dims
-    static_assert(VG == ATT_THREADS || VG * 2 == ATT_THREADS, "value staging");
+    static_assert(VG <= ATT_THREADS, "value staging");
     __shared__ AttnStage<D> st[2];
 
     const int tid = threadIdx.x;
