@@ -11,8 +11,9 @@
 //
 // attn_i8_kernel: a workgroup of 12 waves (three per SIMD) takes 384 queries of
 // one (batch, head), each wave 32 queries, and walks the keys in blocks of 64
-// through two LDS stages (flash-attention style: running maximum and sum,
-// the output accumulators rescaled only when some query's maximum grew).
+// through two LDS stages (flash-attention style: running reference maximum
+// and sum, the output accumulators rescaled only when some query's maximum
+// outgrew its reference by more than 2^8).
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_i32_32x32x32_i8 (K from LDS as the "A" operand, the wave's Q
 //    codes in registers as "B"), so a lane holds 16 keys of ONE query: the
@@ -47,7 +48,7 @@ constexpr int ATT_THREADS = 64 * AW;
 
 template <int D>
 struct AttnStage {
-    int8_t k[AK * D];                // key codes, 16-byte chunks of row r XOR-swizzled by r % (D / 16)
+    int8_t k[AK * D];                // key codes, 16-byte chunks of row r XOR-swizzled by (r / (256 / D)) % (D / 16)
     uint16_t vt[D * VT_STRIDE];      // dequantized values sv[key] * vc[key][d] as BF16, transposed: vt[d][key]
     float sk[AK];
 };
@@ -66,6 +67,10 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     constexpr int KCH = (AK * CPR + ATT_THREADS - 1) / ATT_THREADS;   // key chunks staged per thread
     constexpr int VG = AK / 4 * D / 4;           // value groups of 4 keys x 4 dims
     static_assert(VG <= ATT_THREADS, "value staging");
+    // chunk swizzle of a key row: 256 bytes of LDS banks hold 256 / D rows, so
+    // rows r and r + 256 / D share banks; XOR the chunk with the row's next bits
+    // to put the 16 rows read by 16 lanes on 16 distinct 16-byte bank groups
+    auto kswz = [](int row) { return (row / (256 / D)) & (CPR - 1); };
     __shared__ AttnStage<D> st[2];
 
     const int tid = threadIdx.x;
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
             const int ch = tid + ATT_THREADS * i;
             if (ch < AK * CPR) {
                 const int row = ch / CPR;
-                *reinterpret_cast<u32x4*>(S.k + row * D + (((ch % CPR) ^ (row % CPR)) << 4)) = kreg[i];
+                *reinterpret_cast<u32x4*>(S.k + row * D + (((ch % CPR) ^ kswz(row)) << 4)) = kreg[i];
             }
         }
         if (vthread) {
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
             for (int kt = 0; kt < 2; ++kt) {
                 const int row = kt * 32 + fr;
                 const i32x4 kf =
-                    *reinterpret_cast<const i32x4*>(S.k + row * D + ((((2 * s + h) ^ (row % CPR))) << 4));
+                    *reinterpret_cast<const i32x4*>(S.k + row * D + (((2 * s + h) ^ kswz(row)) << 4));
                 sacc[kt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], sacc[kt], 0, 0, 0);
             }
         }
@@ -189,18 +194,24 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
             }
         }
         bm = __builtin_fmaxf(bm, __shfl_xor(bm, 32));
-        const float m_new = __builtin_fmaxf(m_run, bm);
-        const float nm = -m_new * sqc;
-        if (__any(m_new != m_run)) {       // the output and the sum only need rescaling when a maximum grew
-            // (the first block: nothing accumulated yet; also avoids -inf * 0 for a zero query)
-            const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(__builtin_fmaf(m_run, sqc, nm));
+        // The reference maximum only moves when the block's maximum exceeds it
+        // by more than 2^8 in the exponent (the probabilities stay <= 256, far
+        // inside FP32 and BF16 range, and out = sum p v / sum p does not depend
+        // on the reference), so the rescale below is rare after the first blocks.
+        const bool grow = m_run == -__builtin_inff() || (bm - m_run) * sqc > 8.0f;
+        if (__any(grow)) {
+            // the first block: nothing accumulated yet (also avoids -inf * 0 for a zero query)
+            const float alpha = !grow ? 1.0f
+                                : m_run == -__builtin_inff() ? 0.0f
+                                : __builtin_amdgcn_exp2f((m_run - bm) * sqc);
+            m_run = grow ? bm : m_run;
             l_run *= alpha;
 #pragma unroll
             for (int dt = 0; dt < NS; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
         }
-        m_run = m_new;
+        const float nm = -m_run * sqc;
 
         // p as BF16: 16-key step s16 = 2 kt + g / 2 holds keys 16 s16 + 8 (g % 2) + 4h + e
         // at element 4 (g % 2) + e
