@@ -157,7 +157,7 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     auto block = [&](int kb, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const AttnStage<D>& S = st[kb & 1];
-        if (kb + 1 < nkb) gload(kb + 1);
+        gload(kb + 1);   // rows clamped to Lk - 1 past the last block
 
         // S^T tiles: keys kt*32 + 8g + 4h + e (element 4g + e), query fr; the
         // two tiles' MFMAs alternate (independent accumulators)
@@ -214,11 +214,14 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
         const float nm = -m_run * sqc;
 
         // p as BF16: 16-key step s16 = 2 kt + g / 2 holds keys 16 s16 + 8 (g % 2) + 4h + e
-        // at element 4 (g % 2) + e
-        u32x4 pb[4];
+        // at element 4 (g % 2) + e.  O^T tiles: dims dt*32 + 8g + 4h + e (element
+        // 4g + e), query fr.  The first tile's probabilities go to the matrix
+        // cores before the second tile's are computed, so that this VALU work
+        // (and the next block's staging) issues while those MFMAs run.
         float ls = 0.0f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
+            u32x4 pb[2];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 float pv[4];
@@ -229,27 +232,40 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
                     if (TAIL) pv[e] = kb * AK + kt * 32 + 8 * g + 4 * h + e < Lk ? pv[e] : 0.0f;
                     ls += pv[e];
                 }
-                pb[2 * kt + g / 2][2 * (g % 2)] = pack_bf16x2(pv[0], pv[1]);
-                pb[2 * kt + g / 2][2 * (g % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
+                pb[g / 2][2 * (g % 2)] = pack_bf16x2(pv[0], pv[1]);
+                pb[g / 2][2 * (g % 2) + 1] = pack_bf16x2(pv[2], pv[3]);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int s16 = 2 * kt + s2;
+                const bf16x8 bop = __builtin_bit_cast(bf16x8, pb[s2]);
+#pragma unroll
+                for (int dt = 0; dt < NS; ++dt) {
+                    const uint16_t* vrow = S.vt + (dt * 32 + fr) * VT_STRIDE + 16 * s16 + 4 * h;
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+                    const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+                    o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bop, o[dt], 0,
+                                                                    0, 0);
+                }
             }
         }
         l_run += ls;
-
-        // O^T tiles: dims dt*32 + 8g + 4h + e (element 4g + e), query fr
+        // staging of the next block (for the last block it reloads clamped rows
+        // into the stage nobody reads any more: no branch, one scheduling region)
+        sstore(st[(kb + 1) & 1]);
+        // schedule: value-tile reads first, the first tile's probabilities, then
+        // each of its MFMAs followed by a share of the remaining VALU work
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * 4 * NS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
 #pragma unroll
-        for (int s16 = 0; s16 < 4; ++s16) {
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, pb[s16]);
-#pragma unroll
-            for (int dt = 0; dt < NS; ++dt) {
-                const uint16_t* vrow = S.vt + (dt * 32 + fr) * VT_STRIDE + 16 * s16 + 4 * h;
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-                const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bop, o[dt], 0, 0, 0);
-            }
+        for (int i = 0; i < 2 * NS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
 
-        if (kb + 1 < nkb) sstore(st[(kb + 1) & 1]);
+
         __syncthreads();
     };
     const int nfull = Lk / AK;
