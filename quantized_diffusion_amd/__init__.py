@@ -35,7 +35,7 @@ __all__ = [
     "ACT_NONE", "ACT_GELU_TANH", "ACT_GELU_ERF", "ACT_SILU", "ACT_RELU", "pack_fp6", "fp6_scaled_mm",
     "fp6_gemm_i32", "w4a4_fp6_workspace_size", "convrot_w4a4_linear_fp6", "prepare_weights_w4a4_fp6",
     "quantize_and_rotate_rowwise_fp6", "set_gemm_tiles", "int8_gemm_tiles", "GEMM_TILES_AUTO", "GEMM_TILES_256x256",
-    "GEMM_TILES_256x384", "int8_attention", "attention_workspace_size",
+    "GEMM_TILES_256x384", "int8_attention", "attention_workspace_size", "int8_attention_codes",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -54,7 +54,7 @@ EXPORTED_SYMBOLS = (
     "qd_int8_linear_act", "qd_quantize_rowwise_act", "qd_input_act", "qd_pack_fp6", "qd_fp6_scaled_mm",
     "qd_fp6_gemm_i32", "qd_w4a4_fp6_workspace_size", "qd_convrot_w4a4_linear_fp6",
     "qd_quantize_and_rotate_rowwise_fp6", "qd_set_gemm_tiles", "qd_int8_gemm_tiles",
-    "qd_int8_attention_workspace_size", "qd_int8_attention",
+    "qd_int8_attention_workspace_size", "qd_int8_attention", "qd_int8_attention_codes",
 )
 
 
@@ -98,6 +98,8 @@ def lib():
         L.qd_int8_attention_workspace_size.argtypes = [I64, I64, I64, I64]
         L.qd_int8_attention.restype = St
         L.qd_int8_attention.argtypes = [P, P, P, St, I64, I64, I64, I64, ctypes.c_float, P, SZ, P, P]
+        L.qd_int8_attention_codes.restype = St
+        L.qd_int8_attention_codes.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_float, P, P]
         L.qd_set_gemm_tiles.restype = St
         L.qd_set_gemm_tiles.argtypes = [St]
         L.qd_int8_gemm_tiles.restype = St
@@ -371,6 +373,26 @@ def int8_attention(q, k, v, scale: float = 0.0, workspace=None, out=None):
         out = torch.empty((BH, Lq, D), dtype=torch.bfloat16, device=dev)
     _check(lib().qd_int8_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), BH, Lq, Lk, D, float(scale),
                                    _ptr(workspace), workspace.numel(), _ptr(out), _stream(dev)))
+    return out
+
+
+def int8_attention_codes(qc, sq, kc, sk, vc, sv, scale: float = 0.0, out=None):
+    """The attention step on per-token codes: qc [BH, Lq, D] / kc, vc [BH, Lk, D]
+    int8 and scales sq [BH, Lq] / sk, sv [BH, Lk] float32 -> BF16 [BH, Lq, D]."""
+    torch = _torch()
+    BH, Lq, D = qc.shape
+    Lk = kc.shape[1]
+    if kc.shape != (BH, Lk, D) or vc.shape != (BH, Lk, D) or sq.shape != (BH, Lq) or sk.shape != (BH, Lk) \
+            or sv.shape != (BH, Lk):
+        raise ValueError("code / scale shapes disagree")
+    for t, n in ((qc, "qc"), (kc, "kc"), (vc, "vc"), (sq, "sq"), (sk, "sk"), (sv, "sv")):
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    dev = _dev(qc, sq, kc, sk, vc, sv, out)
+    if out is None:
+        out = torch.empty((BH, Lq, D), dtype=torch.bfloat16, device=dev)
+    _check(lib().qd_int8_attention_codes(_ptr(qc), _ptr(sq), _ptr(kc), _ptr(sk), _ptr(vc), _ptr(sv), BH, Lq, Lk,
+                                         D, float(scale), _ptr(out), _stream(dev)))
     return out
 
 

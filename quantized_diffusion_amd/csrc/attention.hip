@@ -54,7 +54,7 @@ struct AttnStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __restrict__ qc,
+__global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* __restrict__ qc,
                                                               const float* __restrict__ sq,
                                                               const int8_t* __restrict__ kc,
                                                               const float* __restrict__ sk,
@@ -66,7 +66,6 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     constexpr int CPR = D / 16;                  // 16-byte chunks per key row
     constexpr int KCH = (AK * CPR + ATT_THREADS - 1) / ATT_THREADS;   // key chunks staged per thread
     constexpr int VG = AK / 4 * D / 4;           // value groups of 4 keys x 4 dims
-    static_assert(VG <= ATT_THREADS, "value staging");
     // chunk swizzle of a key row: 256 bytes of LDS banks hold 256 / D rows, so
     // rows r and r + 256 / D share banks; XOR the chunk with the row's next bits
     // to put the 16 rows read by 16 lanes on 16 distinct 16-byte bank groups
@@ -92,12 +91,11 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
     // staging of key block kb: registers first (loads in flight during the
     // previous block's math), then LDS.  Value group vg: keys 4 (vg % 16) + 0..3,
     // dims 4 (vg / 16) + 0..3.
+    constexpr int VGI = (VG + ATT_THREADS - 1) / ATT_THREADS;   // value groups staged per thread
     u32x4 kreg[KCH];
-    uint32_t vreg[4];
-    float vscale[4];
+    uint32_t vreg[VGI][4];
+    float vscale[VGI][4];
     float skr = 0.0f;
-    const bool vthread = tid < VG;
-    const int vkq = tid & 15, vdg = tid >> 4;
     auto gload = [&](int kb) {
         const int k0 = kb * AK;
 #pragma unroll
@@ -108,12 +106,16 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
                 kreg[i] = *reinterpret_cast<const u32x4*>(kc + (kbase + key) * D + (ch % CPR) * 16);
             }
         }
-        if (vthread) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = min(k0 + 4 * vkq + j, Lk - 1);
-                vreg[j] = *reinterpret_cast<const uint32_t*>(vc + (kbase + key) * D + 4 * vdg);
-                vscale[j] = sv[kbase + key];
+        for (int i = 0; i < VGI; ++i) {
+            const int vg = tid + ATT_THREADS * i;
+            if (vg < VG) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = min(k0 + 4 * (vg & 15) + j, Lk - 1);
+                    vreg[i][j] = *reinterpret_cast<const uint32_t*>(vc + (kbase + key) * D + 4 * (vg >> 4));
+                    vscale[i][j] = sv[kbase + key];
+                }
             }
         }
         if (tid < AK) skr = sk[kbase + min(k0 + tid, Lk - 1)];
@@ -127,14 +129,19 @@ __global__ __launch_bounds__(ATT_THREADS) void attn_i8_kernel(const int8_t* __re
                 *reinterpret_cast<u32x4*>(S.k + row * D + (((ch % CPR) ^ kswz(row)) << 4)) = kreg[i];
             }
         }
-        if (vthread) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {      // dim 4 vdg + e: keys 4 vkq .. +3
-                float f[4];
+        for (int i = 0; i < VGI; ++i) {
+            const int vg = tid + ATT_THREADS * i;
+            if (vg < VG) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) f[j] = (float)(int8_t)((vreg[j] >> (8 * e)) & 0xFFu) * vscale[j];
-                const u32x2 pk = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
-                *reinterpret_cast<u32x2*>(S.vt + (4 * vdg + e) * VT_STRIDE + 4 * vkq) = pk;
+                for (int e = 0; e < 4; ++e) {      // dim 4 (vg / 16) + e: keys 4 (vg % 16) .. +3
+                    float f[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        f[j] = (float)(int8_t)((vreg[i][j] >> (8 * e)) & 0xFFu) * vscale[i][j];
+                    const u32x2 pk = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+                    *reinterpret_cast<u32x2*>(S.vt + (4 * (vg >> 4) + e) * VT_STRIDE + 4 * (vg & 15)) = pk;
+                }
             }
         }
         if (tid < AK) S.sk[tid] = skr;
