@@ -19,7 +19,7 @@
 // the slice so that the copy queue never stalls a wave for long.  The output
 // tile is staged through the ring so that every store writes whole rows.
 // A wide variant owns 256 x 384 output tiles (twelve accumulators per wave,
-// three 40 KB stages), moving 17 % fewer bytes from L2 into LDS per MAC; the
+// four 40 KB stages), moving 17 % fewer bytes from L2 into LDS per MAC; the
 // launcher picks the tile by shape (rounds of one workgroup per CU).
 // A general kernel (any K % 16 == 0) stages operands through registers.
 //
@@ -614,20 +614,20 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
 // twelve v_mfma_i32_32x32x32_i8 accumulators (192 registers).  Per MAC it
 // moves 640 / (256 * 384) bytes from L2 into LDS instead of 512 / (256 * 256),
 // 17 % less, which is what limits the 256 x 256 kernel (the copies' power
-// and latency).  Same slice protocol as gemm_i8_w8_kernel with three 40 KB
-// stages (activation copies of slice t+3 go into stage t after slice t's
-// barrier, weight copies of slice t+2 at the start of slice t: leads of
-// about two and a half and two slices).  There is no room for a second set of
+// and latency).  Same slice protocol as gemm_i8_w8_kernel with four 40 KB
+// stages filling all 160 KB of LDS (activation copies of slice t+4 go into
+// stage t after slice t's barrier, weight copies of slice t+3 at the start
+// of slice t); the epilogue's scales and bias are copied into LDS only after
+// the K loop, above the staged output rows.  There is no room for a second set of
 // activation fragments, so each activation fragment is reloaded with the
 // next K half's data as soon as its three MFMAs are issued; the weight
 // fragments are double-buffered.  The output tile is staged through the ring
 // in two halves of 128 rows (768 bytes each, 16-byte chunks XOR-swizzled by
 // the row within groups of 16).
 constexpr int BNW = 384;                        // weight rows per wide tile
-constexpr int W12_NS = 3;
+constexpr int W12_NS = 4;
 constexpr int W12_STG = (BM + BNW) * BK;        // 40 KB per stage
 constexpr int W12_PER = 5;                      // copies per slice per thread (2 activation + 3 weight)
-constexpr int W12_EPI = 4 * 1024;               // sx[256] f32, sw[384] f32, bias[384] bf16
 
 __device__ __forceinline__ int w12_chunk(int ch, int sr) { return (ch & ~15) | ((ch ^ sr) & 15); }
 
@@ -640,8 +640,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     constexpr int PER = W12_PER;
     constexpr int RING = NS * STG;                 // >= 128 rows x 768 bytes of staged output
     static_assert(RING >= 128 * 768, "output staging");
-    __shared__ __attribute__((aligned(1024))) int8_t smem[RING + W12_EPI];
-    float* l_sx = reinterpret_cast<float*>(smem + RING);
+    __shared__ __attribute__((aligned(1024))) int8_t smem[RING];
+    float* l_sx = reinterpret_cast<float*>(smem + 128 * 768);   // after the K loop, above the staged rows
     float* l_sw = l_sx + 256;
     uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + BNW);
 
@@ -666,14 +666,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     const int wm = wave & 1;    // 128-row half of the activation tile
     const int wn = wave >> 1;   // 96-row quarter of the weight tile
 
-    if (MODE == MODE_BF16) {
-        if (tid < BM) l_sx[tid] = ep.a_scale[min(m0 + tid, M - 1) * ep.a_step];
-        if (tid < BNW) {
-            const int n = min(n0 + tid, N - 1);
-            l_sw[tid] = ep.w_scale[n * ep.w_step];
-            l_b[tid] = ep.bias ? ep.bias[n] : (uint16_t)0;
-        }
-    }
+    
 
     // copy instruction i of this wave covers rows 16 * (wave + 8 i) + lane / 4
     // of the activation tile (i < 2) and of the weight tile (i < 3)
@@ -802,7 +795,14 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
 
     if (MODE == MODE_BF16) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_s_barrier();   // the ring is free
+        if (tid < BM) l_sx[tid] = ep.a_scale[min(m0 + tid, M - 1) * ep.a_step];
+        if (tid < BNW) {
+            const int n = min(n0 + tid, N - 1);
+            l_sw[tid] = ep.w_scale[n * ep.w_step];
+            l_b[tid] = ep.bias ? ep.bias[n] : (uint16_t)0;
+        }
+        __syncthreads();
         uint16_t* out = static_cast<uint16_t*>(ep.out);
         // phase ph stages fragments j = 2 ph, 2 ph + 1 of every wave: tile rows
         // wm * 128 + 64 ph + 32 jj + lane % 32 -> staged row wm * 64 + 32 jj + lane % 32
