@@ -24,7 +24,7 @@ hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* 
 
 // Tensor-wise quantization: two launches; partial holds kTensorwisePartials
 // floats (K % 16 == 0).
-constexpr int kTensorwisePartials = 1024;
+constexpr int kTensorwisePartials = 2048;
 hipError_t launch_quant_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                    int64_t ldq, float* scale, float* partial, hipStream_t stream);
 
