@@ -9,10 +9,16 @@
 //  1. tw_amax_kernel: workgroup g takes rows g, g + G, ... and writes the
 //     largest |x| it saw to partial[g] (the caller's workspace);
 //  2. tw_quant_kernel: every workgroup reduces partial[0 .. G) (a maximum is
-//     exact in any order), forms s and r = fl(1/s), and quantizes the same
-//     rows with the reciprocal fast path and the exact-division fallback of
-//     the per-row quantizer; workgroup 0 writes s.
+//     exact in any order), forms s and r = fl(1/s), and quantizes rows
+//     M-1-g, M-1-g-G, ... with the reciprocal fast path and the
+//     exact-division fallback of the per-row quantizer; workgroup 0 writes s.
 // Each thread keeps U 16-byte chunks of a row in flight per iteration.
+// The second pass walks the rows in the opposite order to the first: the
+// rows the first pass read last are the ones most likely still held in the
+// memory-side cache (256 MB on MI355X, smaller than a large activation), so
+// they are read first, before the pass's own reads evict them.  The codes
+// are stored with the streaming hint so that they do not evict those rows
+// either (a GEMM reading the codes right after measured no slower for it).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,7 +86,8 @@ __global__ __launch_bounds__(kThreads) void tw_quant_kernel(const uint8_t* __res
     const int mode = (s >= kSlowScale) ? 1 : (s == 0.0f ? 0 : 2);
     const float r = 1.0f / s;
 
-    for (int row = blockIdx.x; row < M; row += gridDim.x) {
+    for (int i = blockIdx.x; i < M; i += gridDim.x) {
+        const int row = M - 1 - i;
         const uint8_t* src = x + (int64_t)row * ldx_bytes;
         int8_t* dst = q + (int64_t)row * ldq;
         for (int c0 = 0; c0 < cpr; c0 += U * kThreads) {
@@ -119,9 +126,10 @@ __global__ __launch_bounds__(kThreads) void tw_quant_kernel(const uint8_t* __res
                 if (E == 8) {
                     const u32x2 p = {pack4(code[0], code[1], code[2], code[3]),
                                      pack4(code[4 % E], code[5 % E], code[6 % E], code[7 % E])};
-                    *reinterpret_cast<u32x2*>(dst + (int64_t)c * E) = p;
+                    __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(dst + (int64_t)c * E));
                 } else {
-                    *reinterpret_cast<uint32_t*>(dst + (int64_t)c * E) = pack4(code[0], code[1], code[2], code[3]);
+                    __builtin_nontemporal_store(pack4(code[0], code[1], code[2], code[3]),
+                                                reinterpret_cast<uint32_t*>(dst + (int64_t)c * E));
                 }
             }
         }
