@@ -3,7 +3,9 @@
 
 One step = one int8_linear call over the whole input (rotate+quantize kernel,
 then the INT8 MFMA GEMM with the fused dequantizing epilogue), inputs already
-resident in HBM.  The reported value is 2*M*N*K / step time in TOP/s (INT8
+resident in HBM.  The weights are prepared offline (rotated, quantized and
+stored in the K-sliced layout: int8_linear_sliced; --row-major-weights runs
+int8_linear on the row-major codes instead, same results).  The reported value is 2*M*N*K / step time in TOP/s (INT8
 ops; the rotation and quantization are inside the timed step).
 
 Prints ONE JSON line.  Besides the headline it carries:
@@ -150,6 +152,8 @@ def main():
     ap.add_argument("--op", choices=["linear", "tensorwise", "attention"], default="linear",
                     help="linear: the whole layer (default); tensorwise: quantize_int8_tensorwise on the "
                          "workload's activations; attention: int8_attention on 40 heads x 16384 tokens x 128")
+    ap.add_argument("--row-major-weights", action="store_true",
+                    help="INT8 layer on row-major weight codes (int8_linear) instead of the K-sliced layout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -205,6 +209,9 @@ def main():
     else:
         wq, sw = qd.prepare_weights_w4a4(Wf) if int4 else qd.prepare_weights(Wf)
     del Wf
+    # INT8 weights in the K-sliced layout (also offline), unless asked for the row-major path
+    sliced = not int4 and not args.row_major_weights and K % 64 == 0
+    wsl = qd.slice_weights(wq) if sliced else None
     ws = torch.empty(qd.w4a4_fp6_workspace_size(M, K) if fp6 else qd.workspace_size(M, K), dtype=torch.uint8,
                      device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -215,6 +222,8 @@ def main():
             qd.convrot_w4a4_linear_fp6(x, wq, sw, bias, 256, ws, y)
         elif int4:
             qd.convrot_w4a4_linear(x, wq, sw, bias, 256, ws, y)
+        elif sliced:
+            qd.int8_linear_sliced(x, wsl, sw, bias, act, 256, ws, y)
         elif act:
             qd.int8_linear_act(x, wq, sw, bias, act, 256, ws, y)
         else:
@@ -250,18 +259,21 @@ def main():
     elif int4:
         ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_int4(x, 256, aq, sx), reps, torch)
         ms_g = time_launches(lambda: qd.int4_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
-    elif act:
-        ms_q = time_launches(lambda: qd.quantize_rowwise_act(x, act, 256, aq, sx), reps, torch)
-        ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     else:
-        ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
-        ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+        if act:
+            ms_q = time_launches(lambda: qd.quantize_rowwise_act(x, act, 256, aq, sx), reps, torch)
+        else:
+            ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
+        if sliced:
+            ms_g = time_launches(lambda: qd.int8_scaled_mm_sliced(aq, sx, wsl, sw, bias, y2), reps, torch)
+        else:
+            ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     same = bool(torch.equal(y2, y))
     q_bytes = (2.75 if fp6 else 3.0) * M * K + 4.0 * M
     g_min_bytes = float((M * K * 3 // 4 + N * K * 3 // 4) if fp6 else (M * K + (N * K // 2 if int4 else N * K))) \
         + 2 * M * N + 4 * M + 4 * N + 2 * N
     gemm_tops = ops / (ms_g * 1e-3) / 1e12
-    traffic = load_traffic(w.name + (" (FP6)" if fp6 else ""))
+    traffic = load_traffic(w.name + (" (FP6)" if fp6 else " (row-major weights)" if not int4 and not sliced else ""))
     out = {
         "metric": (f"W4A4 rotated linear TOPS on the FP6 matrix path (incl. rotate+quant) & % of INT8 MFMA "
                    f"peak, M{M}/K{K}/N{N}" if fp6 else
@@ -284,7 +296,8 @@ def main():
                    "rotation": "block-256 Walsh-Hadamard",
                    "activations": "bf16 -> int4 codes in int8 storage" if int4 else "bf16",
                    "weights": ("packed int4 per-channel fp32 scale, unpacked to int8 in the GEMM" if int4
-                               else "int8 per-channel fp32 scale"),
+                               else "int8 per-channel fp32 scale, K-sliced layout" if sliced
+                               else "int8 per-channel fp32 scale, row-major"),
                    "bias": "bf16", "output": "bf16", "parallelism": "single GPU"},
         "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
         "roofline": {"bound": "mfma", "kernel": ("gemm_f6_w8_kernel<MODE_BF16>" if fp6 else
@@ -292,7 +305,7 @@ def main():
                                                  "gemm_i8_w12_kernel<MODE_BF16> (256x384 tiles)"
                                                  if qd.int8_gemm_tiles(M, N, K) == qd.GEMM_TILES_256x384 else
                                                  "gemm_i8_w8_kernel<MODE_BF16, 4, WF_I8> (256x256 tiles)")
-                     + " (fused bf16 epilogue)",
+                     + (" (fused bf16 epilogue, K-sliced weights)" if sliced else " (fused bf16 epilogue)"),
                      "achieved": round(gemm_tops, 2), "peak": PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS,
                      "unit": "TFLOP/s" if fp6 else "TOP/s",
                      "frac": round(gemm_tops / (PEAK_FP6_TFLOPS if fp6 else PEAK_INT8_TOPS), 4),

@@ -216,6 +216,46 @@ qd_status_t qd_dequantize_int8(const int8_t* q, int64_t M, int64_t K, int64_t ld
                                void* out, int64_t ldo, hipStream_t stream);
 
 /*
+ * K-sliced INT8 weights: an offline re-layout of the weight codes that the
+ * GEMM reads faster (it is an operand format of this library, not a page's).
+ * Byte (n, k) of the [N, K] codes is stored at
+ *     (k / 64) * N * 64 + n * 64 + k % 64,
+ * i.e. the 64-byte K slices of all N rows one after another, slice by slice
+ * (N * K bytes, no row stride).  Reading a weight slice then moves whole
+ * 128-byte lines: one copy instruction of the GEMM fetches 1 KB of
+ * consecutive bytes instead of 16 separate 64-byte pieces, which costs less
+ * power per byte and lets the matrix cores run at a higher clock.  Values
+ * and results are those of the row-major entry points, bit for bit.
+ *
+ * qd_int8_slice_weights: wq [N, K] row-major (row stride ldw bytes, a
+ * multiple of 16, >= K) -> w_sliced (N * K bytes, caller-owned, 16-byte
+ * aligned).  K % 64 == 0 (QD_EUNSUPPORTED otherwise).  Enqueued on stream.
+ */
+qd_status_t qd_int8_slice_weights(const int8_t* wq, int64_t N, int64_t K, int64_t ldw, int8_t* w_sliced,
+                                  hipStream_t stream);
+
+/*
+ * qd_int8_linear_act with K-sliced weights (from qd_int8_slice_weights of
+ * the codes qd_quantize_and_rotate_rowwise made, same rotate_block).  Same
+ * arguments and requirements otherwise, plus K % 64 == 0; same results.
+ */
+qd_status_t qd_int8_linear_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                  qd_act_t input_act, const int8_t* w_sliced, int64_t N, const float* w_scale,
+                                  const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                  size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream);
+
+/* qd_int8_scaled_mm with K-sliced weights (K % 64 == 0); same results. */
+qd_status_t qd_int8_scaled_mm_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                                     const float* a_scale, const int8_t* w_sliced, int64_t N,
+                                     const float* w_scale, const void* bias_bf16, void* y_bf16,
+                                     int64_t ldy, hipStream_t stream);
+
+/* qd_int8_gemm_i32 with K-sliced weights (K % 64 == 0); same accumulators. */
+qd_status_t qd_int8_gemm_i32_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                                    const int8_t* w_sliced, int64_t N, int32_t* acc, int64_t ldc,
+                                    hipStream_t stream);
+
+/*
  * The raw INT32 accumulators of the same GEMM kernel (its INT32-store
  * epilogue), for verifying the exact contraction:
  *   acc[m, n] = sum_k aq[m, k] * wq[n, k], acc row stride ldc elements.

@@ -20,6 +20,8 @@ plus
   pack_int4(q), prepare_weights_w4a4(W) -> packed INT4 weights (two per byte)
   convrot_w4a4_linear(x, wp, w_scale, bias) -> bf16 y through the rotated INT4 path
   int4_scaled_mm / int4_gemm_i32        -> the packed-INT4 GEMM alone
+  slice_weights(wq) -> K-sliced INT8 weights; int8_linear_sliced / int8_scaled_mm_sliced /
+  int8_gemm_i32_sliced                  -> the same results with the faster weight layout
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ __all__ = [
     "fp6_gemm_i32", "w4a4_fp6_workspace_size", "convrot_w4a4_linear_fp6", "prepare_weights_w4a4_fp6",
     "quantize_and_rotate_rowwise_fp6", "set_gemm_tiles", "int8_gemm_tiles", "GEMM_TILES_AUTO", "GEMM_TILES_256x256",
     "GEMM_TILES_256x384", "int8_attention", "attention_workspace_size", "int8_attention_codes",
+    "slice_weights", "int8_linear_sliced", "int8_scaled_mm_sliced", "int8_gemm_i32_sliced",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -55,6 +58,7 @@ EXPORTED_SYMBOLS = (
     "qd_fp6_gemm_i32", "qd_w4a4_fp6_workspace_size", "qd_convrot_w4a4_linear_fp6",
     "qd_quantize_and_rotate_rowwise_fp6", "qd_set_gemm_tiles", "qd_int8_gemm_tiles",
     "qd_int8_attention_workspace_size", "qd_int8_attention", "qd_int8_attention_codes",
+    "qd_int8_slice_weights", "qd_int8_linear_sliced", "qd_int8_scaled_mm_sliced", "qd_int8_gemm_i32_sliced",
 )
 
 
@@ -137,6 +141,14 @@ def lib():
         L.qd_quantize_and_rotate_rowwise_fp6.argtypes = [P, St, I64, I64, I64, I32, P, I64, P, P]
         L.qd_convrot_w4a4_linear_fp6.restype = St
         L.qd_convrot_w4a4_linear_fp6.argtypes = [P, St, I64, I64, I64, P, I64, I64, P, P, I32, P, SZ, P, I64, P]
+        L.qd_int8_slice_weights.restype = St
+        L.qd_int8_slice_weights.argtypes = [P, I64, I64, I64, P, P]
+        L.qd_int8_linear_sliced.restype = St
+        L.qd_int8_linear_sliced.argtypes = [P, St, I64, I64, I64, St, P, I64, P, P, I32, P, SZ, P, I64, P]
+        L.qd_int8_scaled_mm_sliced.restype = St
+        L.qd_int8_scaled_mm_sliced.argtypes = [P, I64, I64, I64, P, P, I64, P, P, P, I64, P]
+        L.qd_int8_gemm_i32_sliced.restype = St
+        L.qd_int8_gemm_i32_sliced.argtypes = [P, I64, I64, I64, P, I64, P, I64, P]
         _lib = L
     return _lib
 
@@ -342,6 +354,94 @@ def int8_gemm_i32(aq, wq, out=None):
     _mat(out, "out")
     _check(lib().qd_int8_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wq), N, wq.stride(0), _ptr(out),
                                   out.stride(0), _stream(dev)))
+    return out
+
+
+# --------------------------------------------------- K-sliced INT8 weights
+
+def _sliced(w, name="w_sliced"):
+    """(K, N) of K-sliced weights: a contiguous int8 tensor [K / 64, N, 64]."""
+    torch = _torch()
+    if w.dtype != torch.int8 or w.dim() != 3 or w.shape[2] != 64 or not w.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int8 tensor [K / 64, N, 64] (from slice_weights)")
+    return w.shape[0] * 64, w.shape[1]
+
+
+def slice_weights(wq, out=None):
+    """Row-major INT8 weight codes wq [N, K] (K % 64 == 0) -> the K-sliced
+    layout the GEMM reads faster: int8 [K / 64, N, 64], element [u, n, j] =
+    wq[n, 64 u + j].  Offline, like prepare_weights."""
+    torch = _torch()
+    _mat(wq, "wq")
+    dev = _dev(wq, out)
+    N, K = wq.shape
+    if out is None:
+        out = torch.empty((max(K // 64, 0), N, 64), dtype=torch.int8, device=dev)
+    _check(lib().qd_int8_slice_weights(_ptr(wq), N, K, wq.stride(0), _ptr(out), _stream(dev)))
+    return out
+
+
+def int8_linear_sliced(x, w_sliced, w_scale, bias=None, input_act: int = ACT_NONE, rotate_block: int = 256,
+                       workspace=None, out=None):
+    """int8_linear_act with K-sliced weights (slice_weights of prepare_weights'
+    codes): identical results, faster GEMM."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, w_sliced, w_scale, bias, workspace, out)
+    M, K = x.shape
+    Kw, N = _sliced(w_sliced)
+    if Kw != K:
+        raise ValueError("x and w_sliced disagree on K")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_int8_linear_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act), _ptr(w_sliced),
+                                       N, _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
+                                       _stream(dev)))
+    return out
+
+
+def int8_scaled_mm_sliced(aq, a_scale, w_sliced, w_scale, bias=None, out=None):
+    """int8_scaled_mm with K-sliced weights: identical results."""
+    torch = _torch()
+    _mat(aq, "aq")
+    dev = _dev(aq, a_scale, w_sliced, w_scale, bias, out)
+    M, K = aq.shape
+    Kw, N = _sliced(w_sliced)
+    if Kw != K:
+        raise ValueError("aq and w_sliced disagree on K")
+    _rows_vec(a_scale, M, torch.float32, "a_scale")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_int8_scaled_mm_sliced(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(w_sliced), N,
+                                          _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def int8_gemm_i32_sliced(aq, w_sliced, out=None):
+    """int8_gemm_i32 with K-sliced weights: identical accumulators."""
+    torch = _torch()
+    _mat(aq, "aq")
+    dev = _dev(aq, w_sliced, out)
+    M, K = aq.shape
+    Kw, N = _sliced(w_sliced)
+    if Kw != K:
+        raise ValueError("aq and w_sliced disagree on K")
+    if out is None:
+        out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
+    _mat(out, "out")
+    _check(lib().qd_int8_gemm_i32_sliced(_ptr(aq), M, K, aq.stride(0), _ptr(w_sliced), N, _ptr(out),
+                                         out.stride(0), _stream(dev)))
     return out
 
 

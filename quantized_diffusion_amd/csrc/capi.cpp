@@ -161,6 +161,22 @@ qd_status_t qd_int8_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t ld
                                                y_bf16, ldy, M, N, K, stream));
 }
 
+qd_status_t qd_int8_scaled_mm_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                                     const float* a_scale, const int8_t* w_sliced, int64_t N,
+                                     const float* w_scale, const void* bias_bf16, void* y_bf16,
+                                     int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_int8_scaled_mm_sliced";
+    if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K-sliced weights need K %% 64 == 0 (K=%lld)", (long long)K);
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, w_sliced, N, K, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    return hip_status(fn, qd::launch_gemm_bf16(aq, lda, a_scale, w_sliced, K, w_scale, bias_bf16, y_bf16, ldy,
+                                               M, N, K, stream, 1, 1, true));
+}
+
 qd_status_t qd_int8_scaled_mm_ex(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
                                  const float* a_scale, int64_t a_scale_len, const int8_t* wq,
                                  int64_t N, int64_t ldw, const float* w_scale, int64_t w_scale_len,
@@ -209,7 +225,9 @@ static qd_status_t linear_impl(const char* fn, const void* x, qd_dtype_t x_dtype
                                int64_t ldx, qd_act_t act, const int8_t* wq, int64_t N, int64_t ldw,
                                const float* w_scale, const void* bias_bf16, int32_t rotate_block,
                                void* workspace, size_t workspace_bytes, void* y_bf16, int64_t ldy,
-                               hipStream_t stream) {
+                               hipStream_t stream, bool w_sliced = false) {
+    if (w_sliced && K % 64 != 0)
+        return fail(QD_EUNSUPPORTED, fn, "K-sliced weights need K %% 64 == 0 (K=%lld)", (long long)K);
     if (rotate_block != 0 && rotate_block != 256)
         return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 0 or 256 (got %d)", rotate_block);
     const bool rotate = rotate_block == 256;
@@ -236,7 +254,7 @@ static qd_status_t linear_impl(const char* fn, const void* x, qd_dtype_t x_dtype
     hipError_t e = qd::launch_rotquant(x, (int)x_dtype, rotate, 127, M, K, ldx, aq, ldq, sx, stream, (int)act);
     if (e != hipSuccess) return hip_status(fn, e);
     return hip_status(fn, qd::launch_gemm_bf16(aq, ldq, sx, wq, ldw, w_scale, bias_bf16, y_bf16,
-                                               ldy, M, N, K, stream));
+                                               ldy, M, N, K, stream, 1, 1, w_sliced));
 }
 
 qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
@@ -255,6 +273,28 @@ qd_status_t qd_int8_linear_act(const void* x, qd_dtype_t x_dtype, int64_t M, int
                                hipStream_t stream) {
     return linear_impl("qd_int8_linear_act", x, x_dtype, M, K, ldx, input_act, wq, N, ldw, w_scale, bias_bf16,
                        rotate_block, workspace, workspace_bytes, y_bf16, ldy, stream);
+}
+
+qd_status_t qd_int8_linear_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                  qd_act_t input_act, const int8_t* w_sliced, int64_t N, const float* w_scale,
+                                  const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                  size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream) {
+    return linear_impl("qd_int8_linear_sliced", x, x_dtype, M, K, ldx, input_act, w_sliced, N, K, w_scale,
+                       bias_bf16, rotate_block, workspace, workspace_bytes, y_bf16, ldy, stream, true);
+}
+
+qd_status_t qd_int8_slice_weights(const int8_t* wq, int64_t N, int64_t K, int64_t ldw, int8_t* w_sliced,
+                                  hipStream_t stream) {
+    const char* fn = "qd_int8_slice_weights";
+    if (N < 0 || K <= 0) return fail(QD_EINVAL, fn, "need N >= 0 and K > 0 (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 64", (long long)K);
+    if (ldw < K) return fail(QD_EINVAL, fn, "ldw (%lld) must be >= K", (long long)ldw);
+    if (N == 0) return ok();
+    if (!wq || !w_sliced) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (!aligned16(wq) || !aligned16(w_sliced) || ldw % 16 != 0)
+        return fail(QD_EUNSUPPORTED, fn, "wq, w_sliced and ldw must be 16-byte aligned");
+    if (N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "N too large");
+    return hip_status(fn, qd::launch_slice_weights(wq, ldw, N, K, w_sliced, stream));
 }
 
 qd_status_t qd_quantize_rowwise_act(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
@@ -307,6 +347,17 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
     if (st != QD_OK) return st;
     if (M == 0 || N == 0) return ok();
     return hip_status(fn, qd::launch_gemm_i32(aq, lda, wq, ldw, acc, ldc, M, N, K, stream));
+}
+
+qd_status_t qd_int8_gemm_i32_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+                                    const int8_t* w_sliced, int64_t N, int32_t* acc, int64_t ldc,
+                                    hipStream_t stream) {
+    const char* fn = "qd_int8_gemm_i32_sliced";
+    if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K-sliced weights need K %% 64 == 0 (K=%lld)", (long long)K);
+    qd_status_t st = check_gemm(fn, aq, M, K, lda, w_sliced, N, K, acc, ldc, 4);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    return hip_status(fn, qd::launch_gemm_i32(aq, lda, w_sliced, K, acc, ldc, M, N, K, stream, true));
 }
 
 size_t qd_int8_attention_workspace_size(int64_t BH, int64_t Lq, int64_t Lk, int64_t D) {

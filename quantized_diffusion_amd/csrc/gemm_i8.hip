@@ -355,8 +355,8 @@ enum { WF_I8 = 0, WF_I4 = 1 };   // weight operand: INT8, or INT4 packed two per
 __device__ __forceinline__ int swz4(int row) { return (row >> 3) & 1; }
 
 template <int MODE, int NS, int WF>
-__global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __restrict__ A, int64_t lda,
-                                                           const int8_t* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __restrict__ A, int64_t lda, int64_t a_ss,
+                                                           const int8_t* __restrict__ W, int64_t ldw, int64_t w_ss,
                                                            int M, int N, int K, EpiArgs ep) {
     constexpr int WROW = WF == WF_I4 ? BK / 2 : BK;          // weight bytes per row per slice
     constexpr int STG = BM * BK + BN * WROW;                 // bytes per stage
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
         const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
-        if (part == 0) dma16(sb + lrow[i], ga[i] + (int64_t)u * BK);
-        else if (WF == WF_I8 || i == 0) dma16(sb + BM * BK + lwrow[i], gw[i] + (int64_t)u * WROW);
+        if (part == 0) dma16(sb + lrow[i], ga[i] + (int64_t)u * a_ss);
+        else if (WF == WF_I8 || i == 0) dma16(sb + BM * BK + lwrow[i], gw[i] + (int64_t)u * w_ss);
     };
     auto issue = [&](int u) {
         copy_part(u, 0, 0);
@@ -632,8 +632,8 @@ constexpr int W12_PER = 5;                      // copies per slice per thread (
 __device__ __forceinline__ int w12_chunk(int ch, int sr) { return (ch & ~15) | ((ch ^ sr) & 15); }
 
 template <int MODE>
-__global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __restrict__ A, int64_t lda,
-                                                            const int8_t* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __restrict__ A, int64_t lda, int64_t a_ss,
+                                                            const int8_t* __restrict__ W, int64_t ldw, int64_t w_ss,
                                                             int M, int N, int K, EpiArgs ep) {
     constexpr int NS = W12_NS;
     constexpr int STG = W12_STG;
@@ -682,8 +682,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
         const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG) + (uint32_t)(16 * (wave + 8 * i) * BK);
-        if (part == 0) dma16(sb, ga[i] + (int64_t)u * BK);
-        else dma16(sb + BM * BK, gw[i] + (int64_t)u * BK);
+        if (part == 0) dma16(sb, ga[i] + (int64_t)u * a_ss);
+        else dma16(sb + BM * BK, gw[i] + (int64_t)u * w_ss);
     };
 
     // fragment b of a wave: rows base + 32 b + lane % 32, 16-byte chunk 2 kk + lane / 32;
@@ -1174,20 +1174,41 @@ bool use_wide(int64_t M, int64_t N) {
     return 141 * r2 < 100 * r1;
 }
 
+// Weight addressing: row-major (row n at wq + n * ldw), or K-sliced (byte
+// (n, k) at (k / 64) * N * 64 + n * 64 + k % 64, K % 64 == 0): the 64-byte
+// K slices of consecutive rows are adjacent, so each copy instruction of
+// the eight-wave kernels reads 1 KB of consecutive bytes (eight whole
+// 128-byte lines instead of sixteen half lines).
 template <int MODE>
-hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, int64_t M,
+hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, bool w_sliced, int64_t M,
                   int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t w_rs = w_sliced ? BK : ldw;
+    const int64_t w_ss = w_sliced ? N * BK : BK;
     if (K % BK == 0 && use_wide(M, N))
         gemm_i8_w12_kernel<MODE><<<dim3((unsigned)(((M + BM - 1) / BM) * ((N + BNW - 1) / BNW))), dim3(NT8), 0,
-                                   stream>>>(aq, lda, wq, ldw, (int)M, (int)N, (int)K, ep);
+                                   stream>>>(aq, lda, BK, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
     else if (K % BK == 0)
-        gemm_i8_w8_kernel<MODE, 4, WF_I8><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(aq, lda, wq, ldw, (int)M,
-                                                                                (int)N, (int)K, ep);
-    else
+        gemm_i8_w8_kernel<MODE, 4, WF_I8><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+            aq, lda, BK, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
+    else if (!w_sliced)
         gemm_i8_kernel<MODE><<<dim3((unsigned)tiles), dim3(NT), 0, stream>>>(aq, lda, wq, ldw, (int)M,
                                                                             (int)N, (int)K, ep);
+    else
+        return hipErrorInvalidValue;   // K-sliced weights need K % 64 == 0 (checked by the callers)
     return hipGetLastError();
+}
+
+// 16-byte chunk o of the K-sliced copy: slice o / (4N), row (o / 4) % N, quarter o % 4.
+__global__ __launch_bounds__(256) void slice_weights_kernel(const int8_t* __restrict__ wq, int64_t ldw, int64_t N,
+                                                            int64_t chunks, int8_t* __restrict__ out) {
+    for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < chunks; o += (int64_t)gridDim.x * 256) {
+        const int64_t u = o / (4 * N);
+        const int64_t r = o - u * 4 * N;
+        const int64_t n = r >> 2;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(wq + n * ldw + u * BK + (r & 3) * 16);
+        *reinterpret_cast<u32x4*>(out + o * 16) = v;
+    }
 }
 
 }  // namespace
@@ -1199,16 +1220,24 @@ bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K) { return K % BK == 0 
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
-                            int a_step, int w_step) {
+                            int a_step, int w_step, bool w_sliced) {
     EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, a_step, w_step};
-    return launch<MODE_BF16>(aq, lda, wq, ldw, M, N, K, ep, stream);
+    return launch<MODE_BF16>(aq, lda, wq, ldw, w_sliced, M, N, K, ep, stream);
 }
 
 hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
                            int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool w_sliced) {
     EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
-    return launch<MODE_I32>(aq, lda, wq, ldw, M, N, K, ep, stream);
+    return launch<MODE_I32>(aq, lda, wq, ldw, w_sliced, M, N, K, ep, stream);
+}
+
+hipError_t launch_slice_weights(const int8_t* wq, int64_t ldw, int64_t N, int64_t K, int8_t* out,
+                                hipStream_t stream) {
+    const int64_t chunks = K / BK * N * 4;
+    const int64_t blocks = (chunks + 255) / 256 < 65536 ? (chunks + 255) / 256 : 65536;
+    slice_weights_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(wq, ldw, N, chunks, out);
+    return hipGetLastError();
 }
 
 // Packed-INT4 weights (K % 64 == 0): five 24 KB stages, four slices in flight.
@@ -1219,7 +1248,7 @@ hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_sca
     EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, a_step, w_step};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
-        aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);
+        aq, lda, BK, reinterpret_cast<const int8_t*>(wp), ldw, BK / 2, (int)M, (int)N, (int)K, ep);
     return hipGetLastError();
 }
 
@@ -1248,7 +1277,7 @@ hipError_t launch_gemm_w4_i32(const int8_t* aq, int64_t lda, const uint8_t* wp, 
     EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     gemm_i8_w8_kernel<MODE_I32, 5, WF_I4><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
-        aq, lda, reinterpret_cast<const int8_t*>(wp), ldw, (int)M, (int)N, (int)K, ep);
+        aq, lda, BK, reinterpret_cast<const int8_t*>(wp), ldw, BK / 2, (int)M, (int)N, (int)K, ep);
     return hipGetLastError();
 }
 

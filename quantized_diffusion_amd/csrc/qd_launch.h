@@ -42,15 +42,21 @@ bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K);
 
 // y (BF16) = epilogue(aq . wq^T); bias may be null.  a_step / w_step: 1 for a
 // scale per row / per output channel, 0 for one scale for the whole operand.
+// w_sliced: wq in the K-sliced layout (byte (n, k) at (k / 64) * N * 64 +
+// n * 64 + k % 64, ldw unused, K % 64 == 0) instead of row-major.
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
-                            int a_step = 1, int w_step = 1);
+                            int a_step = 1, int w_step = 1, bool w_sliced = false);
 
 // acc (INT32) = aq . wq^T.
 hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
                            int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t stream);
+                           hipStream_t stream, bool w_sliced = false);
+
+// Row-major INT8 codes wq [N, K] (row stride ldw) -> the K-sliced layout (N * K bytes), K % 64 == 0.
+hipError_t launch_slice_weights(const int8_t* wq, int64_t ldw, int64_t N, int64_t K, int8_t* out,
+                                hipStream_t stream);
 
 // Packed-INT4 weights wp [N, K/2] (row stride ldw bytes), K % 64 == 0.
 hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const uint8_t* wp,

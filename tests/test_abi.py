@@ -322,3 +322,49 @@ def test_attention_codes_validation():
     assert f(1, 4, 4, 64, qc=FAKE_ODD) == qd.QD_EUNSUPPORTED
     assert f(1, 4, 4, 64, s=ctypes.c_void_p(0x100002)) == qd.QD_EUNSUPPORTED
     assert f(1, 4, 4, 64, qc=NULL) == qd.QD_EINVAL
+
+
+def test_sliced_weights_validation():
+    """K-sliced weight entry points: argument checks before any device work."""
+    L = qd.lib()
+    A = FAKE
+    ws = ctypes.c_size_t(1 << 30)
+    # slicing: K % 64, ldw >= K, alignment, nulls, empty
+    assert L.qd_int8_slice_weights(A, 8, 96, 96, A, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_slice_weights(A, 8, 128, 64, A, STREAM) == qd.QD_EINVAL
+    assert L.qd_int8_slice_weights(NULL, 8, 128, 128, A, STREAM) == qd.QD_EINVAL
+    assert L.qd_int8_slice_weights(FAKE_ODD, 8, 128, 128, A, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_slice_weights(A, 8, 128, 136, A, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_slice_weights(NULL, 0, 128, 128, NULL, STREAM) == qd.QD_OK
+    assert L.qd_int8_slice_weights(A, -1, 128, 128, A, STREAM) == qd.QD_EINVAL
+    # GEMMs: K % 64 (K % 16 alone is not enough for the sliced layout)
+    assert L.qd_int8_scaled_mm_sliced(A, 4, 96, 96, A, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_gemm_i32_sliced(A, 4, 96, 96, A, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_scaled_mm_sliced(A, 4, 128, 128, NULL, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EINVAL
+    assert L.qd_int8_gemm_i32_sliced(A, 4, 128, 64, A, 8, A, 8, STREAM) == qd.QD_EINVAL
+    assert L.qd_int8_gemm_i32_sliced(A, 4, 128, 128, FAKE_ODD, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_gemm_i32_sliced(A, 0, 128, 128, A, 8, A, 8, STREAM) == qd.QD_OK
+    # the layer: K % 64 with or without rotation, then the usual checks
+    f = lambda K, rb, x=A, w=A, act=qd.ACT_NONE: L.qd_int8_linear_sliced(
+        x, qd.QD_BF16, 4, K, K, act, w, 8, A, NULL, rb, ctypes.c_void_p(0x100000), ws, A, 8, STREAM)
+    assert f(96, 0) == qd.QD_EUNSUPPORTED
+    assert f(320, 256) == qd.QD_EUNSUPPORTED
+    assert f(128, 128) == qd.QD_EUNSUPPORTED
+    assert f(128, 0, w=NULL) == qd.QD_EINVAL
+    assert f(128, 0, x=FAKE_ODD) == qd.QD_EUNSUPPORTED
+    assert f(128, 0, act=9) == qd.QD_EUNSUPPORTED
+    assert L.qd_int8_linear_sliced(A, qd.QD_BF16, 0, 128, 128, qd.ACT_NONE, A, 8, A, NULL, 0, NULL, ctypes.c_size_t(0),
+                                   A, 8, STREAM) == qd.QD_OK
+
+
+def test_sliced_python_shape_checks():
+    """The binding's layout checks reject anything but an int8 [K / 64, N, 64] tensor (CPU tensors suffice)."""
+    import torch
+
+    with pytest.raises(ValueError):
+        qd._sliced(torch.zeros(4, 8, 32, dtype=torch.int8))
+    with pytest.raises(ValueError):
+        qd._sliced(torch.zeros(4, 8, 64, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        qd._sliced(torch.zeros(8, 4, 64, dtype=torch.int8).transpose(0, 1))
+    assert qd._sliced(torch.zeros(3, 5, 64, dtype=torch.int8)) == (192, 5)

@@ -1,0 +1,161 @@
+"""K-sliced INT8 weights: the re-layout against numpy's reshape, and the GEMM
+and the whole layer on sliced weights against the oracle (INT32 bit for bit,
+BF16 within one ulp) and against the row-major entry points (bit for bit:
+the same kernels with other copy addresses)."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_bf16_within_1ulp, bf16_bits, host, say, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def qd():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import quantized_diffusion_amd as q
+    q.lib()
+    return q
+
+
+@pytest.fixture(params=[1, 2], ids=["tiles256x256", "tiles256x384"])
+def tiles(request, qd):
+    qd.set_gemm_tiles(request.param)
+    yield request.param
+    qd.set_gemm_tiles(qd.GEMM_TILES_AUTO)
+
+
+def _codes(shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.integers(-128, 128, shape, dtype=np.int64).astype(np.int8)
+
+
+@pytest.mark.parametrize("N,K,pad", [(1, 64, 0), (8, 128, 16), (255, 320, 0), (384, 5376, 64), (1000, 1024, 0)])
+def test_slice_weights_layout(qd, N, K, pad):
+    """Element [u, n, j] of the sliced copy is wq[n, 64 u + j] (also from a strided wq)."""
+    import torch
+    say(f"slice_weights N={N} K={K} pad={pad}")
+    w = _codes((N, K + pad), 10 + N + K)
+    wd = to_dev(w)[:, :K]
+    ws = qd.slice_weights(wd)
+    assert ws.shape == (K // 64, N, 64) and ws.dtype == torch.int8
+    ref = np.ascontiguousarray(w[:, :K].reshape(N, K // 64, 64).transpose(1, 0, 2))
+    assert np.array_equal(host(ws), ref)
+
+
+SHAPES = [(1, 1, 64), (256, 256, 64), (257, 255, 128), (70, 130, 128), (300, 520, 512),
+          (513, 1000, 5376), (64, 4100, 1024)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_sliced_gemm_i32_exact(qd, O, tiles, M, N, K):
+    say(f"sliced gemm i32 M={M} N={N} K={K} tiles={tiles}")
+    a = _codes((M, K), M * 7 + N * 3 + K)
+    w = _codes((N, K), M * 5 + N * 11 + K)
+    wd = to_dev(w)
+    acc = qd.int8_gemm_i32_sliced(to_dev(a), qd.slice_weights(wd))
+    ref = O.gemm_i32(a, w)
+    assert np.array_equal(host(acc), ref)
+    assert np.array_equal(host(qd.int8_gemm_i32(to_dev(a), wd)), ref)
+
+
+def test_sliced_gemm_i32_extremes(qd, O, tiles):
+    say(f"sliced gemm i32 extremes tiles={tiles}")
+    K = 5376
+    a = np.full((300, K), 127, np.int8)
+    a[1::2] = -127
+    w = np.full((260, K), 127, np.int8)
+    w[::3] = -128
+    acc = qd.int8_gemm_i32_sliced(to_dev(a), qd.slice_weights(to_dev(w)))
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+
+
+@pytest.mark.parametrize("M,N,K,with_bias", [(256, 512, 512, True), (257, 264, 5376, True),
+                                              (77, 1000, 768, False), (1, 8, 64, True)])
+def test_sliced_scaled_mm(qd, O, tiles, M, N, K, with_bias):
+    import torch
+    say(f"sliced scaled_mm M={M} N={N} K={K} bias={with_bias} tiles={tiles}")
+    g = np.random.Generator(np.random.PCG64(M + N + K))
+    a = _codes((M, K), 3 * M + K)
+    w = _codes((N, K), 5 * N + K)
+    sx = (g.random(M, dtype=np.float32) * 1e-3).astype(np.float32)
+    sw = (g.random(N, dtype=np.float32) * 1e-3).astype(np.float32)
+    b = (g.standard_normal(N, dtype=np.float32) * 0.1).astype(np.float32) if with_bias else None
+    from synth import f32_to_bf16_bits
+    bb = f32_to_bf16_bits(b) if with_bias else None
+    bd = to_dev_bf16(bb) if with_bias else None
+    wd = to_dev(w)
+    y = qd.int8_scaled_mm_sliced(to_dev(a), to_dev(sx), qd.slice_weights(wd), to_dev(sw), bd)
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, bb)
+    assert_bf16_within_1ulp(bf16_bits(y), yo, "scaled_mm_sliced")
+    y_rm = qd.int8_scaled_mm(to_dev(a), to_dev(sx), wd, to_dev(sw), bd)
+    assert torch.equal(y, y_rm)
+
+
+@pytest.mark.parametrize("act", [0, 1, 3])
+@pytest.mark.parametrize("M,rotate", [(1, 256), (255, 256), (300, 256), (77, 0)])
+def test_int8_linear_sliced(qd, O, tiles, act, M, rotate):
+    """The whole layer on sliced weights: oracle within one ulp, and the same
+    bits as int8_linear_act on the row-major codes."""
+    import torch
+    from synth import make_bias, make_w, workload
+    say(f"int8_linear_sliced M={M} act={act} rotate={rotate} tiles={tiles}")
+    w = workload(1)
+    W, b = make_w(w), make_bias(w)
+    g = np.random.Generator(np.random.PCG64(900 + M + act))
+    from synth import f32_to_bf16_bits
+    x = f32_to_bf16_bits(g.standard_normal((M, w.K), dtype=np.float32))
+    wqo, swo = O.prepare_weights(W, block=rotate)
+    wq = to_dev(wqo)
+    xd, bd = to_dev_bf16(x), to_dev_bf16(b)
+    y = qd.int8_linear_sliced(xd, qd.slice_weights(wq), to_dev(swo), bd, input_act=act, rotate_block=rotate)
+    y_rm = qd.int8_linear_act(xd, wq, to_dev(swo), bd, input_act=act, rotate_block=rotate)
+    assert torch.equal(y, y_rm)
+    yo = O.linear(x, wqo, swo, b, block=rotate, act=act)
+    assert_bf16_within_1ulp(bf16_bits(y), yo, "int8_linear_sliced")
+
+
+def test_int8_linear_sliced_full_size(qd, O):
+    """The M32700/K5376/N16128 workload in the launch configuration the
+    benchmark times: the same bits as int8_linear on row-major weights, and
+    sampled outputs against the oracle."""
+    import torch
+    from synth import iter_w, iter_x, make_bias, workload
+    w = workload(3)
+    M, K, N = w.M, w.K, w.N
+    dev = torch.device("cuda:0")
+    say(f"sliced full-size {w.name}: inputs")
+    x_host = np.empty((M, K), np.uint16)
+    xd = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for r0, r1, bits in iter_x(w):
+        x_host[r0:r1] = bits
+        xd[r0:r1].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    W = np.empty((N, K), np.float32)
+    Wd = torch.empty((N, K), dtype=torch.float32, device=dev)
+    for r0, r1, chunk in iter_w(w):
+        W[r0:r1] = chunk
+        Wd[r0:r1].copy_(torch.from_numpy(chunk))
+    b = make_bias(w)
+    bd = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, sw = qd.prepare_weights(Wd)
+    del Wd
+    wsl = qd.slice_weights(wq)
+    ws = torch.empty(qd.workspace_size(M, K), dtype=torch.uint8, device=dev)
+    say("  int8_linear_sliced and int8_linear")
+    y = qd.int8_linear_sliced(xd, wsl, sw, bd, workspace=ws)
+    y_rm = qd.int8_linear(xd, wq, sw, bd, 256, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_rm)
+    del y_rm
+    say("  sampled outputs against the oracle")
+    wqo, swo = O.prepare_weights(W)
+    del W
+    qo, so = O.quantize_rowwise(x_host, "bf16", 256)
+    g = np.random.Generator(np.random.PCG64(9300))
+    rows = np.concatenate([g.integers(0, M, 4000), np.full(N, M - 1)])
+    cols = np.concatenate([g.integers(0, N, 4000), np.arange(N)])
+    yo, _ = O.linear_points(qo, so, rows, wqo, swo, b, cols)
+    yg = bf16_bits(y[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)])
+    assert_bf16_within_1ulp(yg, yo, "sliced full size")
