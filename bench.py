@@ -259,15 +259,17 @@ def main():
     elif int4:
         ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_int4(x, 256, aq, sx), reps, torch)
         ms_g = time_launches(lambda: qd.int4_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+    elif sliced:
+        # the layer's own pair: K-sliced activation codes and weights
+        asl = aq.view(K // 64, M, 64)
+        ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_sliced(x, 256, asl, sx, act), reps, torch)
+        ms_g = time_launches(lambda: qd.int8_scaled_mm_sliced(asl, sx, wsl, sw, bias, y2), reps, torch)
     else:
         if act:
             ms_q = time_launches(lambda: qd.quantize_rowwise_act(x, act, 256, aq, sx), reps, torch)
         else:
             ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise(x, 256, aq, sx), reps, torch)
-        if sliced:
-            ms_g = time_launches(lambda: qd.int8_scaled_mm_sliced(aq, sx, wsl, sw, bias, y2), reps, torch)
-        else:
-            ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
+        ms_g = time_launches(lambda: qd.int8_scaled_mm(aq, sx, wq, sw, bias, y2), reps, torch)
     same = bool(torch.equal(y2, y))
     q_bytes = (2.75 if fp6 else 3.0) * M * K + 4.0 * M
     g_min_bytes = float((M * K * 3 // 4 + N * K * 3 // 4) if fp6 else (M * K + (N * K // 2 if int4 else N * K))) \
@@ -318,7 +320,7 @@ def main():
                      "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "min_hbm_bytes": g_min_bytes},
             "separate_launch_output_identical": same,
-            "quantizer_writes": "fp6 operand format" if fp6 else "int8 codes",
+            "quantizer_writes": "fp6 operand format" if fp6 else "int8 codes, K-sliced" if sliced else "int8 codes",
         },
         "device": torch.cuda.get_device_name(0),
         "wall_s_timed_region": round(t_wall, 4),

@@ -238,20 +238,37 @@ qd_status_t qd_int8_slice_weights(const int8_t* wq, int64_t N, int64_t K, int64_
  * qd_int8_linear_act with K-sliced weights (from qd_int8_slice_weights of
  * the codes qd_quantize_and_rotate_rowwise made, same rotate_block).  Same
  * arguments and requirements otherwise, plus K % 64 == 0; same results.
+ * With rotate_block 256 the activation codes in the workspace are K-sliced
+ * as well (same workspace size).
  */
 qd_status_t qd_int8_linear_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
                                   qd_act_t input_act, const int8_t* w_sliced, int64_t N, const float* w_scale,
                                   const void* bias_bf16, int32_t rotate_block, void* workspace,
                                   size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream);
 
-/* qd_int8_scaled_mm with K-sliced weights (K % 64 == 0); same results. */
-qd_status_t qd_int8_scaled_mm_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+/*
+ * The rotating quantizer (as qd_quantize_rowwise_act with rotate_block 256;
+ * QD_ACT_NONE is qd_quantize_and_rotate_rowwise) writing its codes in the
+ * same K-sliced layout: byte (m, k) at (k / 64) * M * 64 + m * 64 + k % 64
+ * (M * K bytes, 16-byte aligned).  qd_int8_linear_sliced keeps its
+ * activation codes this way when it rotates.
+ */
+qd_status_t qd_quantize_and_rotate_rowwise_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                                  int64_t ldx, qd_act_t input_act, int32_t block,
+                                                  int8_t* q_sliced, float* row_scale, hipStream_t stream);
+
+/*
+ * qd_int8_scaled_mm with K-sliced weights (K % 64 == 0); the activation
+ * codes aq are row-major with row stride lda (a_sliced == 0) or K-sliced
+ * (a_sliced != 0, lda ignored).  Same results.
+ */
+qd_status_t qd_int8_scaled_mm_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
                                      const float* a_scale, const int8_t* w_sliced, int64_t N,
                                      const float* w_scale, const void* bias_bf16, void* y_bf16,
                                      int64_t ldy, hipStream_t stream);
 
-/* qd_int8_gemm_i32 with K-sliced weights (K % 64 == 0); same accumulators. */
-qd_status_t qd_int8_gemm_i32_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+/* qd_int8_gemm_i32 with K-sliced weights (and aq as in qd_int8_scaled_mm_sliced); same accumulators. */
+qd_status_t qd_int8_gemm_i32_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
                                     const int8_t* w_sliced, int64_t N, int32_t* acc, int64_t ldc,
                                     hipStream_t stream);
 

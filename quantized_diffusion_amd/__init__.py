@@ -39,6 +39,7 @@ __all__ = [
     "quantize_and_rotate_rowwise_fp6", "set_gemm_tiles", "int8_gemm_tiles", "GEMM_TILES_AUTO", "GEMM_TILES_256x256",
     "GEMM_TILES_256x384", "int8_attention", "attention_workspace_size", "int8_attention_codes",
     "slice_weights", "int8_linear_sliced", "int8_scaled_mm_sliced", "int8_gemm_i32_sliced",
+    "quantize_and_rotate_rowwise_sliced",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -59,6 +60,7 @@ EXPORTED_SYMBOLS = (
     "qd_quantize_and_rotate_rowwise_fp6", "qd_set_gemm_tiles", "qd_int8_gemm_tiles",
     "qd_int8_attention_workspace_size", "qd_int8_attention", "qd_int8_attention_codes",
     "qd_int8_slice_weights", "qd_int8_linear_sliced", "qd_int8_scaled_mm_sliced", "qd_int8_gemm_i32_sliced",
+    "qd_quantize_and_rotate_rowwise_sliced",
 )
 
 
@@ -146,9 +148,11 @@ def lib():
         L.qd_int8_linear_sliced.restype = St
         L.qd_int8_linear_sliced.argtypes = [P, St, I64, I64, I64, St, P, I64, P, P, I32, P, SZ, P, I64, P]
         L.qd_int8_scaled_mm_sliced.restype = St
-        L.qd_int8_scaled_mm_sliced.argtypes = [P, I64, I64, I64, P, P, I64, P, P, P, I64, P]
+        L.qd_int8_scaled_mm_sliced.argtypes = [P, I64, I64, I64, I32, P, P, I64, P, P, P, I64, P]
+        L.qd_quantize_and_rotate_rowwise_sliced.restype = St
+        L.qd_quantize_and_rotate_rowwise_sliced.argtypes = [P, St, I64, I64, I64, St, I32, P, P, P]
         L.qd_int8_gemm_i32_sliced.restype = St
-        L.qd_int8_gemm_i32_sliced.argtypes = [P, I64, I64, I64, P, I64, P, I64, P]
+        L.qd_int8_gemm_i32_sliced.argtypes = [P, I64, I64, I64, I32, P, I64, P, I64, P]
         _lib = L
     return _lib
 
@@ -407,12 +411,37 @@ def int8_linear_sliced(x, w_sliced, w_scale, bias=None, input_act: int = ACT_NON
     return out
 
 
-def int8_scaled_mm_sliced(aq, a_scale, w_sliced, w_scale, bias=None, out=None):
-    """int8_scaled_mm with K-sliced weights: identical results."""
+def _a_operand(aq, name="aq"):
+    """(M, K, lda, a_sliced) of activation codes: row-major int8 [M, K] or K-sliced [K / 64, M, 64]."""
+    if aq.dim() == 3:
+        K, M = _sliced(aq, name)
+        return M, K, K, 1
+    _mat(aq, name)
+    return aq.shape[0], aq.shape[1], aq.stride(0), 0
+
+
+def quantize_and_rotate_rowwise_sliced(x, block: int = 256, out_q=None, out_scale=None, input_act: int = ACT_NONE):
+    """quantize_and_rotate_rowwise (with input_act: quantize_rowwise_act) with the
+    codes in the K-sliced layout: returns (int8 [K / 64, M, 64], fp32 row scales [M])."""
     torch = _torch()
-    _mat(aq, "aq")
+    _mat(x, "x")
+    dev = _dev(x, out_q, out_scale)
+    M, K = x.shape
+    if out_q is None:
+        out_q = torch.empty((max(K // 64, 0), M, 64), dtype=torch.int8, device=dev)
+    if out_scale is None:
+        out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(lib().qd_quantize_and_rotate_rowwise_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act),
+                                                       block, _ptr(out_q), _ptr(out_scale), _stream(dev)))
+    return out_q, out_scale
+
+
+def int8_scaled_mm_sliced(aq, a_scale, w_sliced, w_scale, bias=None, out=None):
+    """int8_scaled_mm with K-sliced weights; aq row-major [M, K] or K-sliced
+    [K / 64, M, 64].  Identical results."""
+    torch = _torch()
     dev = _dev(aq, a_scale, w_sliced, w_scale, bias, out)
-    M, K = aq.shape
+    M, K, lda, a_sl = _a_operand(aq)
     Kw, N = _sliced(w_sliced)
     if Kw != K:
         raise ValueError("aq and w_sliced disagree on K")
@@ -423,24 +452,23 @@ def int8_scaled_mm_sliced(aq, a_scale, w_sliced, w_scale, bias=None, out=None):
     if out is None:
         out = _bf16_out(M, N, dev)
     _mat(out, "out")
-    _check(lib().qd_int8_scaled_mm_sliced(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(w_sliced), N,
+    _check(lib().qd_int8_scaled_mm_sliced(_ptr(aq), M, K, lda, a_sl, _ptr(a_scale), _ptr(w_sliced), N,
                                           _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
     return out
 
 
 def int8_gemm_i32_sliced(aq, w_sliced, out=None):
-    """int8_gemm_i32 with K-sliced weights: identical accumulators."""
+    """int8_gemm_i32 with K-sliced weights (aq as in int8_scaled_mm_sliced): identical accumulators."""
     torch = _torch()
-    _mat(aq, "aq")
     dev = _dev(aq, w_sliced, out)
-    M, K = aq.shape
+    M, K, lda, a_sl = _a_operand(aq)
     Kw, N = _sliced(w_sliced)
     if Kw != K:
         raise ValueError("aq and w_sliced disagree on K")
     if out is None:
         out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
     _mat(out, "out")
-    _check(lib().qd_int8_gemm_i32_sliced(_ptr(aq), M, K, aq.stride(0), _ptr(w_sliced), N, _ptr(out),
+    _check(lib().qd_int8_gemm_i32_sliced(_ptr(aq), M, K, lda, a_sl, _ptr(w_sliced), N, _ptr(out),
                                          out.stride(0), _stream(dev)))
     return out
 

@@ -161,20 +161,33 @@ qd_status_t qd_int8_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t ld
                                                y_bf16, ldy, M, N, K, stream));
 }
 
-qd_status_t qd_int8_scaled_mm_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+qd_status_t qd_int8_scaled_mm_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
                                      const float* a_scale, const int8_t* w_sliced, int64_t N,
                                      const float* w_scale, const void* bias_bf16, void* y_bf16,
                                      int64_t ldy, hipStream_t stream) {
     const char* fn = "qd_int8_scaled_mm_sliced";
     if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K-sliced weights need K %% 64 == 0 (K=%lld)", (long long)K);
-    qd_status_t st = check_gemm(fn, aq, M, K, lda, w_sliced, N, K, y_bf16, ldy, 8);
+    qd_status_t st = check_gemm(fn, aq, M, K, a_sliced ? K : lda, w_sliced, N, K, y_bf16, ldy, 8);
     if (st != QD_OK) return st;
     if (M == 0 || N == 0) return ok();
     if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
     if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
         return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
     return hip_status(fn, qd::launch_gemm_bf16(aq, lda, a_scale, w_sliced, K, w_scale, bias_bf16, y_bf16, ldy,
-                                               M, N, K, stream, 1, 1, true));
+                                               M, N, K, stream, 1, 1, true, a_sliced != 0));
+}
+
+qd_status_t qd_quantize_and_rotate_rowwise_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                                  int64_t ldx, qd_act_t input_act, int32_t block,
+                                                  int8_t* q_sliced, float* row_scale, hipStream_t stream) {
+    const char* fn = "qd_quantize_and_rotate_rowwise_sliced";
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, true, block, q_sliced, K, row_scale);
+    if (st != QD_OK) return st;
+    st = check_act(fn, input_act, x_dtype, K);
+    if (st != QD_OK) return st;
+    if (M == 0) return ok();
+    return hip_status(fn, qd::launch_rotquant_sliced(x, (int)x_dtype, M, K, ldx, q_sliced, row_scale, stream,
+                                                     (int)input_act));
 }
 
 qd_status_t qd_int8_scaled_mm_ex(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
@@ -251,10 +264,14 @@ static qd_status_t linear_impl(const char* fn, const void* x, qd_dtype_t x_dtype
     if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
     if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
         return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
-    hipError_t e = qd::launch_rotquant(x, (int)x_dtype, rotate, 127, M, K, ldx, aq, ldq, sx, stream, (int)act);
+    // with K-sliced weights and rotation, the activation codes go to the workspace K-sliced too
+    const bool a_sliced = w_sliced && rotate;
+    hipError_t e = a_sliced ? qd::launch_rotquant_sliced(x, (int)x_dtype, M, K, ldx, aq, sx, stream, (int)act)
+                            : qd::launch_rotquant(x, (int)x_dtype, rotate, 127, M, K, ldx, aq, ldq, sx, stream,
+                                                  (int)act);
     if (e != hipSuccess) return hip_status(fn, e);
     return hip_status(fn, qd::launch_gemm_bf16(aq, ldq, sx, wq, ldw, w_scale, bias_bf16, y_bf16,
-                                               ldy, M, N, K, stream, 1, 1, w_sliced));
+                                               ldy, M, N, K, stream, 1, 1, w_sliced, a_sliced));
 }
 
 qd_status_t qd_int8_linear(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
@@ -349,15 +366,15 @@ qd_status_t qd_int8_gemm_i32(const int8_t* aq, int64_t M, int64_t K, int64_t lda
     return hip_status(fn, qd::launch_gemm_i32(aq, lda, wq, ldw, acc, ldc, M, N, K, stream));
 }
 
-qd_status_t qd_int8_gemm_i32_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
+qd_status_t qd_int8_gemm_i32_sliced(const int8_t* aq, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
                                     const int8_t* w_sliced, int64_t N, int32_t* acc, int64_t ldc,
                                     hipStream_t stream) {
     const char* fn = "qd_int8_gemm_i32_sliced";
     if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K-sliced weights need K %% 64 == 0 (K=%lld)", (long long)K);
-    qd_status_t st = check_gemm(fn, aq, M, K, lda, w_sliced, N, K, acc, ldc, 4);
+    qd_status_t st = check_gemm(fn, aq, M, K, a_sliced ? K : lda, w_sliced, N, K, acc, ldc, 4);
     if (st != QD_OK) return st;
     if (M == 0 || N == 0) return ok();
-    return hip_status(fn, qd::launch_gemm_i32(aq, lda, w_sliced, K, acc, ldc, M, N, K, stream, true));
+    return hip_status(fn, qd::launch_gemm_i32(aq, lda, w_sliced, K, acc, ldc, M, N, K, stream, true, a_sliced != 0));
 }
 
 size_t qd_int8_attention_workspace_size(int64_t BH, int64_t Lq, int64_t Lk, int64_t D) {

@@ -1174,24 +1174,27 @@ bool use_wide(int64_t M, int64_t N) {
     return 141 * r2 < 100 * r1;
 }
 
-// Weight addressing: row-major (row n at wq + n * ldw), or K-sliced (byte
+// Operand addressing: row-major (row n at wq + n * ldw), or K-sliced (byte
 // (n, k) at (k / 64) * N * 64 + n * 64 + k % 64, K % 64 == 0): the 64-byte
 // K slices of consecutive rows are adjacent, so each copy instruction of
 // the eight-wave kernels reads 1 KB of consecutive bytes (eight whole
-// 128-byte lines instead of sixteen half lines).
+// 128-byte lines instead of sixteen half lines).  Either operand may be
+// K-sliced (the weights offline, the activation codes by the quantizer).
 template <int MODE>
-hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, bool w_sliced, int64_t M,
-                  int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
+hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, bool w_sliced, bool a_sliced,
+                  int64_t M, int64_t N, int64_t K, const EpiArgs& ep, hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t w_rs = w_sliced ? BK : ldw;
     const int64_t w_ss = w_sliced ? N * BK : BK;
+    const int64_t a_rs = a_sliced ? BK : lda;
+    const int64_t a_ss = a_sliced ? M * BK : BK;
     if (K % BK == 0 && use_wide(M, N))
         gemm_i8_w12_kernel<MODE><<<dim3((unsigned)(((M + BM - 1) / BM) * ((N + BNW - 1) / BNW))), dim3(NT8), 0,
-                                   stream>>>(aq, lda, BK, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
+                                   stream>>>(aq, a_rs, a_ss, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
     else if (K % BK == 0)
         gemm_i8_w8_kernel<MODE, 4, WF_I8><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
-            aq, lda, BK, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
-    else if (!w_sliced)
+            aq, a_rs, a_ss, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
+    else if (!w_sliced && !a_sliced)
         gemm_i8_kernel<MODE><<<dim3((unsigned)tiles), dim3(NT), 0, stream>>>(aq, lda, wq, ldw, (int)M,
                                                                             (int)N, (int)K, ep);
     else
@@ -1220,16 +1223,16 @@ bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K) { return K % BK == 0 
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
-                            int a_step, int w_step, bool w_sliced) {
+                            int a_step, int w_step, bool w_sliced, bool a_sliced) {
     EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, a_step, w_step};
-    return launch<MODE_BF16>(aq, lda, wq, ldw, w_sliced, M, N, K, ep, stream);
+    return launch<MODE_BF16>(aq, lda, wq, ldw, w_sliced, a_sliced, M, N, K, ep, stream);
 }
 
 hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
                            int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t stream, bool w_sliced) {
+                           hipStream_t stream, bool w_sliced, bool a_sliced) {
     EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
-    return launch<MODE_I32>(aq, lda, wq, ldw, w_sliced, M, N, K, ep, stream);
+    return launch<MODE_I32>(aq, lda, wq, ldw, w_sliced, a_sliced, M, N, K, ep, stream);
 }
 
 hipError_t launch_slice_weights(const int8_t* wq, int64_t ldw, int64_t N, int64_t K, int8_t* out,

@@ -16,6 +16,10 @@ hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int6
 
 // Rotating INT4 quantizer writing the FP6 operand format directly (16-bit
 // inputs, dtype 1 or 2): q6 [M, 3K/4] bytes, row stride ld6 (multiple of 16).
+// The rotating INT8 quantizer writing the K-sliced code layout (byte (m, k)
+// at (k / 64) * M * 64 + m * 64 + k % 64), K % 256 == 0; act as launch_rotquant.
+hipError_t launch_rotquant_sliced(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                  float* scale, hipStream_t stream, int act);
 hipError_t launch_rotquant_fp6(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q6,
                                int64_t ld6, float* scale, hipStream_t stream);
 
@@ -43,16 +47,17 @@ bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K);
 // y (BF16) = epilogue(aq . wq^T); bias may be null.  a_step / w_step: 1 for a
 // scale per row / per output channel, 0 for one scale for the whole operand.
 // w_sliced: wq in the K-sliced layout (byte (n, k) at (k / 64) * N * 64 +
-// n * 64 + k % 64, ldw unused, K % 64 == 0) instead of row-major.
+// n * 64 + k % 64, ldw unused, K % 64 == 0) instead of row-major; a_sliced:
+// aq likewise (M rows, lda unused).
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
                             int64_t ldy, int64_t M, int64_t N, int64_t K, hipStream_t stream,
-                            int a_step = 1, int w_step = 1, bool w_sliced = false);
+                            int a_step = 1, int w_step = 1, bool w_sliced = false, bool a_sliced = false);
 
 // acc (INT32) = aq . wq^T.
 hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw,
                            int32_t* acc, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t stream, bool w_sliced = false);
+                           hipStream_t stream, bool w_sliced = false, bool a_sliced = false);
 
 // Row-major INT8 codes wq [N, K] (row stride ldw) -> the K-sliced layout (N * K bytes), K % 64 == 0.
 hipError_t launch_slice_weights(const int8_t* wq, int64_t ldw, int64_t N, int64_t K, int8_t* out,

@@ -185,7 +185,7 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
 // ldq its row stride in bytes, 3K/4 bytes per row): each 8-code chunk is
 // 48 bits, three 2-byte pieces placed in the block's 192-byte image at their
 // head / tail positions.
-template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false>
+template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false, bool SL = false>
 __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void rotquant_kernel(const uint8_t* __restrict__ x,
                                                         int64_t ldx_bytes, int M, int K, int nb,
                                                         int R, int8_t* __restrict__ q,
@@ -351,7 +351,10 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
             const int rl2 = (int)(__umul24((uint32_t)qq, nb_inv) >> 20);
             const int row2 = blockIdx.x * R + rl2;
             if (rl2 < R && row2 < M) {
-                int8_t* dst = q + (int64_t)row2 * ldq + (qq - rl2 * nb) * 256 + 16 * (lane & 15);
+                // SL: K-sliced codes, ldq = the slice stride (M * 64 bytes)
+                const int blk2 = qq - rl2 * nb, kin = 16 * (lane & 15);
+                int8_t* dst = SL ? q + (int64_t)(4 * blk2 + (kin >> 6)) * ldq + (int64_t)row2 * 64 + (kin & 63)
+                                 : q + (int64_t)row2 * ldq + blk2 * 256 + kin;
                 store_codes(val[j], dst);
             }
         }
@@ -437,7 +440,7 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
     }
 }
 
-template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false>
+template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false, bool SL = false>
 hipError_t launch_staged(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                          float* scale, hipStream_t stream, int R, int threads) {
     constexpr int ESZ = 16 / In::E;
@@ -447,12 +450,12 @@ hipError_t launch_staged(const void* x, int64_t M, int64_t K, int64_t ldx, int8_
                        (UsesLut<ACT, In16<In>::value>::value ? (size_t)kLutBytes : 0);
     const hipError_t e = build_lut<ACT, In16<In>::value>(stream);
     if (e != hipSuccess) return e;
-    rotquant_kernel<In, ROT, QMAX, STAGE, ACT, F6><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
+    rotquant_kernel<In, ROT, QMAX, STAGE, ACT, F6, SL><<<dim3((unsigned)grid), dim3(threads), lds, stream>>>(
         static_cast<const uint8_t*>(x), ldx * ESZ, (int)M, (int)K, nb, R, q, ldq, scale);
     return hipGetLastError();
 }
 
-template <class In, bool ROT, int QMAX, int ACT = ACT_NONE, bool F6 = false>
+template <class In, bool ROT, int QMAX, int ACT = ACT_NONE, bool F6 = false, bool SL = false>
 hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                         float* scale, hipStream_t stream) {
     const int nb = (int)((K + 255) / 256);
@@ -473,7 +476,8 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     if (F6)
         return launch_staged<In, ROT, QMAX, true, ACT, true>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
     if (ROT)
-        return launch_staged<In, ROT, QMAX, true, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
+        return launch_staged<In, ROT, QMAX, true, ACT, false, SL>(x, M, K, ldx, q, ldq, scale, stream, R,
+                                                                 best_threads);
     return launch_staged<In, ROT, QMAX, false, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
 }
 
@@ -558,6 +562,26 @@ hipError_t launch_act16(const void* x, int64_t n, int act, void* out, hipStream_
 }
 
 }  // namespace
+
+// Rotated INT8 codes in the K-sliced layout (byte (m, k) at (k / 64) * M * 64 + m * 64 + k % 64).
+hipError_t launch_rotquant_sliced(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                  float* scale, hipStream_t stream, int act) {
+    const int64_t plane = M * 64;
+#define QD_SLICED(IN, A) return launch_typed<IN, true, 127, A, false, true>(x, M, K, ldx, q, plane, scale, stream);
+#define QD_SLICED_ACTS(IN)                          \
+    switch (act) {                                  \
+        case ACT_GELU_TANH: QD_SLICED(IN, ACT_GELU_TANH) \
+        case ACT_GELU_ERF: QD_SLICED(IN, ACT_GELU_ERF)   \
+        case ACT_SILU: QD_SLICED(IN, ACT_SILU)           \
+        case ACT_RELU: QD_SLICED(IN, ACT_RELU)           \
+        default: QD_SLICED(IN, ACT_NONE)                 \
+    }
+    if (dtype == 0) QD_SLICED(InF32, ACT_NONE)
+    if (dtype == 1) { QD_SLICED_ACTS(InBF16) }
+    QD_SLICED_ACTS(InF16)
+#undef QD_SLICED
+#undef QD_SLICED_ACTS
+}
 
 hipError_t launch_rotquant_fp6(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q6,
                                int64_t ld6, float* scale, hipStream_t stream) {

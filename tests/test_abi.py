@@ -338,12 +338,24 @@ def test_sliced_weights_validation():
     assert L.qd_int8_slice_weights(NULL, 0, 128, 128, NULL, STREAM) == qd.QD_OK
     assert L.qd_int8_slice_weights(A, -1, 128, 128, A, STREAM) == qd.QD_EINVAL
     # GEMMs: K % 64 (K % 16 alone is not enough for the sliced layout)
-    assert L.qd_int8_scaled_mm_sliced(A, 4, 96, 96, A, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EUNSUPPORTED
-    assert L.qd_int8_gemm_i32_sliced(A, 4, 96, 96, A, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
-    assert L.qd_int8_scaled_mm_sliced(A, 4, 128, 128, NULL, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EINVAL
-    assert L.qd_int8_gemm_i32_sliced(A, 4, 128, 64, A, 8, A, 8, STREAM) == qd.QD_EINVAL
-    assert L.qd_int8_gemm_i32_sliced(A, 4, 128, 128, FAKE_ODD, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
-    assert L.qd_int8_gemm_i32_sliced(A, 0, 128, 128, A, 8, A, 8, STREAM) == qd.QD_OK
+    for a_sl in (0, 1):
+        assert L.qd_int8_scaled_mm_sliced(A, 4, 96, 96, a_sl, A, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+        assert L.qd_int8_gemm_i32_sliced(A, 4, 96, 96, a_sl, A, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+        assert L.qd_int8_scaled_mm_sliced(A, 4, 128, 128, a_sl, NULL, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EINVAL
+        assert L.qd_int8_gemm_i32_sliced(A, 4, 128, 128, a_sl, FAKE_ODD, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+        assert L.qd_int8_gemm_i32_sliced(A, 0, 128, 128, a_sl, A, 8, A, 8, STREAM) == qd.QD_OK
+    # lda matters for row-major codes only
+    assert L.qd_int8_gemm_i32_sliced(A, 4, 128, 64, 0, A, 8, A, 8, STREAM) == qd.QD_EINVAL
+    # the sliced quantizer: rotation block 256, K % 256
+    q = lambda K, blk=256, x=A, dt=qd.QD_BF16, act=qd.ACT_NONE: L.qd_quantize_and_rotate_rowwise_sliced(
+        x, dt, 4, K, K, act, blk, A, A, STREAM)
+    assert q(320) == qd.QD_EUNSUPPORTED
+    assert q(512, blk=0) == qd.QD_EUNSUPPORTED
+    assert q(512, x=NULL) == qd.QD_EINVAL
+    assert q(512, x=FAKE_ODD) == qd.QD_EUNSUPPORTED
+    assert q(512, dt=qd.QD_F32, act=qd.ACT_SILU) == qd.QD_EUNSUPPORTED
+    assert q(512, act=7) == qd.QD_EUNSUPPORTED
+    assert L.qd_quantize_and_rotate_rowwise_sliced(A, qd.QD_BF16, 0, 512, 512, 0, 256, A, A, STREAM) == qd.QD_OK
     # the layer: K % 64 with or without rotation, then the usual checks
     f = lambda K, rb, x=A, w=A, act=qd.ACT_NONE: L.qd_int8_linear_sliced(
         x, qd.QD_BF16, 4, K, K, act, w, 8, A, NULL, rb, ctypes.c_void_p(0x100000), ws, A, 8, STREAM)

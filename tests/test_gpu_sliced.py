@@ -49,16 +49,56 @@ SHAPES = [(1, 1, 64), (256, 256, 64), (257, 255, 128), (70, 130, 128), (300, 520
           (513, 1000, 5376), (64, 4100, 1024)]
 
 
+def _slice_np(a):
+    """[R, K] -> the K-sliced layout [K / 64, R, 64] (numpy reshape)."""
+    R, K = a.shape
+    return np.ascontiguousarray(a.reshape(R, K // 64, 64).transpose(1, 0, 2))
+
+
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_sliced_gemm_i32_exact(qd, O, tiles, M, N, K):
+    """K-sliced weights with row-major and with K-sliced activation codes."""
     say(f"sliced gemm i32 M={M} N={N} K={K} tiles={tiles}")
     a = _codes((M, K), M * 7 + N * 3 + K)
     w = _codes((N, K), M * 5 + N * 11 + K)
     wd = to_dev(w)
-    acc = qd.int8_gemm_i32_sliced(to_dev(a), qd.slice_weights(wd))
+    wsl = qd.slice_weights(wd)
     ref = O.gemm_i32(a, w)
-    assert np.array_equal(host(acc), ref)
+    assert np.array_equal(host(qd.int8_gemm_i32_sliced(to_dev(a), wsl)), ref)
+    assert np.array_equal(host(qd.int8_gemm_i32_sliced(to_dev(_slice_np(a)), wsl)), ref)
     assert np.array_equal(host(qd.int8_gemm_i32(to_dev(a), wd)), ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 512), (63, 768), (257, 5376), (130, 7168), (1000, 1024)])
+def test_quantize_sliced(qd, O, dtype, M, K):
+    """The rotating quantizer writing K-sliced codes: the oracle's codes re-laid out, same scales."""
+    say(f"sliced rotquant {dtype} M={M} K={K}")
+    g = np.random.Generator(np.random.PCG64(40 + M + K))
+    xf = g.standard_normal((M, K), dtype=np.float32)
+    if dtype == "bf16":
+        from synth import f32_to_bf16_bits
+        x = f32_to_bf16_bits(xf)
+        xd = to_dev_bf16(x)
+    else:
+        x = xf if dtype == "f32" else xf.astype(np.float16)
+        xd = to_dev(x)
+    q, s = qd.quantize_and_rotate_rowwise_sliced(xd)
+    qo, so = O.quantize_rowwise(x, dtype, 256)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), _slice_np(qo))
+
+
+@pytest.mark.parametrize("act", [1, 2, 3, 4])
+def test_quantize_sliced_act(qd, O, act):
+    from synth import f32_to_bf16_bits
+    say(f"sliced rotquant act={act}")
+    g = np.random.Generator(np.random.PCG64(70 + act))
+    x = f32_to_bf16_bits(g.standard_normal((77, 1280), dtype=np.float32) * 3)
+    q, s = qd.quantize_and_rotate_rowwise_sliced(to_dev_bf16(x), input_act=act)
+    qo, so = O.quantize_rowwise(x, "bf16", 256, act=act)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), _slice_np(qo))
 
 
 def test_sliced_gemm_i32_extremes(qd, O, tiles):
@@ -87,11 +127,15 @@ def test_sliced_scaled_mm(qd, O, tiles, M, N, K, with_bias):
     bb = f32_to_bf16_bits(b) if with_bias else None
     bd = to_dev_bf16(bb) if with_bias else None
     wd = to_dev(w)
-    y = qd.int8_scaled_mm_sliced(to_dev(a), to_dev(sx), qd.slice_weights(wd), to_dev(sw), bd)
+    wsl = qd.slice_weights(wd)
+    y = qd.int8_scaled_mm_sliced(to_dev(a), to_dev(sx), wsl, to_dev(sw), bd)
     yo = O.epilogue(O.gemm_i32(a, w), sx, sw, bb)
     assert_bf16_within_1ulp(bf16_bits(y), yo, "scaled_mm_sliced")
     y_rm = qd.int8_scaled_mm(to_dev(a), to_dev(sx), wd, to_dev(sw), bd)
     assert torch.equal(y, y_rm)
+    if K % 64 == 0:
+        y_as = qd.int8_scaled_mm_sliced(to_dev(_slice_np(a)), to_dev(sx), wsl, to_dev(sw), bd)
+        assert torch.equal(y_as, y_rm)
 
 
 @pytest.mark.parametrize("act", [0, 1, 3])
