@@ -153,7 +153,7 @@ def main():
                     help="linear: the whole layer (default); tensorwise: quantize_int8_tensorwise on the "
                          "workload's activations; attention: int8_attention on 40 heads x 16384 tokens x 128")
     ap.add_argument("--row-major-weights", action="store_true",
-                    help="INT8 layer on row-major weight codes (int8_linear) instead of the K-sliced layout")
+                    help="row-major operands (int8_linear, convrot_w4a4_linear_fp6) instead of the K-sliced layout")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -209,16 +209,21 @@ def main():
     else:
         wq, sw = qd.prepare_weights_w4a4(Wf) if int4 else qd.prepare_weights(Wf)
     del Wf
-    # INT8 weights in the K-sliced layout (also offline), unless asked for the row-major path
+    # weights in the K-sliced layout (also offline), unless asked for the row-major path:
+    # INT8 weights, or the FP6 operand of the W4A4 layer
     sliced = not int4 and not args.row_major_weights and K % 64 == 0
     wsl = qd.slice_weights(wq) if sliced else None
+    sliced6 = fp6 and not args.row_major_weights
+    w6s = qd.fp6_slice_weights(wq, K) if sliced6 else None
     ws = torch.empty(qd.w4a4_fp6_workspace_size(M, K) if fp6 else qd.workspace_size(M, K), dtype=torch.uint8,
                      device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
     def step():
-        if fp6:
+        if sliced6:
+            qd.convrot_w4a4_linear_fp6_sliced(x, w6s, sw, bias, 256, ws, y)
+        elif fp6:
             qd.convrot_w4a4_linear_fp6(x, wq, sw, bias, 256, ws, y)
         elif int4:
             qd.convrot_w4a4_linear(x, wq, sw, bias, 256, ws, y)
@@ -252,7 +257,11 @@ def main():
     sx = torch.empty(M, dtype=torch.float32, device=dev)
     y2 = torch.empty_like(y)
     reps = max(5, args.steps)
-    if fp6:
+    if sliced6:
+        a6s = torch.empty((K // 128, M, 96), dtype=torch.uint8, device=dev)
+        ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_fp6_sliced(x, 256, a6s, sx), reps, torch)
+        ms_g = time_launches(lambda: qd.fp6_scaled_mm_sliced(a6s, sx, w6s, sw, bias, y2), reps, torch)
+    elif fp6:
         a6 = torch.empty((M, K // 4 * 3), dtype=torch.uint8, device=dev)
         ms_q = time_launches(lambda: qd.quantize_and_rotate_rowwise_fp6(x, 256, a6, sx), reps, torch)
         ms_g = time_launches(lambda: qd.fp6_scaled_mm(a6, sx, wq, sw, K, bias, y2), reps, torch)
@@ -275,7 +284,8 @@ def main():
     g_min_bytes = float((M * K * 3 // 4 + N * K * 3 // 4) if fp6 else (M * K + (N * K // 2 if int4 else N * K))) \
         + 2 * M * N + 4 * M + 4 * N + 2 * N
     gemm_tops = ops / (ms_g * 1e-3) / 1e12
-    traffic = load_traffic(w.name + (" (FP6)" if fp6 else " (row-major weights)" if not int4 and not sliced else ""))
+    traffic = load_traffic(w.name + (" (FP6, K-sliced)" if sliced6 else " (FP6)" if fp6 else
+                                     " (row-major weights)" if not int4 and not sliced else ""))
     out = {
         "metric": (f"W4A4 rotated linear TOPS on the FP6 matrix path (incl. rotate+quant) & % of INT8 MFMA "
                    f"peak, M{M}/K{K}/N{N}" if fp6 else
@@ -302,7 +312,8 @@ def main():
                                else "int8 per-channel fp32 scale, row-major"),
                    "bias": "bf16", "output": "bf16", "parallelism": "single GPU"},
         "frac_of_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": ("gemm_f6_w8_kernel<MODE_BF16>" if fp6 else
+        "roofline": {"bound": "mfma", "kernel": ("gemm_f6_w8_kernel<MODE_BF16> (K-sliced operands)" if sliced6 else
+                                                 "gemm_f6_w8_kernel<MODE_BF16>" if fp6 else
                                                  "gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4>" if int4 else
                                                  "gemm_i8_w12_kernel<MODE_BF16> (256x384 tiles)"
                                                  if qd.int8_gemm_tiles(M, N, K) == qd.GEMM_TILES_256x384 else
@@ -320,7 +331,8 @@ def main():
                      "frac_of_int8_peak": round(gemm_tops / PEAK_INT8_TOPS, 4),
                      "min_hbm_bytes": g_min_bytes},
             "separate_launch_output_identical": same,
-            "quantizer_writes": "fp6 operand format" if fp6 else "int8 codes, K-sliced" if sliced else "int8 codes",
+            "quantizer_writes": ("fp6 operand format, K-sliced" if sliced6 else "fp6 operand format" if fp6 else
+                                 "int8 codes, K-sliced" if sliced else "int8 codes"),
         },
         "device": torch.cuda.get_device_name(0),
         "wall_s_timed_region": round(t_wall, 4),

@@ -480,6 +480,42 @@ qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_
                                        const void* bias_bf16, int32_t rotate_block, void* workspace,
                                        size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream);
 
+/*
+ * K-sliced FP6 operands (the FP6 counterpart of the K-sliced INT8 layout
+ * above): byte b of row r of an FP6 operand ([R, 3K/4] bytes, K % 128 == 0)
+ * stored at (b / 96) * R * 96 + r * 96 + b % 96, i.e. the 96-byte slices
+ * of 128 values of all rows one after another (R * 3K/4 bytes).  Row-major
+ * FP6 rows are 96 bytes per slice and straddle 128-byte lines; K-sliced,
+ * a copy instruction of the GEMM reads 1 KB of consecutive bytes.  Same
+ * values, same results as the row-major entry points, bit for bit.
+ *
+ * qd_fp6_slice_weights: w6 [N, 3K/4] row-major (row stride ldw bytes, a
+ * multiple of 16) -> w6_sliced (caller-owned, 16-byte aligned).
+ * qd_quantize_and_rotate_rowwise_fp6_sliced: as qd_quantize_and_rotate_rowwise_fp6
+ * with the K-sliced output (BF16 or FP16 input, K % 256 == 0).
+ * qd_fp6_scaled_mm_sliced / qd_fp6_gemm_i32_sliced: as qd_fp6_scaled_mm /
+ * qd_fp6_gemm_i32 with K-sliced weights; a6 row-major with row stride lda
+ * (a_sliced == 0) or K-sliced (a_sliced != 0, lda ignored).
+ * qd_convrot_w4a4_linear_fp6_sliced: the layer with K-sliced weights, its
+ * quantizer writing the activation operand K-sliced into the workspace
+ * (same size as qd_w4a4_fp6_workspace_size); BF16 or FP16 input only.
+ */
+qd_status_t qd_fp6_slice_weights(const uint8_t* w6, int64_t N, int64_t K, int64_t ldw, uint8_t* w6_sliced,
+                                 hipStream_t stream);
+qd_status_t qd_quantize_and_rotate_rowwise_fp6_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                                      int64_t ldx, int32_t block, uint8_t* q6_sliced,
+                                                      float* row_scale, hipStream_t stream);
+qd_status_t qd_fp6_scaled_mm_sliced(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
+                                    const float* a_scale, const uint8_t* w6_sliced, int64_t N, const float* w_scale,
+                                    const void* bias_bf16, void* y_bf16, int64_t ldy, hipStream_t stream);
+qd_status_t qd_fp6_gemm_i32_sliced(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
+                                   const uint8_t* w6_sliced, int64_t N, int32_t* acc, int64_t ldc,
+                                   hipStream_t stream);
+qd_status_t qd_convrot_w4a4_linear_fp6_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                              const uint8_t* w6_sliced, int64_t N, const float* w_scale,
+                                              const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                              size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,8 @@ __all__ = [
     "quantize_and_rotate_rowwise_fp6", "set_gemm_tiles", "int8_gemm_tiles", "GEMM_TILES_AUTO", "GEMM_TILES_256x256",
     "GEMM_TILES_256x384", "int8_attention", "attention_workspace_size", "int8_attention_codes",
     "slice_weights", "int8_linear_sliced", "int8_scaled_mm_sliced", "int8_gemm_i32_sliced",
-    "quantize_and_rotate_rowwise_sliced",
+    "quantize_and_rotate_rowwise_sliced", "fp6_slice_weights", "quantize_and_rotate_rowwise_fp6_sliced",
+    "fp6_scaled_mm_sliced", "fp6_gemm_i32_sliced", "convrot_w4a4_linear_fp6_sliced",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -60,7 +61,8 @@ EXPORTED_SYMBOLS = (
     "qd_quantize_and_rotate_rowwise_fp6", "qd_set_gemm_tiles", "qd_int8_gemm_tiles",
     "qd_int8_attention_workspace_size", "qd_int8_attention", "qd_int8_attention_codes",
     "qd_int8_slice_weights", "qd_int8_linear_sliced", "qd_int8_scaled_mm_sliced", "qd_int8_gemm_i32_sliced",
-    "qd_quantize_and_rotate_rowwise_sliced",
+    "qd_quantize_and_rotate_rowwise_sliced", "qd_fp6_slice_weights", "qd_quantize_and_rotate_rowwise_fp6_sliced",
+    "qd_fp6_scaled_mm_sliced", "qd_fp6_gemm_i32_sliced", "qd_convrot_w4a4_linear_fp6_sliced",
 )
 
 
@@ -153,6 +155,16 @@ def lib():
         L.qd_quantize_and_rotate_rowwise_sliced.argtypes = [P, St, I64, I64, I64, St, I32, P, P, P]
         L.qd_int8_gemm_i32_sliced.restype = St
         L.qd_int8_gemm_i32_sliced.argtypes = [P, I64, I64, I64, I32, P, I64, P, I64, P]
+        L.qd_fp6_slice_weights.restype = St
+        L.qd_fp6_slice_weights.argtypes = [P, I64, I64, I64, P, P]
+        L.qd_quantize_and_rotate_rowwise_fp6_sliced.restype = St
+        L.qd_quantize_and_rotate_rowwise_fp6_sliced.argtypes = [P, St, I64, I64, I64, I32, P, P, P]
+        L.qd_fp6_scaled_mm_sliced.restype = St
+        L.qd_fp6_scaled_mm_sliced.argtypes = [P, I64, I64, I64, I32, P, P, I64, P, P, P, I64, P]
+        L.qd_fp6_gemm_i32_sliced.restype = St
+        L.qd_fp6_gemm_i32_sliced.argtypes = [P, I64, I64, I64, I32, P, I64, P, I64, P]
+        L.qd_convrot_w4a4_linear_fp6_sliced.restype = St
+        L.qd_convrot_w4a4_linear_fp6_sliced.argtypes = [P, St, I64, I64, I64, P, I64, P, P, I32, P, SZ, P, I64, P]
         _lib = L
     return _lib
 
@@ -721,6 +733,109 @@ def convrot_w4a4_linear_fp6(x, w6, w_scale, bias=None, rotate_block: int = 256, 
                                             _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
                                             _stream(dev)))
+    return out
+
+
+def _f6_sliced(w, name="w6_sliced"):
+    """(K, R) of a K-sliced FP6 operand: a contiguous uint8 tensor [K / 128, R, 96]."""
+    torch = _torch()
+    if w.dtype != torch.uint8 or w.dim() != 3 or w.shape[2] != 96 or not w.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor [K / 128, R, 96] (K-sliced FP6)")
+    return w.shape[0] * 128, w.shape[1]
+
+
+def fp6_slice_weights(w6, K: int, out=None):
+    """Row-major FP6 weights w6 [N, 3K/4] (K % 128 == 0) -> the K-sliced layout
+    uint8 [K / 128, N, 96], element [u, n, j] = w6[n, 96 u + j].  Offline."""
+    torch = _torch()
+    _mat(w6, "w6")
+    dev = _dev(w6, out)
+    N = w6.shape[0]
+    if out is None:
+        out = torch.empty((max(K // 128, 0), N, 96), dtype=torch.uint8, device=dev)
+    _check(lib().qd_fp6_slice_weights(_ptr(w6), N, K, w6.stride(0), _ptr(out), _stream(dev)))
+    return out
+
+
+def quantize_and_rotate_rowwise_fp6_sliced(x, block: int = 256, out_q6=None, out_scale=None):
+    """quantize_and_rotate_rowwise_fp6 with the K-sliced FP6 output: (uint8 [K / 128, M, 96], fp32 [M])."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, out_q6, out_scale)
+    M, K = x.shape
+    if out_q6 is None:
+        out_q6 = torch.empty((max(K // 128, 0), M, 96), dtype=torch.uint8, device=dev)
+    if out_scale is None:
+        out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _check(lib().qd_quantize_and_rotate_rowwise_fp6_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), block,
+                                                           _ptr(out_q6), _ptr(out_scale), _stream(dev)))
+    return out_q6, out_scale
+
+
+def _f6_a_operand(a6, K):
+    """(M, lda, a_sliced) of an FP6 activation operand: row-major [M, 3K/4] or K-sliced [K / 128, M, 96]."""
+    if a6.dim() == 3:
+        Ka, M = _f6_sliced(a6, "a6")
+        if Ka != K:
+            raise ValueError("a6 and w6_sliced disagree on K")
+        return M, K // 4 * 3, 1
+    _mat(a6, "a6")
+    return a6.shape[0], a6.stride(0), 0
+
+
+def fp6_scaled_mm_sliced(a6, a_scale, w6_sliced, w_scale, bias=None, out=None):
+    """fp6_scaled_mm with K-sliced FP6 weights (a6 row-major or K-sliced): identical results."""
+    torch = _torch()
+    dev = _dev(a6, a_scale, w6_sliced, w_scale, bias, out)
+    K, N = _f6_sliced(w6_sliced)
+    M, lda, a_sl = _f6_a_operand(a6, K)
+    _rows_vec(a_scale, M, torch.float32, "a_scale")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_fp6_scaled_mm_sliced(_ptr(a6), M, K, lda, a_sl, _ptr(a_scale), _ptr(w6_sliced), N, _ptr(w_scale),
+                                         _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
+def fp6_gemm_i32_sliced(a6, w6_sliced, out=None):
+    """fp6_gemm_i32 with K-sliced FP6 weights: identical exact sums."""
+    torch = _torch()
+    dev = _dev(a6, w6_sliced, out)
+    K, N = _f6_sliced(w6_sliced)
+    M, lda, a_sl = _f6_a_operand(a6, K)
+    if out is None:
+        out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
+    _check(lib().qd_fp6_gemm_i32_sliced(_ptr(a6), M, K, lda, a_sl, _ptr(w6_sliced), N, _ptr(out), out.stride(0),
+                                        _stream(dev)))
+    return out
+
+
+def convrot_w4a4_linear_fp6_sliced(x, w6_sliced, w_scale, bias=None, rotate_block: int = 256, workspace=None,
+                                   out=None):
+    """convrot_w4a4_linear_fp6 with K-sliced FP6 weights (fp6_slice_weights): identical results."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, w6_sliced, w_scale, bias, workspace, out)
+    M, K = x.shape
+    Kw, N = _f6_sliced(w6_sliced)
+    if Kw != K:
+        raise ValueError("x and w6_sliced disagree on K")
+    _rows_vec(w_scale, N, torch.float32, "w_scale")
+    if bias is not None:
+        _rows_vec(bias, N, torch.bfloat16, "bias")
+    if workspace is None:
+        workspace = torch.empty(max(w4a4_fp6_workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = _bf16_out(M, N, dev)
+    _mat(out, "out")
+    _check(lib().qd_convrot_w4a4_linear_fp6_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(w6_sliced), N,
+                                                   _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
+                                                   workspace.numel() * workspace.element_size(), _ptr(out),
+                                                   out.stride(0), _stream(dev)))
     return out
 
 

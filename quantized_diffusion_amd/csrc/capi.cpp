@@ -627,14 +627,15 @@ size_t qd_w4a4_fp6_workspace_size(int64_t M, int64_t K) {
     return ws_codes_bytes(M, K) + round_up((size_t)M * (size_t)f6_ld(K), kAlign) + round_up((size_t)M * sizeof(float), kAlign);
 }
 
-qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
-                                       const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale,
-                                       const void* bias_bf16, int32_t rotate_block, void* workspace,
-                                       size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream) {
-    const char* fn = "qd_convrot_w4a4_linear_fp6";
+static qd_status_t w4a4_fp6_impl(const char* fn, const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                 int64_t ldx, const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale,
+                                 const void* bias_bf16, int32_t rotate_block, void* workspace, size_t workspace_bytes,
+                                 void* y_bf16, int64_t ldy, hipStream_t stream, bool sliced) {
     if (rotate_block != 256) return fail(QD_EUNSUPPORTED, fn, "rotate_block must be 256 (got %d)", rotate_block);
     if (M < 0 || N < 0 || K <= 0)
         return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
+    if (sliced && x_dtype != QD_BF16 && x_dtype != QD_F16)
+        return fail(QD_EUNSUPPORTED, fn, "K-sliced FP6 operands need a BF16 or FP16 input");
     if (M == 0 || N == 0) return ok();
     if (!workspace) return fail(QD_EINVAL, fn, "null workspace");
     if ((uintptr_t)workspace % kAlign) return fail(QD_EUNSUPPORTED, fn, "workspace must be 256-byte aligned");
@@ -648,22 +649,90 @@ qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_
     float* sx = reinterpret_cast<float*>(ws + ws_codes_bytes(M, K) + round_up((size_t)M * (size_t)lda6, kAlign));
     qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, true, rotate_block, aq, ldq, sx);
     if (st != QD_OK) return st;
-    st = check_f6(fn, a6, M, K, lda6, w6, N, ldw, y_bf16, ldy, 8);
+    st = check_f6(fn, a6, M, K, lda6, w6, N, sliced ? K / 4 * 3 : ldw, y_bf16, ldy, 8);
     if (st != QD_OK) return st;
     if (!w_scale) return fail(QD_EINVAL, fn, "null w_scale");
     if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
         return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
     hipError_t e;
     if (x_dtype == QD_BF16 || x_dtype == QD_F16) {
-        // 16-bit inputs: the quantizer writes the FP6 operand format itself
-        e = qd::launch_rotquant_fp6(x, (int)x_dtype, M, K, ldx, a6, lda6, sx, stream);
+        // 16-bit inputs: the quantizer writes the FP6 operand format itself (K-sliced for the sliced layer)
+        e = qd::launch_rotquant_fp6(x, (int)x_dtype, M, K, ldx, a6, lda6, sx, stream, sliced);
     } else {
         e = qd::launch_rotquant(x, (int)x_dtype, true, 7, M, K, ldx, aq, ldq, sx, stream);
         if (e == hipSuccess) e = qd::launch_pack_fp6(aq, ldq, a6, lda6, M, K, stream);
     }
     if (e != hipSuccess) return hip_status(fn, e);
     return hip_status(fn, qd::launch_gemm_f6_bf16(a6, lda6, sx, w6, ldw, w_scale, bias_bf16, y_bf16, ldy, M, N, K,
-                                                  stream));
+                                                  stream, sliced, sliced));
+}
+
+qd_status_t qd_convrot_w4a4_linear_fp6(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                       const uint8_t* w6, int64_t N, int64_t ldw, const float* w_scale,
+                                       const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                       size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream) {
+    return w4a4_fp6_impl("qd_convrot_w4a4_linear_fp6", x, x_dtype, M, K, ldx, w6, N, ldw, w_scale, bias_bf16,
+                         rotate_block, workspace, workspace_bytes, y_bf16, ldy, stream, false);
+}
+
+qd_status_t qd_convrot_w4a4_linear_fp6_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                                              const uint8_t* w6_sliced, int64_t N, const float* w_scale,
+                                              const void* bias_bf16, int32_t rotate_block, void* workspace,
+                                              size_t workspace_bytes, void* y_bf16, int64_t ldy, hipStream_t stream) {
+    return w4a4_fp6_impl("qd_convrot_w4a4_linear_fp6_sliced", x, x_dtype, M, K, ldx, w6_sliced, N, K / 4 * 3,
+                         w_scale, bias_bf16, rotate_block, workspace, workspace_bytes, y_bf16, ldy, stream, true);
+}
+
+qd_status_t qd_fp6_slice_weights(const uint8_t* w6, int64_t N, int64_t K, int64_t ldw, uint8_t* w6_sliced,
+                                 hipStream_t stream) {
+    const char* fn = "qd_fp6_slice_weights";
+    if (N < 0 || K <= 0) return fail(QD_EINVAL, fn, "need N >= 0 and K > 0 (N=%lld, K=%lld)", (long long)N, (long long)K);
+    if (K % 128 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 128", (long long)K);
+    if (ldw < K / 4 * 3) return fail(QD_EINVAL, fn, "ldw (%lld bytes) < 3K/4", (long long)ldw);
+    if (N == 0) return ok();
+    if (!w6 || !w6_sliced) return fail(QD_EINVAL, fn, "null pointer argument");
+    if (!aligned16(w6) || !aligned16(w6_sliced) || ldw % 16 != 0)
+        return fail(QD_EUNSUPPORTED, fn, "w6, w6_sliced and ldw must be 16-byte aligned");
+    if (N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "N too large");
+    return hip_status(fn, qd::launch_slice_fp6(w6, ldw, N, K, w6_sliced, stream));
+}
+
+qd_status_t qd_quantize_and_rotate_rowwise_fp6_sliced(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                                      int64_t ldx, int32_t block, uint8_t* q6_sliced,
+                                                      float* row_scale, hipStream_t stream) {
+    const char* fn = "qd_quantize_and_rotate_rowwise_fp6_sliced";
+    if (x_dtype != QD_BF16 && x_dtype != QD_F16)
+        return fail(QD_EUNSUPPORTED, fn, "FP6 output needs a BF16 or FP16 input");
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, true, block, reinterpret_cast<int8_t*>(q6_sliced),
+                                 K / 4 * 3, row_scale, K / 4 * 3);
+    if (st != QD_OK) return st;
+    if (K % 128 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 128", (long long)K);
+    if (M == 0) return ok();
+    return hip_status(fn, qd::launch_rotquant_fp6(x, (int)x_dtype, M, K, ldx, q6_sliced, 0, row_scale, stream, true));
+}
+
+qd_status_t qd_fp6_scaled_mm_sliced(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
+                                    const float* a_scale, const uint8_t* w6_sliced, int64_t N, const float* w_scale,
+                                    const void* bias_bf16, void* y_bf16, int64_t ldy, hipStream_t stream) {
+    const char* fn = "qd_fp6_scaled_mm_sliced";
+    qd_status_t st = check_f6(fn, a6, M, K, a_sliced ? K / 4 * 3 : lda, w6_sliced, N, K / 4 * 3, y_bf16, ldy, 8);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    if (!a_scale || !w_scale) return fail(QD_EINVAL, fn, "null scale pointer");
+    if (((uintptr_t)w_scale & 15u) || ((uintptr_t)bias_bf16 & 7u))
+        return fail(QD_EUNSUPPORTED, fn, "w_scale must be 16-byte and bias 8-byte aligned");
+    return hip_status(fn, qd::launch_gemm_f6_bf16(a6, lda, a_scale, w6_sliced, 0, w_scale, bias_bf16, y_bf16, ldy, M,
+                                                  N, K, stream, true, a_sliced != 0));
+}
+
+qd_status_t qd_fp6_gemm_i32_sliced(const uint8_t* a6, int64_t M, int64_t K, int64_t lda, int32_t a_sliced,
+                                   const uint8_t* w6_sliced, int64_t N, int32_t* acc, int64_t ldc,
+                                   hipStream_t stream) {
+    const char* fn = "qd_fp6_gemm_i32_sliced";
+    qd_status_t st = check_f6(fn, a6, M, K, a_sliced ? K / 4 * 3 : lda, w6_sliced, N, K / 4 * 3, acc, ldc, 4);
+    if (st != QD_OK) return st;
+    if (M == 0 || N == 0) return ok();
+    return hip_status(fn, qd::launch_gemm_f6_i32(a6, lda, w6_sliced, 0, acc, ldc, M, N, K, stream, true, a_sliced != 0));
 }
 
 }  // extern "C"

@@ -919,8 +919,8 @@ __device__ __forceinline__ u32x2 epi_bf16x4_f(const float* a4, float sx, const f
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __restrict__ A, int64_t lda,
-                                                           const uint8_t* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __restrict__ A, int64_t lda, int64_t a_ss,
+                                                           const uint8_t* __restrict__ W, int64_t ldw, int64_t w_ss,
                                                            int M, int N, int K, EpiArgs ep) {
     constexpr int NS = F6_NS;
     constexpr int STG = F6_STG;
@@ -982,8 +982,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
         const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
-        if (part == 0) dma16(sb + lslot[i], reinterpret_cast<const int8_t*>(ga[i] + (int64_t)u * F6_RB));
-        else dma16(sb + BM * F6_RB + lslot[i], reinterpret_cast<const int8_t*>(gw[i] + (int64_t)u * F6_RB));
+        if (part == 0) dma16(sb + lslot[i], reinterpret_cast<const int8_t*>(ga[i] + (int64_t)u * a_ss));
+        else dma16(sb + BM * F6_RB + lslot[i], reinterpret_cast<const int8_t*>(gw[i] + (int64_t)u * w_ss));
     };
     auto issue = [&](int u) {
 #pragma unroll
@@ -1202,16 +1202,28 @@ hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, 
     return hipGetLastError();
 }
 
-// 16-byte chunk o of the K-sliced copy: slice o / (4N), row (o / 4) % N, quarter o % 4.
-__global__ __launch_bounds__(256) void slice_weights_kernel(const int8_t* __restrict__ wq, int64_t ldw, int64_t N,
-                                                            int64_t chunks, int8_t* __restrict__ out) {
+// 16-byte chunk o of a K-sliced copy with slices of SB bytes per row:
+// slice o / (R * SB / 16), row (o / (SB / 16)) % R, piece o % (SB / 16).
+template <int SB>
+__global__ __launch_bounds__(256) void slice_rows_kernel(const uint8_t* __restrict__ src, int64_t ld, int64_t R,
+                                                         int64_t chunks, uint8_t* __restrict__ out) {
+    constexpr int CPR = SB / 16;
     for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < chunks; o += (int64_t)gridDim.x * 256) {
-        const int64_t u = o / (4 * N);
-        const int64_t r = o - u * 4 * N;
-        const int64_t n = r >> 2;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(wq + n * ldw + u * BK + (r & 3) * 16);
+        const int64_t u = o / (CPR * R);
+        const int64_t r = o - u * CPR * R;
+        const int64_t row = r / CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + row * ld + u * SB + (r - row * CPR) * 16);
         *reinterpret_cast<u32x4*>(out + o * 16) = v;
     }
+}
+
+template <int SB>
+hipError_t launch_slice_rows(const uint8_t* src, int64_t ld, int64_t R, int64_t nslices, uint8_t* out,
+                             hipStream_t stream) {
+    const int64_t chunks = nslices * R * (SB / 16);
+    const int64_t blocks = (chunks + 255) / 256 < 65536 ? (chunks + 255) / 256 : 65536;
+    slice_rows_kernel<SB><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(src, ld, R, chunks, out);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1237,10 +1249,12 @@ hipError_t launch_gemm_i32(const int8_t* aq, int64_t lda, const int8_t* wq, int6
 
 hipError_t launch_slice_weights(const int8_t* wq, int64_t ldw, int64_t N, int64_t K, int8_t* out,
                                 hipStream_t stream) {
-    const int64_t chunks = K / BK * N * 4;
-    const int64_t blocks = (chunks + 255) / 256 < 65536 ? (chunks + 255) / 256 : 65536;
-    slice_weights_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(wq, ldw, N, chunks, out);
-    return hipGetLastError();
+    return launch_slice_rows<BK>(reinterpret_cast<const uint8_t*>(wq), ldw, N, K / BK, reinterpret_cast<uint8_t*>(out),
+                                 stream);
+}
+
+hipError_t launch_slice_fp6(const uint8_t* w6, int64_t ldw, int64_t N, int64_t K, uint8_t* out, hipStream_t stream) {
+    return launch_slice_rows<F6_RB>(w6, ldw, N, K / F6_BK, out, stream);
 }
 
 // Packed-INT4 weights (K % 64 == 0): five 24 KB stages, four slices in flight.
@@ -1255,22 +1269,27 @@ hipError_t launch_gemm_w4_bf16(const int8_t* aq, int64_t lda, const float* a_sca
     return hipGetLastError();
 }
 
+// FP6 operands row-major (row stride ld bytes) or K-sliced (96-byte slices,
+// byte (r, b) at (b / 96) * R * 96 + r * 96 + b % 96).
 hipError_t launch_gemm_f6_bf16(const uint8_t* a6, int64_t lda, const float* a_scale, const uint8_t* w6,
                                int64_t ldw, const float* w_scale, const void* bias, void* y, int64_t ldy,
-                               int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream, bool w_sliced, bool a_sliced) {
     EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, 1, 1};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_f6_w8_kernel<MODE_BF16><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(a6, lda, w6, ldw, (int)M, (int)N,
-                                                                                  (int)K, ep);
+    gemm_f6_w8_kernel<MODE_BF16><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+        a6, a_sliced ? F6_RB : lda, a_sliced ? M * F6_RB : F6_RB, w6, w_sliced ? F6_RB : ldw,
+        w_sliced ? N * F6_RB : F6_RB, (int)M, (int)N, (int)K, ep);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_f6_i32(const uint8_t* a6, int64_t lda, const uint8_t* w6, int64_t ldw, int32_t* acc,
-                              int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream, bool w_sliced,
+                              bool a_sliced) {
     EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_f6_w8_kernel<MODE_I32><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(a6, lda, w6, ldw, (int)M, (int)N,
-                                                                                 (int)K, ep);
+    gemm_f6_w8_kernel<MODE_I32><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+        a6, a_sliced ? F6_RB : lda, a_sliced ? M * F6_RB : F6_RB, w6, w_sliced ? F6_RB : ldw,
+        w_sliced ? N * F6_RB : F6_RB, (int)M, (int)N, (int)K, ep);
     return hipGetLastError();
 }
 

@@ -20,8 +20,9 @@ hipError_t launch_rotquant(const void* x, int dtype, bool rotate, int qmax, int6
 // at (k / 64) * M * 64 + m * 64 + k % 64), K % 256 == 0; act as launch_rotquant.
 hipError_t launch_rotquant_sliced(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                   float* scale, hipStream_t stream, int act);
+// sliced: q6 in the K-sliced FP6 layout (96-byte slices, ld6 unused).
 hipError_t launch_rotquant_fp6(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q6,
-                               int64_t ld6, float* scale, hipStream_t stream);
+                               int64_t ld6, float* scale, hipStream_t stream, bool sliced = false);
 
 // out[i] = act(x[i]) rounded to the 16-bit input type (dtype 1 BF16, 2 FP16).
 hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* out, hipStream_t stream);
@@ -82,11 +83,18 @@ hipError_t launch_pack_fp6(const int8_t* q, int64_t ldq, uint8_t* out, int64_t l
 
 // FP6-operand GEMM (K % 128 == 0): a6 [M, 3K/4] and w6 [N, 3K/4] bytes in the FP6
 // operand format; BF16 output with the usual epilogue, or exact INT32 sums.
+// w_sliced / a_sliced: that operand in the K-sliced FP6 layout (96-byte
+// slices of 128 values: byte (r, b) at (b / 96) * R * 96 + r * 96 + b % 96;
+// its ld unused).
 hipError_t launch_gemm_f6_bf16(const uint8_t* a6, int64_t lda, const float* a_scale, const uint8_t* w6,
                                int64_t ldw, const float* w_scale, const void* bias, void* y, int64_t ldy,
-                               int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                               int64_t M, int64_t N, int64_t K, hipStream_t stream, bool w_sliced = false,
+                               bool a_sliced = false);
 hipError_t launch_gemm_f6_i32(const uint8_t* a6, int64_t lda, const uint8_t* w6, int64_t ldw, int32_t* acc,
-                              int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                              int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                              bool w_sliced = false, bool a_sliced = false);
+// Row-major FP6 operand [R, 3K/4] (row stride ld bytes) -> K-sliced (R * 3K/4 bytes), K % 128 == 0.
+hipError_t launch_slice_fp6(const uint8_t* w6, int64_t ldw, int64_t N, int64_t K, uint8_t* out, hipStream_t stream);
 
 // out = q * scale (per row or per tensor) as FP32 (out_bf16 = false) or BF16.
 hipError_t launch_dequant(const int8_t* q, int64_t ldq, const float* scale, bool per_row,

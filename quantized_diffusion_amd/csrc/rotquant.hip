@@ -331,7 +331,10 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
             const int rl2 = (int)(__umul24((uint32_t)qq, nb_inv) >> 20);
             const int row2 = blockIdx.x * R + rl2;
             if (rl2 < R && row2 < M) {
-                int8_t* dst = q + (int64_t)row2 * ldq + (qq - rl2 * nb) * 192 + 16 * (sl % 12);
+                // SL: K-sliced FP6 operand, 96-byte slices, ldq = the slice stride (M * 96 bytes)
+                const int blk2 = qq - rl2 * nb, kb = 16 * (sl % 12);
+                int8_t* dst = SL ? q + (int64_t)(2 * blk2 + kb / 96) * ldq + (int64_t)row2 * 96 + kb % 96
+                                 : q + (int64_t)row2 * ldq + blk2 * 192 + kb;
                 store_codes(val[j], dst);
             }
         }
@@ -474,7 +477,7 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
     if (best_threads > MAXT) return hipErrorInvalidValue;   // rows longer than the caller's checks allow
     if (F6)
-        return launch_staged<In, ROT, QMAX, true, ACT, true>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
+        return launch_staged<In, ROT, QMAX, true, ACT, true, SL>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
     if (ROT)
         return launch_staged<In, ROT, QMAX, true, ACT, false, SL>(x, M, K, ldx, q, ldq, scale, stream, R,
                                                                  best_threads);
@@ -584,8 +587,13 @@ hipError_t launch_rotquant_sliced(const void* x, int dtype, int64_t M, int64_t K
 }
 
 hipError_t launch_rotquant_fp6(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* q6,
-                               int64_t ld6, float* scale, hipStream_t stream) {
+                               int64_t ld6, float* scale, hipStream_t stream, bool sliced) {
     int8_t* q = reinterpret_cast<int8_t*>(q6);
+    if (sliced) {
+        const int64_t plane = M * 96;
+        if (dtype == 1) return launch_typed<InBF16, true, 7, ACT_NONE, true, true>(x, M, K, ldx, q, plane, scale, stream);
+        return launch_typed<InF16, true, 7, ACT_NONE, true, true>(x, M, K, ldx, q, plane, scale, stream);
+    }
     if (dtype == 1) return launch_typed<InBF16, true, 7, ACT_NONE, true>(x, M, K, ldx, q, ld6, scale, stream);
     return launch_typed<InF16, true, 7, ACT_NONE, true>(x, M, K, ldx, q, ld6, scale, stream);
 }

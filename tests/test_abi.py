@@ -380,3 +380,29 @@ def test_sliced_python_shape_checks():
     with pytest.raises(ValueError):
         qd._sliced(torch.zeros(8, 4, 64, dtype=torch.int8).transpose(0, 1))
     assert qd._sliced(torch.zeros(3, 5, 64, dtype=torch.int8)) == (192, 5)
+
+
+def test_fp6_sliced_validation():
+    """K-sliced FP6 entry points: argument checks before any device work."""
+    L = qd.lib()
+    A = FAKE
+    ws = ctypes.c_size_t(1 << 30)
+    assert L.qd_fp6_slice_weights(A, 8, 192, 144, A, STREAM) == qd.QD_EUNSUPPORTED      # K % 128
+    assert L.qd_fp6_slice_weights(A, 8, 256, 96, A, STREAM) == qd.QD_EINVAL             # ldw < 3K/4
+    assert L.qd_fp6_slice_weights(NULL, 8, 256, 192, A, STREAM) == qd.QD_EINVAL
+    assert L.qd_fp6_slice_weights(FAKE_ODD, 8, 256, 192, A, STREAM) == qd.QD_EUNSUPPORTED
+    assert L.qd_fp6_slice_weights(NULL, 0, 256, 192, NULL, STREAM) == qd.QD_OK
+    q = lambda K, dt=qd.QD_BF16, blk=256: L.qd_quantize_and_rotate_rowwise_fp6_sliced(A, dt, 4, K, K, blk, A, A, STREAM)
+    assert q(512, dt=qd.QD_F32) == qd.QD_EUNSUPPORTED
+    assert q(384) == qd.QD_EUNSUPPORTED                                                  # K % 256 for the rotation
+    assert q(512, blk=0) == qd.QD_EUNSUPPORTED
+    for a_sl in (0, 1):
+        assert L.qd_fp6_gemm_i32_sliced(A, 4, 192, 144, a_sl, A, 8, A, 8, STREAM) == qd.QD_EUNSUPPORTED
+        assert L.qd_fp6_gemm_i32_sliced(A, 0, 256, 192, a_sl, A, 8, A, 8, STREAM) == qd.QD_OK
+        assert L.qd_fp6_scaled_mm_sliced(A, 4, 256, 192, a_sl, NULL, A, 8, A, NULL, A, 8, STREAM) == qd.QD_EINVAL
+    assert L.qd_fp6_gemm_i32_sliced(A, 4, 256, 96, 0, A, 8, A, 8, STREAM) == qd.QD_EINVAL  # lda < 3K/4 (row-major a6)
+    f = lambda dt, K=512, rb=256: L.qd_convrot_w4a4_linear_fp6_sliced(A, dt, 4, K, K, A, 8, A, NULL, rb,
+                                                                    ctypes.c_void_p(0x100000), ws, A, 8, STREAM)
+    assert f(qd.QD_F32) == qd.QD_EUNSUPPORTED
+    assert f(qd.QD_BF16, rb=0) == qd.QD_EUNSUPPORTED
+    assert f(qd.QD_BF16, K=384) == qd.QD_EUNSUPPORTED

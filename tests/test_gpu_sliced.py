@@ -203,3 +203,112 @@ def test_int8_linear_sliced_full_size(qd, O):
     yo, _ = O.linear_points(qo, so, rows, wqo, swo, b, cols)
     yg = bf16_bits(y[torch.from_numpy(rows).to(dev), torch.from_numpy(cols).to(dev)])
     assert_bf16_within_1ulp(yg, yo, "sliced full size")
+
+
+# ----------------------------------------------------------- K-sliced FP6
+
+def _slice96(b):
+    """Row-major FP6 bytes [R, 3K/4] -> the K-sliced layout [K / 128, R, 96]."""
+    R, B = b.shape
+    return np.ascontiguousarray(b.reshape(R, B // 96, 96).transpose(1, 0, 2))
+
+
+def _int4(shape, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.integers(-7, 8, shape, dtype=np.int64).astype(np.int8)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (255, 384), (384, 5376), (1000, 1024)])
+def test_fp6_slice_weights_layout(qd, O, N, K):
+    say(f"fp6 slice N={N} K={K}")
+    w4 = _int4((N, K), 300 + N + K)
+    w6 = qd.pack_fp6(to_dev(w4))
+    ws = qd.fp6_slice_weights(w6, K)
+    assert np.array_equal(host(ws), _slice96(O.pack_fp6(w4)))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (257, 255, 256), (70, 130, 384), (300, 520, 1024), (513, 1000, 5376)])
+def test_fp6_sliced_gemm_exact(qd, O, M, N, K):
+    say(f"fp6 sliced gemm M={M} N={N} K={K}")
+    a4, w4 = _int4((M, K), 7 * M + K), _int4((N, K), 11 * N + K)
+    a6 = qd.pack_fp6(to_dev(a4))
+    w6s = qd.fp6_slice_weights(qd.pack_fp6(to_dev(w4)), K)
+    ref = O.gemm_i32(a4, w4)
+    assert np.array_equal(host(qd.fp6_gemm_i32_sliced(a6, w6s)), ref)
+    assert np.array_equal(host(qd.fp6_gemm_i32_sliced(to_dev(_slice96(O.pack_fp6(a4))), w6s)), ref)
+
+
+def test_fp6_sliced_gemm_extremes(qd, O):
+    """|sum| = 49 K at K = 28672: the FP32 accumulators stay exact on the sliced path."""
+    K = 28672
+    a4 = np.full((300, K), 7, np.int8)
+    a4[1::2] = -7
+    w4 = np.full((260, K), 7, np.int8)
+    w4[::3] = -7
+    w6s = qd.fp6_slice_weights(qd.pack_fp6(to_dev(w4)), K)
+    acc = qd.fp6_gemm_i32_sliced(qd.pack_fp6(to_dev(a4)), w6s)
+    assert np.array_equal(host(acc), O.gemm_i32(a4, w4))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("M,K", [(1, 256), (63, 768), (257, 5376), (5, 28672)])
+def test_quantize_fp6_sliced(qd, O, dtype, M, K):
+    say(f"fp6 sliced quantizer {dtype} M={M} K={K}")
+    g = np.random.Generator(np.random.PCG64(500 + M + K))
+    xf = g.standard_normal((M, K), dtype=np.float32)
+    if dtype == "bf16":
+        from synth import f32_to_bf16_bits
+        x = f32_to_bf16_bits(xf)
+        xd = to_dev_bf16(x)
+    else:
+        x = xf.astype(np.float16)
+        xd = to_dev(x)
+    q6, s = qd.quantize_and_rotate_rowwise_fp6_sliced(xd)
+    qo, so = O.quantize_rowwise(x, dtype, 256, qmax=7)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q6), _slice96(O.pack_fp6(qo)))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 8), (255, 512, 264), (300, 1024, 520), (257, 5376, 1000)])
+def test_convrot_w4a4_linear_fp6_sliced(qd, O, M, K, N):
+    """The FP6 layer on K-sliced operands: the same bits as the row-major FP6
+    layer, and the oracle's W4A4 layer within one ulp."""
+    import torch
+    from synth import f32_to_bf16_bits
+    say(f"w4a4 fp6 sliced M={M} K={K} N={N}")
+    g = np.random.Generator(np.random.PCG64(800 + M + K + N))
+    x = f32_to_bf16_bits(g.standard_normal((M, K), dtype=np.float32))
+    W = (g.standard_normal((N, K), dtype=np.float32) * 0.02).astype(np.float32)
+    b = f32_to_bf16_bits((g.standard_normal(N, dtype=np.float32) * 0.1).astype(np.float32))
+    w6, sw = qd.prepare_weights_w4a4_fp6(to_dev(W))
+    xd, bd = to_dev_bf16(x), to_dev_bf16(b)
+    y = qd.convrot_w4a4_linear_fp6_sliced(xd, qd.fp6_slice_weights(w6, K), sw, bd)
+    y_rm = qd.convrot_w4a4_linear_fp6(xd, w6, sw, bd)
+    assert torch.equal(y, y_rm)
+    wqo, swo = O.prepare_weights(W, qmax=7)
+    assert_bf16_within_1ulp(bf16_bits(y), O.linear(x, wqo, swo, b, qmax=7), "w4a4 fp6 sliced")
+
+
+def test_w4a4_fp6_sliced_full_size(qd):
+    """The M8192/K28672/N7168 W4A4 workload as the benchmark times it: the
+    same bits as the row-major FP6 layer (whose full-size parity with the
+    oracle is tested in test_gpu_fp6)."""
+    import torch
+    from synth import iter_w, iter_x, make_bias, workload
+    w = workload(5)
+    M, K, N = w.M, w.K, w.N
+    dev = torch.device("cuda:0")
+    say(f"fp6 sliced full-size {w.name}")
+    xd = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for r0, r1, bits in iter_x(w):
+        xd[r0:r1].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    Wd = torch.empty((N, K), dtype=torch.float32, device=dev)
+    for r0, r1, chunk in iter_w(w):
+        Wd[r0:r1].copy_(torch.from_numpy(chunk))
+    bd = torch.from_numpy(make_bias(w).view(np.int16)).view(torch.bfloat16).to(dev)
+    w6, sw = qd.prepare_weights_w4a4_fp6(Wd)
+    del Wd
+    y = qd.convrot_w4a4_linear_fp6_sliced(xd, qd.fp6_slice_weights(w6, K), sw, bd)
+    y_rm = qd.convrot_w4a4_linear_fp6(xd, w6, sw, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_rm)
