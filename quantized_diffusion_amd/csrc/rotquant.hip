@@ -217,7 +217,12 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
     const uint32_t nb_inv = ((1u << 20) + nb - 1) / nb;
     const int rl = (int)(__umul24((uint32_t)quad, nb_inv) >> 20);
     const int blk = quad - rl * nb;
-    const int row = blockIdx.x * R + rl;
+    // K-sliced output (SL): the row groups of one XCD (workgroups g with the
+    // same g % 8) are consecutive, so the neighbouring rows whose codes share
+    // a 128-byte line of a slice are written through the same L2
+    const int G = (int)gridDim.x, g = (int)blockIdx.x;
+    const int wg = SL ? (g % 8) * (G / 8) + min(g % 8, G % 8) + g / 8 : g;
+    const int row = wg * R + rl;
     const bool active = (rl < R) && (row < M);
     if (tid < R) row_amax[tid] = 0u;
 
@@ -226,7 +231,7 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
         // Whole blocks: every lane loads (idle quads read a valid row and
         // discard the result), so the loads need neither a branch nor zeroed
         // registers.  Quads never mix active and idle lanes.
-        const int lrow = min(min(blockIdx.x * R + min(rl, R - 1), row), M - 1);
+        const int lrow = min(min(wg * R + min(rl, R - 1), row), M - 1);
         const uint8_t* src = x + (int64_t)lrow * ldx_bytes + (int64_t)blk * 256 * ESZ;
         u32x4 d[NI];
 #pragma unroll
@@ -329,7 +334,7 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
             const int sl = lane + 64 * j;
             const int qq = (tid >> 6) * 16 + sl / 12;
             const int rl2 = (int)(__umul24((uint32_t)qq, nb_inv) >> 20);
-            const int row2 = blockIdx.x * R + rl2;
+            const int row2 = wg * R + rl2;
             if (rl2 < R && row2 < M) {
                 // SL: K-sliced FP6 operand, 96-byte slices, ldq = the slice stride (M * 96 bytes)
                 const int blk2 = qq - rl2 * nb, kb = 16 * (sl % 12);
@@ -352,7 +357,7 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
         for (int j = 0; j < 4; ++j) {
             const int qq = (tid >> 6) * 16 + 4 * j + (lane >> 4);   // quad of the workgroup
             const int rl2 = (int)(__umul24((uint32_t)qq, nb_inv) >> 20);
-            const int row2 = blockIdx.x * R + rl2;
+            const int row2 = wg * R + rl2;
             if (rl2 < R && row2 < M) {
                 // SL: K-sliced codes, ldq = the slice stride (M * 64 bytes)
                 const int blk2 = qq - rl2 * nb, kin = 16 * (lane & 15);
