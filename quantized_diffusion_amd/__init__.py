@@ -211,6 +211,22 @@ def _mat(t, name):
     return t
 
 
+def _out(t, shape, dtype, name="out"):
+    """A caller-provided output: dtype and shape exactly as the call writes
+    them, rows with a contiguous last dimension (2-D) or fully contiguous
+    (other ranks), so that no kernel writes past the tensor."""
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.dim() == 2:
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+        if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+            raise ValueError(f"{name} rows overlap (row stride {t.stride(0)} < {t.shape[1]})")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
 def _stream(dev):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -247,7 +263,8 @@ def _quantize(fn, x, block, out_q, out_scale, rotate: bool):
         out_q = buf[:, :K]
     if out_scale is None:
         out_scale = torch.empty(M, dtype=torch.float32, device=dev)
-    _mat(out_q, "q")
+    _out(out_q, (M, K), torch.int8, "out_q")
+    _out(out_scale, (M,), torch.float32, "out_scale")
     args = [_ptr(x), _dtype_code(x), M, K, x.stride(0)]
     if rotate:
         args.append(block)
@@ -292,7 +309,8 @@ def quantize_int8_tensorwise(x, out_q=None, out_scale=None, workspace=None):
         out_scale = torch.empty(1, dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = torch.empty(tensorwise_workspace_size(), dtype=torch.uint8, device=dev)
-    _mat(out_q, "q")
+    _out(out_q, (M, K), torch.int8, "out_q")
+    _out(out_scale, (1,), torch.float32, "out_scale")
     _check(lib().qd_quantize_int8_tensorwise(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(out_q),
                                              out_q.stride(0), _ptr(out_scale), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(dev)))
@@ -325,7 +343,7 @@ def int8_scaled_mm(aq, a_scale, wq, w_scale, bias=None, out=None):
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int8_scaled_mm(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(wq), N, wq.stride(0),
                                    _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
     return out
@@ -348,7 +366,7 @@ def int8_scaled_mm_ex(aq, a_scale, wq, w_scale, bias=None, out=None):
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int8_scaled_mm_ex(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), a_scale.numel(), _ptr(wq), N,
                                       wq.stride(0), _ptr(w_scale), w_scale.numel(), _ptr(bias), _ptr(out),
                                       out.stride(0), _stream(dev)))
@@ -367,7 +385,7 @@ def int8_gemm_i32(aq, wq, out=None):
     if out is None:
         ldc = (N + 3) // 4 * 4
         out = torch.empty((M, ldc), dtype=torch.int32, device=dev)[:, :N]
-    _mat(out, "out")
+    _out(out, (M, N), torch.int32)
     _check(lib().qd_int8_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wq), N, wq.stride(0), _ptr(out),
                                   out.stride(0), _stream(dev)))
     return out
@@ -393,6 +411,7 @@ def slice_weights(wq, out=None):
     N, K = wq.shape
     if out is None:
         out = torch.empty((max(K // 64, 0), N, 64), dtype=torch.int8, device=dev)
+    _out(out, (K // 64, N, 64), torch.int8)
     _check(lib().qd_int8_slice_weights(_ptr(wq), N, K, wq.stride(0), _ptr(out), _stream(dev)))
     return out
 
@@ -415,7 +434,7 @@ def int8_linear_sliced(x, w_sliced, w_scale, bias=None, input_act: int = ACT_NON
         workspace = torch.empty(max(workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int8_linear_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act), _ptr(w_sliced),
                                        N, _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
@@ -443,6 +462,8 @@ def quantize_and_rotate_rowwise_sliced(x, block: int = 256, out_q=None, out_scal
         out_q = torch.empty((max(K // 64, 0), M, 64), dtype=torch.int8, device=dev)
     if out_scale is None:
         out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _out(out_q, (K // 64, M, 64), torch.int8, "out_q")
+    _out(out_scale, (M,), torch.float32, "out_scale")
     _check(lib().qd_quantize_and_rotate_rowwise_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act),
                                                        block, _ptr(out_q), _ptr(out_scale), _stream(dev)))
     return out_q, out_scale
@@ -463,7 +484,7 @@ def int8_scaled_mm_sliced(aq, a_scale, w_sliced, w_scale, bias=None, out=None):
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int8_scaled_mm_sliced(_ptr(aq), M, K, lda, a_sl, _ptr(a_scale), _ptr(w_sliced), N,
                                           _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
     return out
@@ -479,7 +500,7 @@ def int8_gemm_i32_sliced(aq, w_sliced, out=None):
         raise ValueError("aq and w_sliced disagree on K")
     if out is None:
         out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
-    _mat(out, "out")
+    _out(out, (M, N), torch.int32)
     _check(lib().qd_int8_gemm_i32_sliced(_ptr(aq), M, K, lda, a_sl, _ptr(w_sliced), N, _ptr(out),
                                          out.stride(0), _stream(dev)))
     return out
@@ -511,6 +532,7 @@ def int8_attention(q, k, v, scale: float = 0.0, workspace=None, out=None):
         workspace = torch.empty(max(1, attention_workspace_size(BH, Lq, Lk, D)), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty((BH, Lq, D), dtype=torch.bfloat16, device=dev)
+    _out(out, (BH, Lq, D), torch.bfloat16)
     _check(lib().qd_int8_attention(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), BH, Lq, Lk, D, float(scale),
                                    _ptr(workspace), workspace.numel(), _ptr(out), _stream(dev)))
     return out
@@ -531,6 +553,7 @@ def int8_attention_codes(qc, sq, kc, sk, vc, sv, scale: float = 0.0, out=None):
     dev = _dev(qc, sq, kc, sk, vc, sv, out)
     if out is None:
         out = torch.empty((BH, Lq, D), dtype=torch.bfloat16, device=dev)
+    _out(out, (BH, Lq, D), torch.bfloat16)
     _check(lib().qd_int8_attention_codes(_ptr(qc), _ptr(sq), _ptr(kc), _ptr(sk), _ptr(vc), _ptr(sv), BH, Lq, Lk,
                                          D, float(scale), _ptr(out), _stream(dev)))
     return out
@@ -572,7 +595,7 @@ def int8_linear(x, wq, w_scale, bias=None, rotate_block: int = 256, workspace=No
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int8_linear(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(wq), N, wq.stride(0),
                                 _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
@@ -599,7 +622,7 @@ def int8_linear_act(x, wq, w_scale, bias=None, input_act: int = ACT_NONE, rotate
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int8_linear_act(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act), _ptr(wq), N,
                                     wq.stride(0), _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
@@ -617,7 +640,8 @@ def quantize_rowwise_act(x, input_act: int, rotate_block: int = 256, out_q=None,
         out_q = torch.empty((M, (K + 15) // 16 * 16), dtype=torch.int8, device=dev)[:, :K]
     if out_scale is None:
         out_scale = torch.empty(M, dtype=torch.float32, device=dev)
-    _mat(out_q, "q")
+    _out(out_q, (M, K), torch.int8, "out_q")
+    _out(out_scale, (M,), torch.float32, "out_scale")
     _check(lib().qd_quantize_rowwise_act(_ptr(x), _dtype_code(x), M, K, x.stride(0), int(input_act), rotate_block,
                                          _ptr(out_q), out_q.stride(0), _ptr(out_scale), _stream(dev)))
     return out_q, out_scale
@@ -631,6 +655,7 @@ def input_act(x, act: int, out=None):
         raise ValueError("x must be contiguous")
     if out is None:
         out = torch.empty_like(x)
+    _out(out, tuple(x.shape), x.dtype)
     _check(lib().qd_input_act(_ptr(x), _dtype_code(x), x.numel(), int(act), _ptr(out), _stream(dev)))
     return out
 
@@ -650,7 +675,7 @@ def pack_fp6(q, out=None):
     R, K = q.shape
     if out is None:
         out = torch.empty((R, _f6_ld(K)), dtype=torch.uint8, device=dev)[:, :K // 4 * 3]
-    _mat(out, "out")
+    _out(out, (R, K // 4 * 3), torch.uint8)
     _check(lib().qd_pack_fp6(_ptr(q), R, K, q.stride(0), _ptr(out), out.stride(0), _stream(dev)))
     return out
 
@@ -666,7 +691,8 @@ def quantize_and_rotate_rowwise_fp6(x, block: int = 256, out_q6=None, out_scale=
         out_q6 = torch.empty((M, _f6_ld(K)), dtype=torch.uint8, device=dev)[:, :K // 4 * 3]
     if out_scale is None:
         out_scale = torch.empty(M, dtype=torch.float32, device=dev)
-    _mat(out_q6, "q6")
+    _out(out_q6, (M, K // 4 * 3), torch.uint8, "out_q6")
+    _out(out_scale, (M,), torch.float32, "out_scale")
     _check(lib().qd_quantize_and_rotate_rowwise_fp6(_ptr(x), _dtype_code(x), M, K, x.stride(0), block,
                                                     _ptr(out_q6), out_q6.stride(0), _ptr(out_scale), _stream(dev)))
     return out_q6, out_scale
@@ -679,10 +705,17 @@ def prepare_weights_w4a4_fp6(w, block: int = 256):
     return pack_fp6(q), s
 
 
+def _f6_rows(t, K, name):
+    _mat(t, name)
+    if t.shape[1] != K // 4 * 3:
+        raise ValueError(f"{name} must hold 3K/4 = {K // 4 * 3} bytes per row, got {t.shape[1]}")
+    return t
+
+
 def fp6_scaled_mm(a6, a_scale, w6, w_scale, K: int, bias=None, out=None):
     """The GEMM on FP6 operands (K values per row), BF16 out with the fused epilogue."""
     torch = _torch()
-    _mat(a6, "a6"), _mat(w6, "w6")
+    _f6_rows(a6, K, "a6"), _f6_rows(w6, K, "w6")
     dev = _dev(a6, a_scale, w6, w_scale, bias, out)
     M, N = a6.shape[0], w6.shape[0]
     _rows_vec(a_scale, M, torch.float32, "a_scale")
@@ -691,7 +724,7 @@ def fp6_scaled_mm(a6, a_scale, w6, w_scale, K: int, bias=None, out=None):
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_fp6_scaled_mm(_ptr(a6), M, K, a6.stride(0), _ptr(a_scale), _ptr(w6), N, w6.stride(0),
                                   _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
     return out
@@ -700,11 +733,12 @@ def fp6_scaled_mm(a6, a_scale, w6, w_scale, K: int, bias=None, out=None):
 def fp6_gemm_i32(a6, w6, K: int, out=None):
     """Exact sums of the FP6 GEMM as int32 [M, N]."""
     torch = _torch()
-    _mat(a6, "a6"), _mat(w6, "w6")
+    _f6_rows(a6, K, "a6"), _f6_rows(w6, K, "w6")
     dev = _dev(a6, w6, out)
     M, N = a6.shape[0], w6.shape[0]
     if out is None:
         out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
+    _out(out, (M, N), torch.int32)
     _check(lib().qd_fp6_gemm_i32(_ptr(a6), M, K, a6.stride(0), _ptr(w6), N, w6.stride(0), _ptr(out),
                                  out.stride(0), _stream(dev)))
     return out
@@ -717,9 +751,10 @@ def w4a4_fp6_workspace_size(M: int, K: int) -> int:
 def convrot_w4a4_linear_fp6(x, w6, w_scale, bias=None, rotate_block: int = 256, workspace=None, out=None):
     """convrot_w4a4_linear with FP6 weights (prepare_weights_w4a4_fp6): same results, FP6 matrix path."""
     torch = _torch()
-    _mat(x, "x"), _mat(w6, "w6")
+    _mat(x, "x")
     dev = _dev(x, w6, w_scale, bias, workspace, out)
     M, K = x.shape
+    _f6_rows(w6, K, "w6")
     N = w6.shape[0]
     _rows_vec(w_scale, N, torch.float32, "w_scale")
     if bias is not None:
@@ -728,7 +763,7 @@ def convrot_w4a4_linear_fp6(x, w6, w_scale, bias=None, rotate_block: int = 256, 
         workspace = torch.empty(max(w4a4_fp6_workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_convrot_w4a4_linear_fp6(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(w6), N, w6.stride(0),
                                             _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                             workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),
@@ -753,6 +788,9 @@ def fp6_slice_weights(w6, K: int, out=None):
     N = w6.shape[0]
     if out is None:
         out = torch.empty((max(K // 128, 0), N, 96), dtype=torch.uint8, device=dev)
+    _out(out, (K // 128, N, 96), torch.uint8)
+    if w6.shape[1] != K // 4 * 3:
+        raise ValueError("w6 must hold 3K/4 bytes per row")
     _check(lib().qd_fp6_slice_weights(_ptr(w6), N, K, w6.stride(0), _ptr(out), _stream(dev)))
     return out
 
@@ -767,6 +805,8 @@ def quantize_and_rotate_rowwise_fp6_sliced(x, block: int = 256, out_q6=None, out
         out_q6 = torch.empty((max(K // 128, 0), M, 96), dtype=torch.uint8, device=dev)
     if out_scale is None:
         out_scale = torch.empty(M, dtype=torch.float32, device=dev)
+    _out(out_q6, (K // 128, M, 96), torch.uint8, "out_q6")
+    _out(out_scale, (M,), torch.float32, "out_scale")
     _check(lib().qd_quantize_and_rotate_rowwise_fp6_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), block,
                                                            _ptr(out_q6), _ptr(out_scale), _stream(dev)))
     return out_q6, out_scale
@@ -779,7 +819,7 @@ def _f6_a_operand(a6, K):
         if Ka != K:
             raise ValueError("a6 and w6_sliced disagree on K")
         return M, K // 4 * 3, 1
-    _mat(a6, "a6")
+    _f6_rows(a6, K, "a6")
     return a6.shape[0], a6.stride(0), 0
 
 
@@ -795,7 +835,7 @@ def fp6_scaled_mm_sliced(a6, a_scale, w6_sliced, w_scale, bias=None, out=None):
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_fp6_scaled_mm_sliced(_ptr(a6), M, K, lda, a_sl, _ptr(a_scale), _ptr(w6_sliced), N, _ptr(w_scale),
                                          _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
     return out
@@ -809,6 +849,7 @@ def fp6_gemm_i32_sliced(a6, w6_sliced, out=None):
     M, lda, a_sl = _f6_a_operand(a6, K)
     if out is None:
         out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
+    _out(out, (M, N), torch.int32)
     _check(lib().qd_fp6_gemm_i32_sliced(_ptr(a6), M, K, lda, a_sl, _ptr(w6_sliced), N, _ptr(out), out.stride(0),
                                         _stream(dev)))
     return out
@@ -831,7 +872,7 @@ def convrot_w4a4_linear_fp6_sliced(x, w6_sliced, w_scale, bias=None, rotate_bloc
         workspace = torch.empty(max(w4a4_fp6_workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_convrot_w4a4_linear_fp6_sliced(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(w6_sliced), N,
                                                    _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                                    workspace.numel() * workspace.element_size(), _ptr(out),
@@ -849,11 +890,11 @@ def dequantize_int8(q, scale, out_dtype=None, out=None):
     dev = _dev(q, scale, out)
     M, K = q.shape
     per_row = scale.numel() == M and M != 1
-    if scale.dtype != torch.float32 or (scale.numel() > 1 and scale.stride(0) != 1):
-        raise ValueError("scale must be a contiguous fp32 tensor")
+    if scale.dtype != torch.float32 or scale.numel() < 1 or (scale.numel() > 1 and scale.stride(0) != 1):
+        raise ValueError("scale must be a non-empty contiguous fp32 tensor")
     if out is None:
         out = torch.empty((M, K), dtype=out_dtype, device=dev)
-    _mat(out, "out")
+    _out(out, (M, K), out.dtype if out.dtype in (torch.float32, torch.bfloat16) else out_dtype)
     _check(lib().qd_dequantize_int8(_ptr(q), M, K, q.stride(0), _ptr(scale), int(per_row),
                                     _dtype_code(out), _ptr(out), out.stride(0), _stream(dev)))
     return out
@@ -871,7 +912,7 @@ def pack_int4(q, out=None):
     if out is None:
         ldp = (K // 2 + 15) // 16 * 16
         out = torch.empty((R, ldp), dtype=torch.uint8, device=dev)[:, : K // 2]
-    _mat(out, "packed")
+    _out(out, (R, K // 2), torch.uint8, "out")
     _check(lib().qd_pack_int4(_ptr(q), R, K, q.stride(0), _ptr(out), out.stride(0), _stream(dev)))
     return out
 
@@ -904,7 +945,7 @@ def int4_scaled_mm(aq, a_scale, wp, w_scale, bias=None, out=None):
         _rows_vec(bias, N, torch.bfloat16, "bias")
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_int4_scaled_mm(_ptr(aq), M, K, aq.stride(0), _ptr(a_scale), _ptr(wp), N, wp.stride(0),
                                    _ptr(w_scale), _ptr(bias), _ptr(out), out.stride(0), _stream(dev)))
     return out
@@ -917,7 +958,7 @@ def int4_gemm_i32(aq, wp, out=None):
     dev = _dev(aq, wp, out)
     if out is None:
         out = torch.empty((M, (N + 3) // 4 * 4), dtype=torch.int32, device=dev)[:, :N]
-    _mat(out, "out")
+    _out(out, (M, N), torch.int32)
     _check(lib().qd_int4_gemm_i32(_ptr(aq), M, K, aq.stride(0), _ptr(wp), N, wp.stride(0), _ptr(out),
                                   out.stride(0), _stream(dev)))
     return out
@@ -940,7 +981,7 @@ def convrot_w4a4_linear(x, wp, w_scale, bias=None, rotate_block: int = 256, work
         workspace = torch.empty(max(workspace_size(M, K), 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = _bf16_out(M, N, dev)
-    _mat(out, "out")
+    _out(out, (M, N), torch.bfloat16)
     _check(lib().qd_convrot_w4a4_linear(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(wp), N, wp.stride(0),
                                         _ptr(w_scale), _ptr(bias), rotate_block, _ptr(workspace),
                                         workspace.numel() * workspace.element_size(), _ptr(out), out.stride(0),

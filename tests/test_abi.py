@@ -406,3 +406,24 @@ def test_fp6_sliced_validation():
     assert f(qd.QD_F32) == qd.QD_EUNSUPPORTED
     assert f(qd.QD_BF16, rb=0) == qd.QD_EUNSUPPORTED
     assert f(qd.QD_BF16, K=384) == qd.QD_EUNSUPPORTED
+
+
+def test_output_tensor_checks():
+    """Caller-provided outputs are checked for dtype and exact shape (the kernels
+    write the whole extent), so a short buffer raises instead of being overrun."""
+    import torch
+
+    qd._out(torch.empty(4, 8, dtype=torch.bfloat16), (4, 8), torch.bfloat16)
+    qd._out(torch.empty(4, 16, dtype=torch.bfloat16)[:, :8], (4, 8), torch.bfloat16)   # padded rows are fine
+    with pytest.raises(ValueError):
+        qd._out(torch.empty(3, 8, dtype=torch.bfloat16), (4, 8), torch.bfloat16)
+    with pytest.raises(ValueError):
+        qd._out(torch.empty(4, 8, dtype=torch.float32), (4, 8), torch.bfloat16)
+    with pytest.raises(ValueError):
+        qd._out(torch.empty(8, 4, dtype=torch.bfloat16).t(), (4, 8), torch.bfloat16)
+    with pytest.raises(ValueError):
+        qd._out(torch.empty(2, 4, 8, 64, dtype=torch.int8)[:, 0], (2, 8, 64), torch.int8)
+    qd._out(torch.empty(2, 8, 64, dtype=torch.int8), (2, 8, 64), torch.int8)
+    with pytest.raises(ValueError):
+        qd._f6_rows(torch.empty(4, 90, dtype=torch.uint8), 128, "a6")
+    qd._f6_rows(torch.empty(4, 96, dtype=torch.uint8), 128, "a6")
