@@ -22,6 +22,10 @@
 // four 40 KB stages), moving 17 % fewer bytes from L2 into LDS per MAC; the
 // launcher picks the tile by shape (rounds of one workgroup per CU).
 // A general kernel (any K % 16 == 0) stages operands through registers.
+// The eight-wave kernels take a row stride and a K-slice stride per operand,
+// so they read row-major operands or the K-sliced layout (each 64-byte K
+// slice of all rows stored contiguously: a copy instruction then reads 1 KB
+// of consecutive bytes, whole 128-byte lines, at lower power per byte).
 //
 // MFMA roles.  The weight tile is the MFMA "A" operand (its rows index n)
 // and the activation tile is "B" (its columns index m), so each lane ends up

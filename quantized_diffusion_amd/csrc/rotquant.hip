@@ -48,6 +48,11 @@
 // instruction writes four whole blocks (1 KB, whole 128-byte lines).  The
 // stores keep the default cache policy: the GEMM reads the codes next, and a
 // whole step measured faster that way than with streaming stores.
+//
+// K-sliced output (SL, for the GEMM's K-sliced operand layout): byte (m, k)
+// goes to (k / S) * M * S + m * S + k % S with S = 64 for INT8 codes and
+// S = 96 bytes (128 values) for the FP6 operand; a block image leaves LDS as
+// its 64- or 96-byte slice pieces.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
