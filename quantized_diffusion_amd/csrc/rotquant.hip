@@ -478,10 +478,15 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     double best_waste = 2.0;
     constexpr int MAXT = kMaxThreads<ACT, In16<In>::value>::value;
     const int r0 = nb >= 64 ? 1 : 64 / nb;
-    for (int r = r0; r <= 2 * r0 && 4 * r * nb <= MAXT; ++r) {
-        const int th = (4 * r * nb + 63) / 64 * 64;
-        const double waste = (double)(th - 4 * r * nb) / th;
-        if (waste < best_waste - 1e-9) { best_waste = waste; R = r; best_threads = th; }
+    // K-sliced INT8 codes: an even row count keeps both rows of every 128-byte
+    // line of a slice (rows 2i, 2i + 1) in one workgroup
+    for (int pass = (SL && !F6) ? 0 : 1; pass < 2 && best_threads == 0; ++pass) {
+        for (int r = r0; r <= 2 * r0 + (pass == 0) && 4 * r * nb <= MAXT; ++r) {
+            if (pass == 0 && (r & 1)) continue;
+            const int th = (4 * r * nb + 63) / 64 * 64;
+            const double waste = (double)(th - 4 * r * nb) / th;
+            if (waste < best_waste - 1e-9) { best_waste = waste; R = r; best_threads = th; }
+        }
     }
     if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }

@@ -70,7 +70,8 @@ def test_sliced_gemm_i32_exact(qd, O, tiles, M, N, K):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-@pytest.mark.parametrize("M,K", [(1, 256), (3, 512), (63, 768), (257, 5376), (130, 7168), (1000, 1024)])
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 512), (63, 768), (257, 5376), (130, 7168), (1000, 1024),
+                                 (7, 28672)])
 def test_quantize_sliced(qd, O, dtype, M, K):
     """The rotating quantizer writing K-sliced codes: the oracle's codes re-laid out, same scales."""
     say(f"sliced rotquant {dtype} M={M} K={K}")
