@@ -255,6 +255,30 @@ def main():
     ops = 2.0 * M * N * K
     tops = ops / (ms * 1e-3) / 1e12
 
+    # distribution of single-step times (one event pair per step), then cold-cache steps: a
+    # 512 MB scratch write before each (untimed) evicts the 256 MB Infinity Cache
+    def timed_steps(n, before=None):
+        evs = []
+        for _ in range(n):
+            if before is not None:
+                before()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in evs)
+
+    warm = timed_steps(args.steps)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = timed_steps(min(args.steps, 10), lambda: scratch.fill_(1))
+    del scratch
+    pick = lambda v, q: round(v[min(len(v) - 1, int(q * len(v)))], 5)
+    step_times = {"warm_median": pick(warm, 0.5), "warm_min": round(warm[0], 5), "warm_p90": pick(warm, 0.9),
+                  "cold_median": pick(cold, 0.5), "cold_min": round(cold[0], 5),
+                  "note": "single steps timed with their own event pair; cold = after a 512 MB scratch write"}
+
     # per-kernel durations (same kernels, launched through their own entry points)
     aq = torch.empty((M, K), dtype=torch.int8, device=dev)
     sx = torch.empty(M, dtype=torch.float32, device=dev)
@@ -337,6 +361,7 @@ def main():
             "quantizer_writes": ("fp6 operand format, K-sliced" if sliced6 else "fp6 operand format" if fp6 else
                                  "int8 codes, K-sliced" if sliced else "int8 codes"),
         },
+        "step_times_ms": step_times,
         "device": torch.cuda.get_device_name(0),
         "wall_s_timed_region": round(t_wall, 4),
         "context": "pages' figure for this workload: 10.5752 ms single call on an RTX 5090 D v2 (another machine)"
