@@ -670,8 +670,6 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     const int wm = wave & 1;    // 128-row half of the activation tile
     const int wn = wave >> 1;   // 96-row quarter of the weight tile
 
-    
-
     // copy instruction i of this wave covers rows 16 * (wave + 8 i) + lane / 4
     // of the activation tile (i < 2) and of the weight tile (i < 3)
     const int8_t* ga[2];
