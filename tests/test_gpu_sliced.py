@@ -313,3 +313,28 @@ def test_w4a4_fp6_sliced_full_size(qd):
     y_rm = qd.convrot_w4a4_linear_fp6(xd, w6, sw, bd)
     torch.cuda.synchronize()
     assert torch.equal(y, y_rm)
+
+
+def test_int8_linear_sliced_strided_and_degenerate(qd, O):
+    """x with a row stride above K, a zero row and a row of one spike, no bias,
+    a reused workspace: the same bits as int8_linear, and the oracle."""
+    import torch
+    from synth import f32_to_bf16_bits, make_w, workload
+    w = workload(1)
+    W = make_w(w)
+    g = np.random.Generator(np.random.PCG64(4242))
+    M, K = 65, w.K
+    xf = g.standard_normal((M, K + 64), dtype=np.float32)
+    xf[3] = 0.0
+    xf[7] = 0.0
+    xf[7, 100] = 5.0
+    x = f32_to_bf16_bits(xf)
+    xd = to_dev_bf16(x)[:, :K]
+    wqo, swo = O.prepare_weights(W)
+    wq = to_dev(wqo)
+    ws = torch.empty(qd.workspace_size(M, K), dtype=torch.uint8, device=xd.device)
+    y = qd.int8_linear_sliced(xd, qd.slice_weights(wq), to_dev(swo), None, workspace=ws)
+    y_rm = qd.int8_linear(xd, wq, to_dev(swo), None, 256, ws)
+    assert torch.equal(y, y_rm)
+    assert_bf16_within_1ulp(bf16_bits(y), O.linear(np.ascontiguousarray(x[:, :K]), wqo, swo, None), "strided")
+    assert not bf16_bits(y)[3].any()    # zero row, no bias: +0 everywhere
