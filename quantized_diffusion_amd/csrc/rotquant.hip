@@ -239,8 +239,14 @@ __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void ro
         const int lrow = min(min(wg * R + min(rl, R - 1), row), M - 1);
         const uint8_t* src = x + (int64_t)lrow * ldx_bytes + (int64_t)blk * 256 * ESZ;
         u32x4 d[NI];
+        // The sliced INT8 quantizer feeds the wide GEMM: x is read once, so a
+        // non-temporal load keeps it from displacing the GEMM's operands in L2
+        // and the memory-side cache.
 #pragma unroll
-        for (int i = 0; i < NI; ++i) d[i] = *reinterpret_cast<const u32x4*>(src + (i * 4 + ql) * 16);
+        for (int i = 0; i < NI; ++i) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(src + (i * 4 + ql) * 16);
+            d[i] = (SL && !F6) ? __builtin_nontemporal_load(p) : *p;
+        }
         if (ACT != ACT_NONE) {
             load_lut();
             // on the raw 16-bit words, before widening: fewer live registers
