@@ -114,12 +114,11 @@ __device__ __forceinline__ void store_bf16x4(const int32_t* a4, float sx, int n,
     }
 }
 
-// Four outputs bf16_rne(((float)acc_e * sx) * sw_e + b_e) packed as BF16 pairs.
-__device__ __forceinline__ u32x2 epi_bf16x4(const int32_t* a4, float sx, const f32x4& sw, const u32x2& bb,
+// Four outputs bf16_rne(((float)acc_e * sx) * sw_e + b_e) packed as BF16 pairs; the
+// bias arrives widened to FP32 (exact), once per tile column in LDS.
+__device__ __forceinline__ u32x2 epi_bf16x4(const int32_t* a4, float sx, const f32x4& sw, const f32x4& b,
                                             bool has_bias) {
 #pragma clang fp contract(off)
-    const float b[4] = {bits_f(bb[0] << 16), bits_f(bb[0] & 0xFFFF0000u), bits_f(bb[1] << 16),
-                        bits_f(bb[1] & 0xFFFF0000u)};
     float o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -351,7 +350,7 @@ __device__ __forceinline__ void dma16(uint32_t lds, const int8_t* src) {
 // (their outputs are never stored).  The tile's row scales, column scales
 // and bias are copied into LDS above the ring during the prologue.
 constexpr int NT8 = 512;
-constexpr int EPI_LDS = 4 * 1024;   // sx[256] f32, sw[256] f32, bias[256] bf16 (+pad)
+constexpr int EPI_LDS = 4 * 1024;   // sx[256] f32, sw[256] f32, bias[256] widened to f32 (+pad)
 
 enum { WF_I8 = 0, WF_I4 = 1 };   // weight operand: INT8, or INT4 packed two per byte
 
@@ -369,7 +368,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING + EPI_LDS];
     float* l_sx = reinterpret_cast<float*>(smem + RING);
     float* l_sw = l_sx + 256;
-    uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + 256);
+    float* l_b = l_sw + 256;
 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
@@ -401,7 +400,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
             const int c = tid - 256;
             const int n = min(n0 + c, N - 1);
             l_sw[c] = ep.w_scale[n * ep.w_step];
-            l_b[c] = ep.bias ? ep.bias[n] : (uint16_t)0;
+            l_b[c] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
         }
     }
 
@@ -566,7 +565,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int c = wn * 64 + 32 * i + 8 * g4 + 4 * fk;
                     const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
-                    const u32x2 bb = *reinterpret_cast<const u32x2*>(l_b + c);
+                    const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                     const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                                            acc[i][j][4 * g4 + 3]};
                     const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
@@ -647,7 +646,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING];
     float* l_sx = reinterpret_cast<float*>(smem + 128 * 768);   // after the K loop, above the staged rows
     float* l_sw = l_sx + 256;
-    uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + BNW);
+    float* l_b = l_sw + BNW;
 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BNW - 1) / BNW;
@@ -802,7 +801,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         if (tid < BNW) {
             const int n = min(n0 + tid, N - 1);
             l_sw[tid] = ep.w_scale[n * ep.w_step];
-            l_b[tid] = ep.bias ? ep.bias[n] : (uint16_t)0;
+            l_b[tid] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
         }
         __syncthreads();
         uint16_t* out = static_cast<uint16_t*>(ep.out);
@@ -821,7 +820,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
                     for (int g4 = 0; g4 < 4; ++g4) {
                         const int c = wn * 96 + 32 * i + 8 * g4 + 4 * fk;
                         const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
-                        const u32x2 bb = *reinterpret_cast<const u32x2*>(l_b + c);
+                        const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                         const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                                                acc[i][j][4 * g4 + 3]};
                         const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
@@ -902,11 +901,9 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Four outputs from exact FP32 sums (same arithmetic as epi_bf16x4).
-__device__ __forceinline__ u32x2 epi_bf16x4_f(const float* a4, float sx, const f32x4& sw, const u32x2& bb,
+__device__ __forceinline__ u32x2 epi_bf16x4_f(const float* a4, float sx, const f32x4& sw, const f32x4& b,
                                               bool has_bias) {
 #pragma clang fp contract(off)
-    const float b[4] = {bits_f(bb[0] << 16), bits_f(bb[0] & 0xFFFF0000u), bits_f(bb[1] << 16),
-                        bits_f(bb[1] & 0xFFFF0000u)};
     float o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -930,7 +927,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING + EPI_LDS];
     float* l_sx = reinterpret_cast<float*>(smem + RING);
     float* l_sw = l_sx + 256;
-    uint16_t* l_b = reinterpret_cast<uint16_t*>(l_sw + 256);
+    float* l_b = l_sw + 256;
 
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
@@ -961,7 +958,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
             const int c = tid - 256;
             const int n = min(n0 + c, N - 1);
             l_sw[c] = ep.w_scale[n * ep.w_step];
-            l_b[c] = ep.bias ? ep.bias[n] : (uint16_t)0;
+            l_b[c] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
         }
     }
 
@@ -1115,7 +1112,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const int c = wn * 64 + 32 * i + 8 * g4 + 4 * fk;
                     const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
-                    const u32x2 bb = *reinterpret_cast<const u32x2*>(l_b + c);
+                    const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                     const float a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                                          acc[i][j][4 * g4 + 3]};
                     const u32x2 pk = epi_bf16x4_f(a4, sx, sw, bb, ep.bias != nullptr);
