@@ -77,9 +77,19 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
     const int wave = tid >> 6;
     const int fr = lane & 31;
     const int h = lane >> 5;
-    const int64_t qbase = (int64_t)blockIdx.y * Lq;
-    const int64_t kbase = (int64_t)blockIdx.y * Lk;
-    const int q_row = blockIdx.x * AQ + wave * 32 + fr;   // this lane's query
+    // Workgroups are dispatched to the 8 XCDs round-robin in launch order;
+    // renumber them so that each XCD takes a contiguous range of (head, query
+    // block) pairs, i.e. whole heads, whose keys and values its L2 then serves
+    // to all of that head's query blocks.
+    const int nqb = (int)gridDim.x;
+    const int Gt = nqb * (int)gridDim.y;
+    const int gl = (int)blockIdx.x + nqb * (int)blockIdx.y;
+    const int xc = gl % 8;
+    const int tl = xc * (Gt / 8) + min(xc, Gt % 8) + gl / 8;
+    const int qb = tl % nqb, hd = tl / nqb;
+    const int64_t qbase = (int64_t)hd * Lq;
+    const int64_t kbase = (int64_t)hd * Lk;
+    const int q_row = qb * AQ + wave * 32 + fr;   // this lane's query
     const int qr = min(q_row, Lq - 1);
 
     i32x4 qf[NS];
