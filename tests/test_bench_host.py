@@ -1,0 +1,46 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, and the rule
+that HBM-traffic figures are reported only for the kernel source they were
+taken on."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stdout
+
+
+def test_kernel_hash_ignores_comments_and_blank_lines(tmp_path):
+    a = tmp_path / "a.hip"
+    b = tmp_path / "b.hip"
+    c = tmp_path / "c.hip"
+    a.write_text("int f(int x) {\n    return x + 1;\n}\n")
+    b.write_text("// header\n/* block\n comment */\nint f(int x) {   // trailing\n\n    return x + 1;\n}\n")
+    c.write_text("int f(int x) {\n    return x + 2;\n}\n")
+    assert bench.kernel_hash(str(a)) == bench.kernel_hash(str(b))
+    assert bench.kernel_hash(str(a)) != bench.kernel_hash(str(c))
+
+
+def test_traffic_only_for_the_current_kernel(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("int k() { return 0; }\n")
+    tf = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "GEMM_SRC", str(src))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tf))
+    rec = {"workloads": {"W": {"hbm_bytes_per_launch": 123}}}
+    tf.write_text(json.dumps(dict(rec, kernel_hash=bench.kernel_hash(str(src)))))
+    assert bench.load_traffic("W") == 123
+    assert bench.load_traffic("other workload") is None
+    src.write_text("int k() { return 1; }\n")          # the kernel changed since the counters
+    assert bench.load_traffic("W") is None
+    tf.write_text("not json")
+    assert bench.load_traffic("W") is None
+
