@@ -75,8 +75,6 @@ def _bind(L):
     L.oracle_quantize_rowwise_act.restype = I
     L.oracle_quantize_rowwise_act.argtypes = [P, I, I64, I64, I64, I, I, I, P, I64, P]
     L.oracle_input_act.argtypes = [P, I, I64, I, P]
-    L.oracle_pack_fp6.restype = I64
-    L.oracle_pack_fp6.argtypes = [P, I64, I64, P]
     L.oracle_linear.restype = I
     L.oracle_linear.argtypes = [P, I, I64, I64, I64, P, P, P, I64, I, I, P]
     L.oracle_linear_points.argtypes = [P, I64, P, P, P, P, P, P, I64, P, P]
@@ -195,16 +193,6 @@ class Oracle:
         t = np.empty((M, N), np.float32)
         self.L.oracle_epilogue_f32(_p(acc), M, N, _p(sx), _p(sw), _p(b), _p(t))
         return t
-
-    def pack_fp6(self, q) -> np.ndarray:
-        """INT4 codes [R, K] -> the FP6 E2M3 operand format, uint8 [R, 3K/4]."""
-        q = np.ascontiguousarray(q, dtype=np.int8)
-        R, K = q.shape
-        out = np.empty((R, K // 4 * 3), np.uint8)
-        bad = self.L.oracle_pack_fp6(_p(q), R, K, _p(out))
-        if bad:
-            raise ValueError(f"{bad} codes are not exact in FP6 E2M3")
-        return out
 
     def input_act(self, x, dtype: str, act: int) -> np.ndarray:
         """act(x) elementwise, rounded to the 16-bit input type; uint16 bits."""

@@ -412,47 +412,6 @@ def check_linear_accuracy(O):
     assert errs[256] < 0.8 * errs[0], errs
 
 
-# ---------------------------------------------------- FP6 operand format
-
-def _decode_fp6_rows(packed: np.ndarray, K: int) -> list:
-    """Values of the FP6 operand format, decoded from its description: per 64
-    values, [piece 0 head 16 B | piece 1 head 16 B | tails (swapped when row
-    bits 3 and 4 differ)], value i of a piece in bits 6i.., E2M3 fields."""
-    rows = []
-    for r, row in enumerate(packed):
-        vals = []
-        for j in range(K // 64):
-            blk = bytes(row[48 * j:48 * j + 48])
-            t0, t1 = (blk[32:40], blk[40:48]) if ((r >> 3) ^ (r >> 4)) & 1 == 0 else (blk[40:48], blk[32:40])
-            for piece in (blk[0:16] + t0, blk[16:32] + t1):
-                bits = int.from_bytes(piece, "little")
-                for i in range(32):
-                    f = (bits >> (6 * i)) & 63
-                    s, e, m = f >> 5, (f >> 3) & 3, f & 7
-                    mag = Fraction(m, 8) if e == 0 else Fraction(2) ** (e - 1) * (1 + Fraction(m, 8))
-                    vals.append(-mag if s else mag)
-        rows.append(vals)
-    return rows
-
-
-def check_fp6_pack(O):
-    g = np.random.Generator(np.random.PCG64(40))
-    q = g.integers(-7, 8, (40, 192), dtype=np.int64).astype(np.int8)     # rows with every (bit 3, bit 4)
-    q[0, :15] = np.arange(-7, 8)
-    packed = O.pack_fp6(q)
-    assert packed.shape == (40, 144)
-    dec = _decode_fp6_rows(packed, 192)
-    for r in range(40):
-        assert dec[r] == [Fraction(int(v)) for v in q[r]], r
-    # a single nonzero code lands in exactly its own field
-    z = np.zeros((1, 64), np.int8)
-    z[0, 37] = 5
-    p = O.pack_fp6(z)
-    piece1 = bytes(p[0, 16:32]) + bytes(p[0, 40:48])
-    assert int.from_bytes(piece1, "little") == 0b011010 << (6 * 5)
-    assert not p[0, :16].any() and not p[0, 32:40].any()
-
-
 # ------------------------------------------------------- input activations
 
 def _act_expected_bits(act: int, xs_float, dtype: str) -> np.ndarray:

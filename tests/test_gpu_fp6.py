@@ -1,10 +1,12 @@
 """GPU parity of W4A4 on the FP6 matrix path, through the C ABI, against the
-oracle: the FP6 operand packing byte for byte, the exact sums of the FP6
+oracle: every value of the FP6 operands the GPU writes, decoded by the tests
+from the format's description, equals the oracle's INT4 code; the exact sums of the FP6
 GEMM against the oracle's INT32 GEMM of the same INT4 codes bit for bit, and
 BF16 outputs within one BF16 ulp (identical to the INT8-path results)."""
 import numpy as np
 import pytest
 
+from fp6_format import assert_fp6_codes
 from gpu_util import assert_bf16_within_1ulp, bf16_bits, host, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +32,8 @@ def test_pack_fp6(qd, O, R, K):
     say(f"pack_fp6 R={R} K={K}")
     q = _codes((R, K), 800 + R)
     p = qd.pack_fp6(to_dev(q))
-    assert np.array_equal(host(p), O.pack_fp6(q))
+    assert p.shape == (R, 3 * K // 4)
+    assert_fp6_codes(host(p), q, "pack_fp6")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (256, 256, 128), (257, 300, 512), (64, 8, 1024),
@@ -120,7 +123,7 @@ def test_w4a4_fp6_full_size(qd, O):
     wq_o, sw_o = O.prepare_weights(W, 256, qmax=7)
     del W
     assert np.array_equal(host(sw).view(np.uint32), sw_o.view(np.uint32))
-    assert np.array_equal(host(w6), O.pack_fp6(wq_o))
+    assert_fp6_codes(host(w6), wq_o, "fp6 weights")
     say("  convrot_w4a4_linear_fp6")
     ws = torch.empty(qd.w4a4_fp6_workspace_size(M, K), dtype=torch.uint8, device=dev)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
@@ -140,8 +143,8 @@ def test_w4a4_fp6_full_size(qd, O):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("M,K", [(1, 256), (33, 1280), (300, 28672), (2, 65536)])
 def test_quantize_fp6_direct(qd, O, dtype, M, K):
-    """The rotating INT4 quantizer writing FP6 directly equals the oracle's
-    codes packed into the FP6 operand format, byte for byte."""
+    """The rotating INT4 quantizer writing FP6 directly: its scales equal the
+    oracle's bit for bit and its FP6 values decode to the oracle's codes."""
     say(f"quantize fp6 direct {dtype} M={M} K={K}")
     g = np.random.Generator(np.random.PCG64(840 + M + K))
     xf = g.standard_normal((M, K), dtype=np.float32)
@@ -156,7 +159,7 @@ def test_quantize_fp6_direct(qd, O, dtype, M, K):
     q6, s = qd.quantize_and_rotate_rowwise_fp6(xd)
     qo, so = O.quantize_rowwise(x, dtype, 256, qmax=7)
     assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
-    assert np.array_equal(host(q6), O.pack_fp6(qo))
+    assert_fp6_codes(host(q6), qo, "quantize fp6")
 
 
 def test_convrot_w4a4_linear_fp6_f32_input(qd, O):

@@ -5,6 +5,7 @@ the same kernels with other copy addresses)."""
 import numpy as np
 import pytest
 
+from fp6_format import assert_fp6_codes, unslice96
 from gpu_util import assert_bf16_within_1ulp, bf16_bits, host, say, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
@@ -225,7 +226,8 @@ def test_fp6_slice_weights_layout(qd, O, N, K):
     w4 = _int4((N, K), 300 + N + K)
     w6 = qd.pack_fp6(to_dev(w4))
     ws = qd.fp6_slice_weights(w6, K)
-    assert np.array_equal(host(ws), _slice96(O.pack_fp6(w4)))
+    assert np.array_equal(host(ws), _slice96(host(w6)))
+    assert_fp6_codes(unslice96(host(ws), N), w4, "fp6 sliced weights")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (257, 255, 256), (70, 130, 384), (300, 520, 1024), (513, 1000, 5376)])
@@ -236,7 +238,7 @@ def test_fp6_sliced_gemm_exact(qd, O, M, N, K):
     w6s = qd.fp6_slice_weights(qd.pack_fp6(to_dev(w4)), K)
     ref = O.gemm_i32(a4, w4)
     assert np.array_equal(host(qd.fp6_gemm_i32_sliced(a6, w6s)), ref)
-    assert np.array_equal(host(qd.fp6_gemm_i32_sliced(to_dev(_slice96(O.pack_fp6(a4))), w6s)), ref)
+    assert np.array_equal(host(qd.fp6_gemm_i32_sliced(to_dev(_slice96(host(a6))), w6s)), ref)
 
 
 def test_fp6_sliced_gemm_extremes(qd, O):
@@ -267,7 +269,7 @@ def test_quantize_fp6_sliced(qd, O, dtype, M, K):
     q6, s = qd.quantize_and_rotate_rowwise_fp6_sliced(xd)
     qo, so = O.quantize_rowwise(x, dtype, 256, qmax=7)
     assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
-    assert np.array_equal(host(q6), _slice96(O.pack_fp6(qo)))
+    assert_fp6_codes(unslice96(host(q6), M), qo, "fp6 sliced quantizer")
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 256, 8), (255, 512, 264), (300, 1024, 520), (257, 5376, 1000)])

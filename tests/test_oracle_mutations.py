@@ -30,8 +30,6 @@ MUTATIONS = {
     "gelu_erf_argument_sign": ("erfcl(-x / sqrtl(2.0L))", "erfcl(x / sqrtl(2.0L))"),
     "act_rounding_one_bit_short": ("round_to_grid(a, 7, -126)", "round_to_grid(a, 6, -126)"),
     "act_fp16_no_subnormals": ("round_to_grid(a, 10, -14)", "round_to_grid(a, 10, -24)"),
-    "fp6_tail_swap_on_bit4_only": ("int first = (int)(((r >> 3) ^ (r >> 4)) & 1);", "int first = (int)((r >> 4) & 1);"),
-    "fp6_exponent_bias_zero": ("ldexpf(1.0f + (float)m / 8.0f, (int)e - 1)", "ldexpf(1.0f + (float)m / 8.0f, (int)e)"),
     "relu_passes_negatives": ("case ORACLE_ACT_RELU: return x > 0.0L ? x : 0.0L;", "case ORACLE_ACT_RELU: return x;"),
     "attention_scale_missing": ("(double)sk[kr] * scale;", "(double)sk[kr];"),
     "attention_value_scale_dropped": ("num += sc[j] * ((double)sv[vr] * (double)vc[vr * D + d]);",
