@@ -56,6 +56,8 @@ def _bind(L):
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.oracle_attention_i8.restype = None
     L.oracle_attention_i8.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
+    L.oracle_attention_probs.restype = None
+    L.oracle_attention_probs.argtypes = [P, P, P, P, I64, I64, I64, I64, ctypes.c_double, P]
     L.oracle_bf16_rne.restype = ctypes.c_uint16
     L.oracle_bf16_rne.argtypes = [ctypes.c_float]
     L.oracle_hadamard256.argtypes = [P]
@@ -248,6 +250,20 @@ class Oracle:
         self.L.oracle_attention_i8(_p(qc), _p(sq), _p(kc), _p(sk), _p(vc), _p(sv), BH, Lq, Lk, D,
                                    float(1.0 / np.sqrt(D) if scale is None else scale), _p(out))
         return out
+
+    def attention_probs(self, qc, sq, kc, sk, scale=None) -> np.ndarray:
+        """Softmax probabilities of INT8 attention on codes: float64 [BH, Lq, Lk],
+        each row summing to 1 (the reading in qdiff_oracle.c)."""
+        qc, kc = (np.ascontiguousarray(a, dtype=np.int8) for a in (qc, kc))
+        sq, sk = (np.ascontiguousarray(a, dtype=np.float32) for a in (sq, sk))
+        BH, Lq, D = qc.shape
+        Lk = kc.shape[1]
+        if kc.shape != (BH, Lk, D) or sq.shape != (BH, Lq) or sk.shape != (BH, Lk):
+            raise ValueError("attention shapes disagree")
+        P = np.empty((BH, Lq, Lk), np.float64)
+        self.L.oracle_attention_probs(_p(qc), _p(sq), _p(kc), _p(sk), BH, Lq, Lk, D,
+                                      float(1.0 / np.sqrt(D) if scale is None else scale), _p(P))
+        return P
 
     def quantize_tokens(self, x, dtype: str = "bf16"):
         """Per-token INT8 codes and scales of x [BH, L, D] (the unrotated row rule)."""

@@ -446,6 +446,28 @@ void oracle_bf16_rne_array(const float* f, int64_t n, uint16_t* out) {
     for (int64_t i = 0; i < n; i++) out[i] = oracle_bf16_rne(f[i]);
 }
 
+/* One query row of INT8 attention on codes (reading in the header): e[j] =
+ * exp(S[i][j] - max_j S[i][j]) for the Lk keys of query qi's head; returns
+ * sum_j e[j]. */
+static double attention_row(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk, int64_t qi,
+                            int64_t Lq, int64_t Lk, int64_t D, double scale, double* e) {
+    const int64_t bh = qi / Lq;
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < Lk; j++) {
+        const int64_t kr = bh * Lk + j;
+        int64_t acc = 0;
+        for (int64_t d = 0; d < D; d++) acc += (int64_t)qc[qi * D + d] * (int64_t)kc[kr * D + d];
+        e[j] = (double)acc * (double)sq[qi] * (double)sk[kr] * scale;
+        if (e[j] > mx) mx = e[j];
+    }
+    double den = 0.0;
+    for (int64_t j = 0; j < Lk; j++) {
+        e[j] = exp(e[j] - mx);
+        den += e[j];
+    }
+    return den;
+}
+
 /* INT8 attention on codes (reading in the header).  qc [BH*Lq, D], kc and vc
  * [BH*Lk, D] INT8 codes with one FP32 scale per row; out [BH*Lq, D] double. */
 void oracle_attention_i8(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
@@ -455,19 +477,7 @@ void oracle_attention_i8(const int8_t* qc, const float* sq, const int8_t* kc, co
     for (int64_t qi = 0; qi < BH * Lq; qi++) {
         const int64_t bh = qi / Lq;
         double* sc = (double*)malloc((size_t)Lk * sizeof(double));
-        double mx = -INFINITY;
-        for (int64_t j = 0; j < Lk; j++) {
-            const int64_t kr = bh * Lk + j;
-            int64_t acc = 0;
-            for (int64_t d = 0; d < D; d++) acc += (int64_t)qc[qi * D + d] * (int64_t)kc[kr * D + d];
-            sc[j] = (double)acc * (double)sq[qi] * (double)sk[kr] * scale;
-            if (sc[j] > mx) mx = sc[j];
-        }
-        double den = 0.0;
-        for (int64_t j = 0; j < Lk; j++) {
-            sc[j] = exp(sc[j] - mx);
-            den += sc[j];
-        }
+        const double den = attention_row(qc, sq, kc, sk, qi, Lq, Lk, D, scale, sc);
         for (int64_t d = 0; d < D; d++) {
             double num = 0.0;
             for (int64_t j = 0; j < Lk; j++) {
@@ -477,5 +487,18 @@ void oracle_attention_i8(const int8_t* qc, const float* sq, const int8_t* kc, co
             out[qi * D + d] = num / den;
         }
         free(sc);
+    }
+}
+
+/* The softmax probabilities of INT8 attention on codes: P [BH*Lq, Lk]
+ * double, P[i][j] = exp(S[i][j] - max_j S[i][j]) / sum_j of the same, so
+ * that out = P (sv * v) row by row. */
+void oracle_attention_probs(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                            int64_t BH, int64_t Lq, int64_t Lk, int64_t D, double scale, double* P) {
+#pragma omp parallel for schedule(static)
+    for (int64_t qi = 0; qi < BH * Lq; qi++) {
+        double* pr = P + qi * Lk;
+        const double den = attention_row(qc, sq, kc, sk, qi, Lq, Lk, D, scale, pr);
+        for (int64_t j = 0; j < Lk; j++) pr[j] = pr[j] / den;
     }
 }

@@ -574,6 +574,29 @@ def check_attention_key_permutation(O):
     assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
 
 
+def check_attention_probs(O):
+    """The softmax probabilities: against torch's float64 softmax of the
+    scores of losslessly quantized inputs (an independent implementation);
+    rows sum to 1; and probabilities times dequantized values give the
+    oracle's attention output."""
+    import torch
+    g = np.random.default_rng(35)
+    BH, Lq, Lk, D, scale = 2, 7, 45, 64, 0.2
+    q = _lossless_rows(g, (BH, Lq, D), -9)
+    k = _lossless_rows(g, (BH, Lk, D), -8)
+    v = g.standard_normal((BH, Lk, D)).astype(np.float32)
+    qc, sq = O.quantize_tokens(q, "f32")
+    kc, sk = O.quantize_tokens(k, "f32")
+    vc, sv = O.quantize_tokens(v, "f32")
+    P = O.attention_probs(qc, sq, kc, sk, scale)
+    s = torch.from_numpy(q.astype(np.float64)) @ torch.from_numpy(k.astype(np.float64)).transpose(1, 2) * scale
+    ref = torch.softmax(s, dim=-1).numpy()
+    assert np.allclose(P, ref, rtol=1e-12, atol=1e-16), np.abs(P - ref).max()
+    assert np.allclose(P.sum(-1), 1.0, rtol=0, atol=1e-13)
+    out = O.attention_codes(qc, sq, kc, sk, vc, sv, scale)
+    assert np.allclose(np.matmul(P, sv[:, :, None].astype(np.float64) * vc), out, rtol=1e-12, atol=1e-15)
+
+
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]
 # Slow exhaustive checks run after the quick ones.
 CHECKS += [v for k, v in sorted(globals().items()) if k.startswith("slowcheck_")]

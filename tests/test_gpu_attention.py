@@ -1,12 +1,15 @@
 """GPU parity of int8_attention, through the C ABI, against the oracle: the
 per-token codes and scales in the workspace bit for bit, and every output
-within the bound derived from the kernel's rounding steps (probabilities and
-dequantized values rounded to BF16 for the value product, BF16 output):
-|out - exact| <= 2^-7 * max_j |sv[j] * vc[j][d]| + 2^-7 * |exact|, twice the
-documented bound."""
+within the rigorous bound derived from the kernel's rounding steps
+(tests/attention_bound.py: the dequantized values' BF16 rounding evaluated
+exactly with the oracle's softmax probabilities, the probabilities' BF16
+rounding, the FP32 sums and the BF16 output bounded term by term, no slack).
+On the CPU, tests/test_attention_bound.py shows that this bound rejects the
+oracle's output with one key or one 64-key block dropped."""
 import numpy as np
 import pytest
 
+from attention_bound import attention_bound
 from gpu_util import host, say
 
 pytestmark = pytest.mark.gpu
@@ -59,16 +62,18 @@ def _check(qd, O, dev, host_in, dtype, scale=0.0, what=""):
         assert np.array_equal(w[off:off + 4 * n].view(np.uint32).reshape(arr.shape), arr.view(np.uint32)), \
             f"{what}: scales"
         off += al(4 * n)
-    want = O.attention_codes(qc, sq, kc, sk, vc, sv, None if scale <= 0 else scale)
+    sc = None if scale <= 0 else scale
+    want = O.attention_codes(qc, sq, kc, sk, vc, sv, sc)
+    P = O.attention_probs(qc, sq, kc, sk, sc)
     got = _bits_of(out).astype(np.uint32) << 16
     got = got.view(np.float32).astype(np.float64)
-    vmax = np.abs(sv[:, :, None].astype(np.float64) * vc).max(axis=1)          # [BH, D]
-    bound = 2.0 ** -7 * vmax[:, None, :] + 2.0 ** -7 * np.abs(want)
+    bound = attention_bound(want, P, qc, sq, kc, sk, vc, sv, 1.0 / np.sqrt(D) if sc is None else sc)
     err = np.abs(got - want)
     bad = np.argwhere(~(err <= bound))
     assert bad.size == 0, f"{what}: {len(bad)} outputs outside the bound, first {tuple(bad[0])}: " \
                           f"got {got[tuple(bad[0])]} want {want[tuple(bad[0])]} bound {bound[tuple(bad[0])]}"
-    say(f"  {what}: max |err| / bound = {float((err / np.maximum(bound, 1e-300)).max()):.3f}")
+    say(f"  {what}: max |err| / bound = {float((err / np.maximum(bound, 1e-300)).max()):.3f}, "
+        f"median bound / |exact| = {float(np.median(bound / np.maximum(np.abs(want), 1e-300))):.3f}")
 
 
 @pytest.mark.parametrize("BH,Lq,Lk,D", [(1, 1, 1, 64), (2, 130, 200, 64), (3, 257, 64, 128), (1, 128, 1000, 128),
@@ -150,7 +155,9 @@ def test_attention_large_sampled(qd, O):
     kc, sk = O.quantize_tokens(h[1], "bf16")
     vc, sv = O.quantize_tokens(h[2], "bf16")
     want = O.attention_codes(qc[:, rows], sq[:, rows], kc, sk, vc, sv)
+    P = O.attention_probs(qc[:, rows], sq[:, rows], kc, sk)
     got = (_bits_of(out[:, torch.from_numpy(rows).cuda()]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    vmax = np.abs(sv[:, :, None].astype(np.float64) * vc).max(axis=1)
-    bound = 2.0 ** -7 * vmax[:, None, :] + 2.0 ** -7 * np.abs(want)
-    assert np.all(np.abs(got - want) <= bound)
+    bound = attention_bound(want, P, qc[:, rows], sq[:, rows], kc, sk, vc, sv, 1.0 / np.sqrt(128))
+    err = np.abs(got - want)
+    assert np.all(err <= bound), f"{int((err > bound).sum())} sampled outputs outside the bound"
+    say(f"  max |err| / bound = {float((err / bound).max()):.3f}")

@@ -36,6 +36,8 @@ MUTATIONS = {
                                       "num += sc[j] * (double)vc[vr * D + d];"),
     "attention_not_normalised": ("out[qi * D + d] = num / den;", "out[qi * D + d] = num;"),
     "attention_keys_of_head0": ("const int64_t kr = bh * Lk + j;", "const int64_t kr = j;"),
+    "attention_probs_not_normalised": ("for (int64_t j = 0; j < Lk; j++) pr[j] = pr[j] / den;",
+                                       "for (int64_t j = 0; j < Lk; j++) pr[j] = pr[j] / (den + 1.0);"),
     "attention_key_scale_of_query": ("(double)sq[qi] * (double)sk[kr]", "(double)sq[qi] * (double)sq[qi]"),
 }
 
