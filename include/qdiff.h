@@ -86,8 +86,10 @@ typedef enum { QD_ACT_NONE = 0, QD_ACT_GELU_TANH = 1, QD_ACT_GELU_ERF = 2, QD_AC
 
 /* Largest K accepted by the quantizers (a row stays in registers). */
 #define QD_MAX_K_QUANT 65536
-/* Largest K accepted by the GEMMs (keeps K * 128 * 128 < 2^31). */
-#define QD_MAX_K_GEMM 131072
+/* Largest K accepted by the GEMMs: the largest multiple of 16 with
+ * K * 128 * 128 < 2^31, so that raw codes (including -128, accepted by the
+ * GEMM entry points) can never overflow the INT32 accumulators. */
+#define QD_MAX_K_GEMM 131056
 
 /* Message for the last non-OK status returned on the calling thread
  * (empty string if none).  The pointer stays valid until the next call. */

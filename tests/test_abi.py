@@ -102,6 +102,30 @@ def test_gemm_i32_validation():
     assert st == qd.QD_EINVAL
 
 
+def test_gemm_k_limit():
+    """K * 128 * 128 must stay below 2^31 (raw codes include -128): K = 131072
+    is refused, the largest accepted K is 131056, on every GEMM entry point."""
+    L = qd.lib()
+    kmax = int(re.search(r"#define QD_MAX_K_GEMM (\d+)", open(HEADER).read()).group(1))
+    assert kmax == 131056 and kmax * 128 * 128 < 2 ** 31 <= (kmax + 16) * 128 * 128
+    for K in (131072, 131072 + 64):
+        st, msg = _status(L.qd_int8_gemm_i32, FAKE, 4, K, K, FAKE, 8, K, FAKE, 8, STREAM)
+        assert st == qd.QD_EUNSUPPORTED and "exceeds" in msg, (K, msg)
+        st, msg = _status(L.qd_int8_scaled_mm, FAKE, 4, K, K, FAKE, FAKE, 8, K, FAKE, NULL, FAKE, 8, STREAM)
+        assert st == qd.QD_EUNSUPPORTED and "exceeds" in msg, (K, msg)
+        st, msg = _status(L.qd_int8_gemm_i32_sliced, FAKE, 4, K, K, 0, FAKE, 8, FAKE, 8, STREAM)
+        assert st == qd.QD_EUNSUPPORTED and "exceeds" in msg, (K, msg)
+        st, msg = _status(L.qd_int4_gemm_i32, FAKE, 4, K, K, FAKE, 8, K // 2, FAKE, 8, STREAM)
+        assert st == qd.QD_EUNSUPPORTED and "exceeds" in msg, (K, msg)
+    K6 = 131072   # multiple of 128, above the limit: the FP6 GEMM refuses it too
+    st, msg = _status(L.qd_fp6_gemm_i32, FAKE, 4, K6, K6 // 4 * 3, FAKE, 8, K6 // 4 * 3, FAKE, 8, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "exceeds" in msg
+    # the limit itself passes validation (M = 0: no launch)
+    K = kmax
+    assert L.qd_int8_gemm_i32(FAKE, 0, K, K, FAKE, 8, K, FAKE, 8, STREAM) == qd.QD_OK
+    assert L.qd_int8_scaled_mm(FAKE, 0, K, K, FAKE, FAKE, 8, K, FAKE, NULL, FAKE, 8, STREAM) == qd.QD_OK
+
+
 def test_linear_validation_and_workspace():
     L = qd.lib()
     M, K, N = 10, 512, 64

@@ -180,6 +180,29 @@ def test_scaled_mm_bf16(qd, O, tiles, M, N, K, with_bias):
     say(f"  {n} of {yo.size} outputs differ from the oracle (allowed: 1 ulp)")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 7, 512), (257, 259, 1024), (129, 263, 768), (513, 1001, 5376),
+                                   (70, 1003, 320)])
+def test_scaled_mm_bf16_column_tail(qd, O, tiles, M, N, K):
+    """N % 8 in {1, 3, 7}: the BF16 epilogue's partial 8-column store at the
+    right edge, into a row stride padded to 8 whose padding must stay untouched."""
+    import torch
+    say(f"scaled_mm column tail M={M} N={N} K={K} tiles={tiles}")
+    g = np.random.Generator(np.random.PCG64(M + 3 * N + K))
+    a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    sx = (g.uniform(0.5, 2.0, M) * 2.0 ** -7).astype(np.float32)
+    sw = (g.uniform(0.5, 2.0, N) * 2.0 ** -12).astype(np.float32)
+    from synth import random_bf16
+    b = random_bf16(N, seed=K + 1, scale=0.1)
+    ldy = (N + 7) // 8 * 8
+    buf = torch.full((M, ldy), -7.0, dtype=torch.bfloat16, device="cuda")
+    y = qd.int8_scaled_mm(to_dev(a), to_dev(sx), to_dev(w), to_dev(sw), to_dev_bf16(b), out=buf[:, :N])
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, b)
+    n = assert_bf16_within_1ulp(bf16_bits(y), yo, "scaled_mm column tail")
+    assert torch.all(buf[:, N:] == -7.0), "the row padding past N was written"
+    say(f"  {n} of {yo.size} outputs differ from the oracle (allowed: 1 ulp)")
+
+
 # ------------------------------------------------------------- whole layer
 
 def test_int8_linear_tiny_config(qd, O):

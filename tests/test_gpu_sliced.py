@@ -163,6 +163,39 @@ def test_int8_linear_sliced(qd, O, tiles, act, M, rotate):
     assert_bf16_within_1ulp(bf16_bits(y), yo, "int8_linear_sliced")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 7, 512), (257, 259, 1024), (513, 1001, 5376), (70, 1003, 256)])
+def test_sliced_column_tail(qd, O, tiles, M, N, K):
+    """N % 8 in {1, 3, 7} on the K-sliced entry points: int8_scaled_mm_sliced
+    (row-major and K-sliced activation codes) and int8_linear_sliced, element
+    by element against the oracle; the padding of the output rows untouched."""
+    import torch
+    from synth import f32_to_bf16_bits
+    say(f"sliced column tail M={M} N={N} K={K} tiles={tiles}")
+    g = np.random.Generator(np.random.PCG64(4 * M + N + K))
+    a = _codes((M, K), 9 * M + K)
+    w = _codes((N, K), 13 * N + K)
+    sx = (g.random(M, dtype=np.float32) * 1e-3).astype(np.float32)
+    sw = (g.random(N, dtype=np.float32) * 1e-3).astype(np.float32)
+    bb = f32_to_bf16_bits((g.standard_normal(N, dtype=np.float32) * 0.1).astype(np.float32))
+    bd = to_dev_bf16(bb)
+    wsl = qd.slice_weights(to_dev(w))
+    ldy = (N + 7) // 8 * 8
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, bb)
+    for a_dev, what in ((to_dev(a), "row-major codes"), (to_dev(_slice_np(a)), "K-sliced codes")):
+        buf = torch.full((M, ldy), 3.0, dtype=torch.bfloat16, device="cuda")
+        y = qd.int8_scaled_mm_sliced(a_dev, to_dev(sx), wsl, to_dev(sw), bd, out=buf[:, :N])
+        assert_bf16_within_1ulp(bf16_bits(y), yo, f"scaled_mm_sliced column tail, {what}")
+        assert torch.all(buf[:, N:] == 3.0), "the row padding past N was written"
+    # the whole layer (rotated, with bias) on N % 8 != 0
+    x = f32_to_bf16_bits(g.standard_normal((M, K), dtype=np.float32))
+    W = (g.standard_normal((N, K), dtype=np.float32) * 0.02).astype(np.float32)
+    wqo, swo = O.prepare_weights(W)
+    buf = torch.full((M, ldy), 3.0, dtype=torch.bfloat16, device="cuda")
+    y = qd.int8_linear_sliced(to_dev_bf16(x), qd.slice_weights(to_dev(wqo)), to_dev(swo), bd, out=buf[:, :N])
+    assert_bf16_within_1ulp(bf16_bits(y), O.linear(x, wqo, swo, bb), "int8_linear_sliced column tail")
+    assert torch.all(buf[:, N:] == 3.0), "the row padding past N was written"
+
+
 def test_int8_linear_sliced_full_size(qd, O):
     """The M32700/K5376/N16128 workload in the launch configuration the
     benchmark times: the same bits as int8_linear on row-major weights, and
