@@ -362,6 +362,25 @@ qd_status_t qd_quantize_int8_tensorwise(const void* x, qd_dtype_t x_dtype, int64
                                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * qd_quantize_int8_tensorwise without a workspace argument.  The partial
+ * maxima live in a fixed array inside the library: 2048 floats (8 KB), one
+ * copy per GPU, held until the process ends.  The partial count is
+ * min(M, 2048), so every input qd_quantize_int8_tensorwise accepts fits;
+ * a count above the array would be QD_EUNSUPPORTED.  Arguments, results
+ * (bit for bit) and errors as qd_quantize_int8_tensorwise; QD_EHIP if the
+ * array's device address cannot be found.  Allocates and frees nothing.
+ * Every call on one GPU uses the same array, and each call writes every
+ * partial it reads before reading it (nothing needs clearing), so calls in
+ * one stream order are safe; calls that overlap on one GPU (other streams
+ * or threads) race and must be serialised by the caller.
+ */
+qd_status_t qd_quantize_int8_tensorwise_noalloc(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                                int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                                hipStream_t stream);
+
+/*
  * qd_int8_scaled_mm with the scale granularity chosen per operand:
  *   y[m, n] = bf16_rne(((float)acc[m, n] * sa(m)) * sw(n) + bias[n]),
  *   sa(m) = a_scale[m] if a_scale_len == M, a_scale[0] if a_scale_len == 1;

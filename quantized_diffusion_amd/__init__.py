@@ -41,6 +41,7 @@ __all__ = [
     "slice_weights", "int8_linear_sliced", "int8_scaled_mm_sliced", "int8_gemm_i32_sliced",
     "quantize_and_rotate_rowwise_sliced", "fp6_slice_weights", "quantize_and_rotate_rowwise_fp6_sliced",
     "fp6_scaled_mm_sliced", "fp6_gemm_i32_sliced", "convrot_w4a4_linear_fp6_sliced",
+    "quantize_int8_tensorwise_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqdiff.so")
@@ -63,6 +64,7 @@ EXPORTED_SYMBOLS = (
     "qd_int8_slice_weights", "qd_int8_linear_sliced", "qd_int8_scaled_mm_sliced", "qd_int8_gemm_i32_sliced",
     "qd_quantize_and_rotate_rowwise_sliced", "qd_fp6_slice_weights", "qd_quantize_and_rotate_rowwise_fp6_sliced",
     "qd_fp6_scaled_mm_sliced", "qd_fp6_gemm_i32_sliced", "qd_convrot_w4a4_linear_fp6_sliced",
+    "qd_quantize_int8_tensorwise_noalloc",
 )
 
 
@@ -125,6 +127,8 @@ def lib():
         L.qd_quantize_tensorwise_workspace_size.argtypes = []
         L.qd_quantize_int8_tensorwise.restype = St
         L.qd_quantize_int8_tensorwise.argtypes = [P, St, I64, I64, I64, P, I64, P, P, SZ, P]
+        L.qd_quantize_int8_tensorwise_noalloc.restype = St
+        L.qd_quantize_int8_tensorwise_noalloc.argtypes = [P, St, I64, I64, I64, P, I64, P, P]
         L.qd_int8_scaled_mm_ex.restype = St
         L.qd_int8_scaled_mm_ex.argtypes = [P, I64, I64, I64, P, I64, P, I64, I64, P, I64, P, P, I64, P]
         L.qd_int8_linear_act.restype = St
@@ -314,6 +318,22 @@ def quantize_int8_tensorwise(x, out_q=None, out_scale=None, workspace=None):
     _check(lib().qd_quantize_int8_tensorwise(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(out_q),
                                              out_q.stride(0), _ptr(out_scale), _ptr(workspace),
                                              workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out_q, out_scale
+
+
+def quantize_int8_tensorwise_noalloc(x, out_q, out_scale):
+    """quantize_int8_tensorwise through the library's allocation-free entry
+    point: the caller passes the outputs (codes int8 [M, K], scale fp32 [1]);
+    the partial maxima live in the library's fixed per-GPU array, so nothing
+    is allocated.  Calls overlapping on one GPU race (see qdiff.h)."""
+    torch = _torch()
+    _mat(x, "x")
+    dev = _dev(x, out_q, out_scale)
+    M, K = x.shape
+    _out(out_q, (M, K), torch.int8, "out_q")
+    _out(out_scale, (1,), torch.float32, "out_scale")
+    _check(lib().qd_quantize_int8_tensorwise_noalloc(_ptr(x), _dtype_code(x), M, K, x.stride(0), _ptr(out_q),
+                                                     out_q.stride(0), _ptr(out_scale), _stream(dev)))
     return out_q, out_scale
 
 

@@ -229,6 +229,25 @@ qd_status_t qd_quantize_int8_tensorwise(const void* x, qd_dtype_t x_dtype, int64
                                                       static_cast<float*>(workspace), stream));
 }
 
+qd_status_t qd_quantize_int8_tensorwise_noalloc(const void* x, qd_dtype_t x_dtype, int64_t M, int64_t K,
+                                                int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                                                hipStream_t stream) {
+    const char* fn = "qd_quantize_int8_tensorwise_noalloc";
+    qd_status_t st = check_quant(fn, x, x_dtype, M, K, ldx, false, 0, q, ldq, scale);
+    if (st != QD_OK) return st;
+    if (M == 0) return ok();
+    float* partial = nullptr;
+    size_t cap = 0;
+    const hipError_t e = qd::tensorwise_scratch(stream, &partial, &cap);
+    if (e != hipSuccess)
+        return fail(QD_EHIP, fn, "locating the library's scratch array failed: %s", hipGetErrorString(e));
+    // pass 1 writes one partial per workgroup, min(M, kTensorwisePartials) of them
+    const int64_t need = M < qd::kTensorwisePartials ? M : qd::kTensorwisePartials;
+    if ((size_t)need > cap)
+        return fail(QD_EUNSUPPORTED, fn, "%lld partial maxima exceed the %zu-float scratch array", (long long)need, cap);
+    return hip_status(fn, qd::launch_quant_tensorwise(x, (int)x_dtype, M, K, ldx, q, ldq, scale, partial, stream));
+}
+
 size_t qd_int8_linear_workspace_size(int64_t M, int64_t K) {
     if (M <= 0 || K <= 0) return 0;
     return ws_codes_bytes(M, K) + round_up((size_t)M * sizeof(float), kAlign);

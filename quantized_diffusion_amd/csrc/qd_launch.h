@@ -32,6 +32,9 @@ hipError_t launch_input_act(const void* x, int dtype, int64_t n, int act, void* 
 constexpr int kTensorwisePartials = 2048;
 hipError_t launch_quant_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                    int64_t ldq, float* scale, float* partial, hipStream_t stream);
+// The library's fixed partial-maxima array on the GPU that runs `stream`
+// (kTensorwisePartials floats): its device address and size in floats.
+hipError_t tensorwise_scratch(hipStream_t stream, float** partial, size_t* floats);
 
 // INT8 attention on per-token codes: qc [BH*Lq, D], kc / vc [BH*Lk, D] with
 // FP32 scales per row; out [BH*Lq, D] BF16; D = 64 or 128.

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "qd_device.h"
 #include "qd_launch.h"
 #include "qd_quant.h"
@@ -151,7 +153,46 @@ hipError_t launch_tw(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q
     return hipGetLastError();
 }
 
+// Partial maxima of the allocation-free entry point: kTensorwisePartials
+// floats (8 KB), one copy per GPU, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); it passes the device address looked up below.
+static __device__ __align__(256) float scratch[kTensorwisePartials];
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+// Device address of `scratch` on the GPU that runs `stream`, looked up with
+// hipGetSymbolAddress once per device (that device current) and cached.
+hipError_t tensorwise_scratch(hipStream_t stream, float** out, size_t* floats) {
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = 0;
+    // the null stream runs on the calling thread's current device
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float*>(p);
+    }
+    *out = addr[dev];
+    *floats = kTensorwisePartials;
+    return hipSuccess;
+}
 
 hipError_t launch_quant_tensorwise(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                    int64_t ldq, float* scale, float* partial, hipStream_t stream) {

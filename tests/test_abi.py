@@ -451,3 +451,19 @@ def test_output_tensor_checks():
     with pytest.raises(ValueError):
         qd._f6_rows(torch.empty(4, 90, dtype=torch.uint8), 128, "a6")
     qd._f6_rows(torch.empty(4, 96, dtype=torch.uint8), 128, "a6")
+
+
+def test_tensorwise_noalloc_validation():
+    """The allocation-free tensor-wise entry point checks its arguments as the
+    workspace entry point does, before any HIP call."""
+    L = qd.lib()
+    f = L.qd_quantize_int8_tensorwise_noalloc
+    assert f(FAKE, Q, 0, 512, 512, FAKE, 512, FAKE, STREAM) == qd.QD_OK           # empty: nothing to do
+    st, msg = _status(f, NULL, Q, 4, 512, 512, FAKE, 512, FAKE, STREAM)
+    assert st == qd.QD_EINVAL and "null" in msg
+    st, msg = _status(f, FAKE, Q, 4, 40, 40, FAKE, 48, FAKE, STREAM)
+    assert st == qd.QD_EUNSUPPORTED
+    st, msg = _status(f, FAKE, Q, 4, 512, 500, FAKE, 512, FAKE, STREAM)
+    assert st == qd.QD_EINVAL
+    st, msg = _status(f, FAKE_ODD, Q, 4, 512, 512, FAKE, 512, FAKE, STREAM)
+    assert st == qd.QD_EUNSUPPORTED and "aligned" in msg
