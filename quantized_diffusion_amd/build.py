@@ -1,4 +1,5 @@
-"""Build libqdiff.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
+"""Build libqdiff.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc,
+and libqdmeasure.so (the benchmark's measurement kernels, measure/*.hip).
 
 Usage: python -m quantized_diffusion_amd.build [-j JOBS] [-v]
 """
@@ -16,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqdiff.so")
+MEASURE_SRC = os.path.join(PKG, "measure")
+MEASURE_LIB = os.path.join(PKG, "libqdmeasure.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -58,7 +61,20 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    _link(sorted(glob.glob(os.path.join(MEASURE_SRC, "*.hip"))), MEASURE_LIB, verbose)
     return LIB
+
+
+def _link(srcs, lib: str, verbose: bool) -> None:
+    """One shared library straight from its sources."""
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", *srcs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build of {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -44,3 +44,24 @@ def test_traffic_only_for_the_current_kernel(tmp_path, monkeypatch):
     tf.write_text("not json")
     assert bench.load_traffic("W") is None
 
+
+
+def test_per_cu_clock_matches_samples_per_compute_unit():
+    """Cycle counters are compared only within one compute unit (earliest sample
+    before, latest after); CUs missing from either side are left out."""
+    import numpy as np
+    rate = 100000.0                         # kHz: 100 MHz wall counter
+    before = [  # cycle, wall, xcd, hw_id (CU field bits 8..15)
+        (1_000_000, 500, 0, 0x0100), (1_000_900, 509, 0, 0x0100),   # CU (0, 1): earliest at wall 500
+        (9_000_000, 700, 1, 0x0100),                                # CU (1, 1): another counter base
+        (5, 600, 2, 0x0300)]                                         # CU (2, 3): no sample after
+    after = [
+        (1_000_000 + 2_000 * 1000, 1500, 0, 0x0100), (1_000_000 + 1_500 * 1000, 1250, 0, 0x0100),
+        (9_000_000 + 1_800 * 2000, 2700, 1, 0x0100)]
+    pad = lambda rows: rows + [rows[0]] * (4 - len(rows))
+    s = np.array([pad(before), pad(after)], dtype=np.int64)
+    cu = bench.per_cu_clock(s, rate)
+    assert set(cu) == {(0, 1), (1, 1)}
+    # CU (0, 1): 2e6 cycles over 1000 wall ticks of 10 ns = 10 us -> 200000 MHz scaled: cycles / us
+    assert abs(cu[(0, 1)] - 2_000_000 / 10.0) < 1e-6
+    assert abs(cu[(1, 1)] - 3_600_000 / 20.0) < 1e-6
