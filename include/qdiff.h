@@ -328,15 +328,17 @@ qd_status_t qd_int8_attention(const void* q, const void* k, const void* v, qd_dt
  * and qd_int8_gemm_i32.  QD_GEMM_TILES_AUTO (the default) chooses 256 x 256
  * or 256 x 384 tiles by shape (the wide tile moves 17 % fewer bytes from L2
  * into LDS per MAC; the narrow one wastes less on small or ragged grids); the
- * other values fix one tile for every later launch in the process, for
+ * other values fix one tile for the calling thread's later launches, for
  * tuning and for testing both kernels on the same shapes.  Results are
- * identical either way.  The setting is process-wide (not per stream) and
- * read when a GEMM is enqueued.  QD_EINVAL for any other value.
+ * identical either way.  The setting belongs to the calling thread (each
+ * thread starts with QD_GEMM_TILES_AUTO; one thread's setting never changes
+ * another's launches) and is read when a GEMM is enqueued.  QD_EINVAL for
+ * any other value.
  */
 typedef enum { QD_GEMM_TILES_AUTO = 0, QD_GEMM_TILES_256x256 = 1, QD_GEMM_TILES_256x384 = 2 } qd_gemm_tiles_t;
 qd_status_t qd_set_gemm_tiles(qd_gemm_tiles_t tiles);
 /* The tile (QD_GEMM_TILES_256x256 or QD_GEMM_TILES_256x384) an INT8-weight
- * GEMM of this shape would use under the current setting. */
+ * GEMM of this shape would use under the calling thread's setting. */
 qd_gemm_tiles_t qd_int8_gemm_tiles(int64_t M, int64_t N, int64_t K);
 
 /*

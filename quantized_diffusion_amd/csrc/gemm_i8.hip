@@ -45,7 +45,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <atomic>
 
 #include "qd_device.h"
 #include "qd_launch.h"
@@ -1158,14 +1157,16 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     }
 }
 
-std::atomic<int> g_tile_policy{GEMM_TILES_AUTO};
+// The tile setting of the calling thread (qd_set_gemm_tiles): a thread's
+// setting never changes another thread's launches.
+thread_local int g_tile_policy = GEMM_TILES_AUTO;
 
 // Tile shape for an INT8-weight GEMM with K % 64 == 0.  Cost model: rounds
 // of 256 concurrent workgroups (one per CU), a round of wide tiles taking
 // 1.41x a round of 256 x 256 tiles (1.5x the MACs at the ~6 % better rate
 // measured on M32700/K5376/N16128).
 bool use_wide(int64_t M, int64_t N) {
-    const int policy = g_tile_policy.load(std::memory_order_relaxed);
+    const int policy = g_tile_policy;
     if (policy != GEMM_TILES_AUTO) return policy == GEMM_TILES_256x384;
     const int64_t tm = (M + BM - 1) / BM;
     const int64_t r1 = (tm * ((N + BN - 1) / BN) + 255) / 256;
@@ -1227,7 +1228,7 @@ hipError_t launch_slice_rows(const uint8_t* src, int64_t ld, int64_t R, int64_t 
 
 }  // namespace
 
-void set_gemm_tile_policy(int policy) { g_tile_policy.store(policy, std::memory_order_relaxed); }
+void set_gemm_tile_policy(int policy) { g_tile_policy = policy; }
 
 bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K) { return K % BK == 0 && use_wide(M, N); }
 

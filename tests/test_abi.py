@@ -467,3 +467,21 @@ def test_tensorwise_noalloc_validation():
     assert st == qd.QD_EINVAL
     st, msg = _status(f, FAKE_ODD, Q, 4, 512, 512, FAKE, 512, FAKE, STREAM)
     assert st == qd.QD_EUNSUPPORTED and "aligned" in msg
+
+
+def test_gemm_tiles_setting_is_per_thread():
+    """A thread's tile setting does not change the tiles another thread's launches use."""
+    import threading
+    L = qd.lib()
+    shape = (32700, 16128, 5376)
+    auto = L.qd_int8_gemm_tiles(*shape)
+    assert L.qd_set_gemm_tiles(qd.GEMM_TILES_256x256) == qd.QD_OK
+    try:
+        seen = {}
+        t = threading.Thread(target=lambda: seen.update(other=L.qd_int8_gemm_tiles(*shape)))
+        t.start()
+        t.join()
+        assert seen["other"] == auto                                   # the other thread: still automatic
+        assert L.qd_int8_gemm_tiles(*shape) == qd.GEMM_TILES_256x256   # this thread: fixed
+    finally:
+        L.qd_set_gemm_tiles(qd.GEMM_TILES_AUTO)
