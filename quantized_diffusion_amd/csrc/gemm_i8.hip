@@ -1157,23 +1157,6 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     }
 }
 
-// The tile setting of the calling thread (qd_set_gemm_tiles): a thread's
-// setting never changes another thread's launches.
-thread_local int g_tile_policy = GEMM_TILES_AUTO;
-
-// Tile shape for an INT8-weight GEMM with K % 64 == 0.  Cost model: rounds
-// of 256 concurrent workgroups (one per CU), a round of wide tiles taking
-// 1.41x a round of 256 x 256 tiles (1.5x the MACs at the ~6 % better rate
-// measured on M32700/K5376/N16128).
-bool use_wide(int64_t M, int64_t N) {
-    const int policy = g_tile_policy;
-    if (policy != GEMM_TILES_AUTO) return policy == GEMM_TILES_256x384;
-    const int64_t tm = (M + BM - 1) / BM;
-    const int64_t r1 = (tm * ((N + BN - 1) / BN) + 255) / 256;
-    const int64_t r2 = (tm * ((N + BNW - 1) / BNW) + 255) / 256;
-    return 141 * r2 < 100 * r1;
-}
-
 // Operand addressing: row-major (row n at wq + n * ldw), or K-sliced (byte
 // (n, k) at (k / 64) * N * 64 + n * 64 + k % 64, K % 64 == 0): the 64-byte
 // K slices of consecutive rows are adjacent, so each copy instruction of
@@ -1188,7 +1171,7 @@ hipError_t launch(const int8_t* aq, int64_t lda, const int8_t* wq, int64_t ldw, 
     const int64_t w_ss = w_sliced ? N * BK : BK;
     const int64_t a_rs = a_sliced ? BK : lda;
     const int64_t a_ss = a_sliced ? M * BK : BK;
-    if (K % BK == 0 && use_wide(M, N))
+    if (gemm_uses_wide_tiles(M, N, K))
         gemm_i8_w12_kernel<MODE><<<dim3((unsigned)(((M + BM - 1) / BM) * ((N + BNW - 1) / BNW))), dim3(NT8), 0,
                                    stream>>>(aq, a_rs, a_ss, wq, w_rs, w_ss, (int)M, (int)N, (int)K, ep);
     else if (K % BK == 0)
@@ -1227,10 +1210,6 @@ hipError_t launch_slice_rows(const uint8_t* src, int64_t ld, int64_t R, int64_t 
 }
 
 }  // namespace
-
-void set_gemm_tile_policy(int policy) { g_tile_policy = policy; }
-
-bool gemm_uses_wide_tiles(int64_t M, int64_t N, int64_t K) { return K % BK == 0 && use_wide(M, N); }
 
 hipError_t launch_gemm_bf16(const int8_t* aq, int64_t lda, const float* a_scale, const int8_t* wq,
                             int64_t ldw, const float* w_scale, const void* bias, void* y,
