@@ -734,6 +734,9 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     auto first_half = [&](int t) {
         // first K half of slice t; its second half's fragments; weight copies of slice t+NS-1
         const bool late = t + NS - 1 < nk;
+        // raised priority while this half's MFMAs issue, normal again for the
+        // barrier wait (measured: 0.6 % faster, same results)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j < 3) w1[j] = rd_w(t, 1, j);
@@ -751,6 +754,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         }
         acc[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[0], a[0], acc[0][0], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         wait_groups<PER>(min(nk - 1, t + NS - 1) - (t + 1));
         __builtin_amdgcn_s_barrier();
