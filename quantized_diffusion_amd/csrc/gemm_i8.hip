@@ -907,9 +907,9 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
 // magnitude <= K * 49 < 2^24, so the FP32 accumulator holds the exact INT32
 // sum and the epilogue sees the same value as the INT8 path.
 //
-// The loop is the eight-wave kernel's (same stage protocol, barrier between
-// the two K halves of a slice) with a slice of 128 values: 96 bytes per row,
-// one MFMA K step (64 values, 48 bytes) per half.  Operands arrive in the FP6
+// The loop is the eight-wave INT8 kernel's protocol (barrier between the two
+// K halves of a slice) with a slice of 128 values: 96 bytes per row, one
+// MFMA K step (64 values, 48 bytes) per half.  Operands arrive in the FP6
 // operand format (qdiff.h): per 64-value block, [piece 0 bytes 0..15 |
 // piece 1 bytes 0..15 | tails], the tails swapped when bits 3 and 4 of the
 // row differ.  In LDS a row's slice is six 16-byte slots (96 bytes, so one
@@ -948,12 +948,27 @@ __device__ __forceinline__ u32x2 epi_bf16x4_f(const float* a4, float sx, const f
     return pk;
 }
 
+// ---------------------------------------------------------------------------
+// The FP6 kernel: a 256 x 256 tile computed by four waves (one per SIMD),
+// each 128 x 128 in sixteen accumulators held in the accumulator registers,
+// so that every fragment read from LDS feeds four MFMAs (eight waves of
+// 128 x 64 need a third more LDS reads per MFMA and ran 2-7 % slower).  The
+// MFMA operands are 6-register FP6 tuples (the intrinsic's 6-dword form),
+// two registers fewer per fragment than the 8-dword builtin.
+typedef int32_t i32x6 __attribute__((ext_vector_type(6)));
+__device__ f32x16 mfma_f6x6(i32x6 a, i32x6 b, f32x16 c, int cbsz, int blgp, int opsel_a, int scale_a, int opsel_b,
+                            int scale_b) __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
+
+constexpr int NT4 = 256;
+constexpr int F6W4_PER = 12;   // copies per slice per thread (6 activation + 6 weight)
+
 template <int MODE>
-__global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __restrict__ A, int64_t lda, int64_t a_ss,
+__global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __restrict__ A, int64_t lda, int64_t a_ss,
                                                            const uint8_t* __restrict__ W, int64_t ldw, int64_t w_ss,
                                                            int M, int N, int K, EpiArgs ep) {
     constexpr int NS = F6_NS;
     constexpr int STG = F6_STG;
+    constexpr int PER = F6W4_PER;
     constexpr int RING = NS * STG > 256 * 512 ? NS * STG : 256 * 512;
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING + EPI_LDS];
     float* l_sx = reinterpret_cast<float*>(smem + RING);
@@ -978,82 +993,60 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
+    const int wm = wave & 1;    // 128-row half of the activation tile
+    const int wn = wave >> 1;   // 128-row half of the weight tile
 
     if (MODE == MODE_BF16) {
-        if (tid < 256) {
-            const int m = min(m0 + tid, M - 1);
-            l_sx[tid] = ep.a_scale[m * ep.a_step];
-        } else {
-            const int c = tid - 256;
-            const int n = min(n0 + c, N - 1);
-            l_sw[c] = ep.w_scale[n * ep.w_step];
-            l_b[c] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
-        }
+        l_sx[tid] = ep.a_scale[min(m0 + tid, M - 1) * ep.a_step];
+        const int n = min(n0 + tid, N - 1);
+        l_sw[tid] = ep.w_scale[n * ep.w_step];
+        l_b[tid] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
     }
 
-    // copies: instruction i (0..2) of wave w fills the 16-byte LDS slots
-    // (3w + i) * 64 + lane of an operand's 24 KB stage part; slot q holds
-    // row q / 6, physical slot q % 6 = logical slot + f6_rot(row) (mod 6)
-    const uint8_t* ga[3];
-    const uint8_t* gw[3];
-    uint32_t lslot[3];
+    // copies: instruction i (0..5) of wave w fills the 16-byte LDS slots
+    // (6w + i) * 64 + lane of an operand's 24 KB stage part (layout as in
+    // gemm_f6_w8_kernel)
+    const uint8_t* ga[6];
+    const uint8_t* gw[6];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int q = (3 * wave + i) * 64 + lane;
+    for (int i = 0; i < 6; ++i) {
+        const int q = (6 * wave + i) * 64 + lane;
         const int row = q / 6;
         const int phys = q - 6 * row;
-        const int logical = (phys + f6_rot(row)) % 6;   // rot is 0 or 3: its own inverse
+        const int logical = (phys + f6_rot(row)) % 6;
         ga[i] = A + (int64_t)min(m0 + row, M - 1) * lda + 16 * logical;
         gw[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 16 * logical;
-        lslot[i] = (uint32_t)((3 * wave + i) * 1024);
     }
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
-        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
-        if (part == 0) dma16(sb + lslot[i], reinterpret_cast<const int8_t*>(ga[i] + (int64_t)u * a_ss));
-        else dma16(sb + BM * F6_RB + lslot[i], reinterpret_cast<const int8_t*>(gw[i] + (int64_t)u * w_ss));
-    };
-    auto issue = [&](int u) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) copy_part(u, 0, i);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) copy_part(u, 1, i);
+        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG) + (uint32_t)((6 * wave + i) * 1024);
+        if (part == 0) dma16(sb, reinterpret_cast<const int8_t*>(ga[i] + (int64_t)u * a_ss));
+        else dma16(sb + BM * F6_RB, reinterpret_cast<const int8_t*>(gw[i] + (int64_t)u * w_ss));
     };
 
     const int fr = lane & 31;
     const int fk = lane >> 5;
-    // LDS byte offsets of a lane's piece in K half kk: 16-byte head, 8-byte tail
-    int a_h[4][2], a_t[4][2], w_h[2][2], w_t[2][2];
+    // fragment b covers rows base + 32 b + lane % 32; the slot rotation and tail
+    // swap depend on row bits 2..4 only, i.e. on lane % 32, so all b share them
+    const int ra = wm * 128 + fr, rw = wn * 128 + fr;
+    int a_h[2], a_t[2], w_h[2], w_t[2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int r = wm * 128 + b * 32 + fr;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            a_h[b][kk] = r * F6_RB + 16 * ((3 * kk + fk + f6_rot(r)) % 6);
-            a_t[b][kk] = r * F6_RB + 16 * ((3 * kk + 2 + f6_rot(r)) % 6) + 8 * (fk ^ f6_swp(r));
-        }
+    for (int kk = 0; kk < 2; ++kk) {
+        a_h[kk] = ra * F6_RB + 16 * ((3 * kk + fk + f6_rot(ra)) % 6);
+        a_t[kk] = ra * F6_RB + 16 * ((3 * kk + 2 + f6_rot(ra)) % 6) + 8 * (fk ^ f6_swp(ra));
+        w_h[kk] = BM * F6_RB + rw * F6_RB + 16 * ((3 * kk + fk + f6_rot(rw)) % 6);
+        w_t[kk] = BM * F6_RB + rw * F6_RB + 16 * ((3 * kk + 2 + f6_rot(rw)) % 6) + 8 * (fk ^ f6_swp(rw));
     }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int r = wn * 64 + b * 32 + fr;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            w_h[b][kk] = BM * F6_RB + r * F6_RB + 16 * ((3 * kk + fk + f6_rot(r)) % 6);
-            w_t[b][kk] = BM * F6_RB + r * F6_RB + 16 * ((3 * kk + 2 + f6_rot(r)) % 6) + 8 * (fk ^ f6_swp(r));
-        }
-    }
-    auto rd = [&](int u, int head, int tail) {
-        const int8_t* base = smem + (u % NS) * STG;
+    auto rd = [&](int u, int head, int tail, int b) {
+        const int8_t* base = smem + (u % NS) * STG + b * 32 * F6_RB;
         const i32x4 h = *reinterpret_cast<const i32x4*>(base + head);
         const u32x2 t = *reinterpret_cast<const u32x2*>(base + tail);
-        return i32x8{h[0], h[1], h[2], h[3], (int32_t)t[0], (int32_t)t[1], 0, 0};
+        return i32x6{h[0], h[1], h[2], h[3], (int32_t)t[0], (int32_t)t[1]};
     };
 
-    f32x16 acc[2][4];
+    f32x16 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -1062,74 +1055,78 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     const int nk = K / F6_BK;
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
-        if (u < nk) issue(u);
-    wait_groups<F6_PER>(min(nk, NS - 1) - 1);
+        if (u < nk) {
+#pragma unroll
+            for (int i = 0; i < 6; ++i) copy_part(u, 0, i);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) copy_part(u, 1, i);
+        }
+    wait_groups<PER>(min(nk, NS - 1) - 1);
     __syncthreads();
     if (NS - 1 < nk) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) copy_part(NS - 1, 0, i);
+        for (int i = 0; i < 6; ++i) copy_part(NS - 1, 0, i);
     }
 
-    i32x8 a0[4], w0[2], a1[4], w1[2];
+    i32x6 a0[4], w0[4], a1[4], w1[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) a0[b] = rd(0, a_h[b][0], a_t[b][0]);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) w0[b] = rd(0, w_h[b][0], w_t[b][0]);
+    for (int b = 0; b < 4; ++b) {
+        a0[b] = rd(0, a_h[0], a_t[0], b);
+        w0[b] = rd(0, w_h[0], w_t[0], b);
+    }
     // STEADY: a slice with NS more after it (every copy issued, one slice in flight)
     auto slice = [&](int t, auto steady_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
         const bool late = STEADY || t + NS - 1 < nk;
-        // first half of slice t; reads of its second half; weight copies of slice t+NS-1
+        // first K step of slice t; reads of its second step; weight copies of slice t+NS-1
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            w1[q] = rd(t, w_h[q][1], w_t[q][1]);
-            a1[2 * q] = rd(t, a_h[2 * q][1], a_t[2 * q][1]);
-            a1[2 * q + 1] = rd(t, a_h[2 * q + 1][1], a_t[2 * q + 1][1]);
+        for (int q = 0; q < 4; ++q) {
+            w1[q] = rd(t, w_h[1], w_t[1], q);
+            a1[q] = rd(t, a_h[1], a_t[1], q);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[q], a0[j], acc[q][j], 2, 2, 0, 127,
-                                                                            0, 127);
+            for (int j = 0; j < 4; ++j) acc[q][j] = mfma_f6x6(w0[q], a0[j], acc[q][j], 2, 2, 0, 127, 0, 127);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (late) {
-                copy_part(t + NS - 1, 1, q);
+                if (q == 0) { copy_part(t + NS - 1, 1, 0); copy_part(t + NS - 1, 1, 1); }
                 if (q == 1) copy_part(t + NS - 1, 1, 2);
+                if (q == 2) { copy_part(t + NS - 1, 1, 3); copy_part(t + NS - 1, 1, 4); }
+                if (q == 3) copy_part(t + NS - 1, 1, 5);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        acc[0][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[0], a1[0], acc[0][0], 2, 2, 0, 127, 0, 127);
+        acc[0][0] = mfma_f6x6(w1[0], a1[0], acc[0][0], 2, 2, 0, 127, 0, 127);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        if (STEADY) wait_vmcnt<(NS - 2) * F6_PER>();
-        else wait_groups<F6_PER>(min(nk - 1, t + NS - 1) - (t + 1));
+        if (STEADY) wait_vmcnt<(NS - 2) * PER>();
+        else wait_groups<PER>(min(nk - 1, t + NS - 1) - (t + 1));
         __builtin_amdgcn_s_barrier();
         const bool early = STEADY || t + NS < nk;
-        // second half of slice t; reads of slice t+1's first half; activation copies of slice t+NS
+        // second K step of slice t; reads of slice t+1's first step; activation copies of slice t+NS
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            w0[q] = rd(t + 1, w_h[q][0], w_t[q][0]);
-            a0[2 * q] = rd(t + 1, a_h[2 * q][0], a_t[2 * q][0]);
-            a0[2 * q + 1] = rd(t + 1, a_h[2 * q + 1][0], a_t[2 * q + 1][0]);
+        for (int q = 0; q < 4; ++q) {
+            w0[q] = rd(t + 1, w_h[0], w_t[0], q);
+            a0[q] = rd(t + 1, a_h[0], a_t[0], q);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (q != 0 || j > 0)
-                    acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[q], a1[j], acc[q][j], 2, 2, 0,
-                                                                                127, 0, 127);
+                if (q != 0 || j != 0) acc[q][j] = mfma_f6x6(w1[q], a1[j], acc[q][j], 2, 2, 0, 127, 0, 127);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (early) {
-                copy_part(t + NS, 0, q);
+                if (q == 0) { copy_part(t + NS, 0, 0); copy_part(t + NS, 0, 1); }
                 if (q == 1) copy_part(t + NS, 0, 2);
+                if (q == 2) { copy_part(t + NS, 0, 3); copy_part(t + NS, 0, 4); }
+                if (q == 3) copy_part(t + NS, 0, 5);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
     int t = 0;
@@ -1139,15 +1136,16 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
     if (MODE == MODE_BF16) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();
+        // acc[i][j][4 g4 + e]: (n, m) = (wn*128 + 32 i + 8 g4 + 4 fk + e, wm*128 + 32 j + fr) in the tile
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = wm * 128 + 32 * j + fr;
             const float sx = l_sx[r];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int c = wn * 64 + 32 * i + 8 * g4 + 4 * fk;
+                    const int c = wn * 128 + 32 * i + 8 * g4 + 4 * fk;
                     const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
                     const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                     const float a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
@@ -1161,8 +1159,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
         __syncthreads();
         uint16_t* out = static_cast<uint16_t*>(ep.out);
 #pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
-            const int q = it * NT8 + tid;
+        for (int it = 0; it < 32; ++it) {
+            const int q = it * NT4 + tid;
             const int r = q >> 5, c = q & 31;
             const int m = m0 + r;
             const int n = n0 + c * 8;
@@ -1181,10 +1179,10 @@ __global__ __launch_bounds__(NT8, 1) void gemm_f6_w8_kernel(const uint8_t* __res
             const int m = m0 + wm * 128 + 32 * j + fr;
             if (m >= M) continue;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const int n = n0 + wn * 64 + 32 * i + 8 * g4 + 4 * fk;
+                    const int n = n0 + wn * 128 + 32 * i + 8 * g4 + 4 * fk;
                     if (n >= N) continue;
                     const int32_t a4[4] = {(int32_t)acc[i][j][4 * g4], (int32_t)acc[i][j][4 * g4 + 1],
                                            (int32_t)acc[i][j][4 * g4 + 2], (int32_t)acc[i][j][4 * g4 + 3]};
@@ -1293,7 +1291,7 @@ hipError_t launch_gemm_f6_bf16(const uint8_t* a6, int64_t lda, const float* a_sc
                                int64_t M, int64_t N, int64_t K, hipStream_t stream, bool w_sliced, bool a_sliced) {
     EpiArgs ep{a_scale, w_scale, static_cast<const uint16_t*>(bias), y, ldy, 1, 1};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_f6_w8_kernel<MODE_BF16><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+    gemm_f6_w4_kernel<MODE_BF16><<<dim3((unsigned)tiles), dim3(NT4), 0, stream>>>(
         a6, a_sliced ? F6_RB : lda, a_sliced ? M * F6_RB : F6_RB, w6, w_sliced ? F6_RB : ldw,
         w_sliced ? N * F6_RB : F6_RB, (int)M, (int)N, (int)K, ep);
     return hipGetLastError();
@@ -1304,7 +1302,7 @@ hipError_t launch_gemm_f6_i32(const uint8_t* a6, int64_t lda, const uint8_t* w6,
                               bool a_sliced) {
     EpiArgs ep{nullptr, nullptr, nullptr, acc, ldc, 0, 0};
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    gemm_f6_w8_kernel<MODE_I32><<<dim3((unsigned)tiles), dim3(NT8), 0, stream>>>(
+    gemm_f6_w4_kernel<MODE_I32><<<dim3((unsigned)tiles), dim3(NT4), 0, stream>>>(
         a6, a_sliced ? F6_RB : lda, a_sliced ? M * F6_RB : F6_RB, w6, w_sliced ? F6_RB : ldw,
         w_sliced ? N * F6_RB : F6_RB, (int)M, (int)N, (int)K, ep);
     return hipGetLastError();
