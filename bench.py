@@ -407,11 +407,13 @@ class LinearRun:
 def time_steps(run, steps: int, warmup: int, torch, clock: bool = True):
     """warmup untimed steps, then `steps` steps between one pair of HIP events
     (and the clock samples just outside them): (ms per step, wall s, clock)."""
-    for _ in range(warmup):
-        run.step()
-    torch.cuda.synchronize()
+    # everything the timed region needs is allocated before the warm-up: an
+    # allocation (or any idle gap) between warm-up and timing would restart the
+    # clock's settling transient (the first launches after idle run slower)
     clk = ClockProbe(torch) if clock else None
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        run.step()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     if clk:
