@@ -37,6 +37,7 @@ def test_pack_fp6(qd, O, R, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (256, 256, 128), (257, 300, 512), (64, 8, 1024),
+                                   (300, 520, 256), (300, 520, 384), (300, 520, 640), (257, 264, 768),
                                    (513, 264, 256), (300, 1000, 28672)])
 def test_fp6_gemm_exact(qd, O, M, N, K):
     say(f"fp6 gemm i32 M={M} N={N} K={K}")

@@ -151,6 +151,18 @@ def test_gemm_i32_exact(qd, O, tiles, M, N, K):
     assert np.array_equal(host(acc), O.gemm_i32(a, w))
 
 
+@pytest.mark.parametrize("K", [192, 256, 320, 384, 448])
+def test_gemm_i32_ring_boundaries(qd, O, tiles, K):
+    """K slices around the LDS ring depth (3 to 7 slices of 64): the K loop's
+    steady phase (slices with the whole ring after them) and its last slices
+    meet at every possible point; INT32 bit for bit, ragged M and N."""
+    say(f"gemm i32 ring boundary K={K} tiles={tiles}")
+    g = np.random.Generator(np.random.PCG64(3 * K + tiles))
+    a = g.integers(-128, 128, (300, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-128, 128, (520, K), dtype=np.int64).astype(np.int8)
+    assert np.array_equal(host(qd.int8_gemm_i32(to_dev(a), to_dev(w))), O.gemm_i32(a, w))
+
+
 def test_gemm_i32_extremes(qd, O, tiles):
     say(f"gemm i32 extremes tiles={tiles}")
     K = 5376

@@ -47,7 +47,7 @@ def test_slice_weights_layout(qd, N, K, pad):
 
 
 SHAPES = [(1, 1, 64), (256, 256, 64), (257, 255, 128), (70, 130, 128), (300, 520, 512),
-          (513, 1000, 5376), (64, 4100, 1024)]
+          (513, 1000, 5376), (64, 4100, 1024), (300, 520, 256), (257, 264, 320), (300, 520, 448)]
 
 
 def _slice_np(a):
@@ -263,7 +263,8 @@ def test_fp6_slice_weights_layout(qd, O, N, K):
     assert_fp6_codes(unslice96(host(ws), N), w4, "fp6 sliced weights")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (257, 255, 256), (70, 130, 384), (300, 520, 1024), (513, 1000, 5376)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (257, 255, 256), (70, 130, 384), (300, 520, 1024), (513, 1000, 5376),
+                                   (300, 520, 640), (257, 264, 512)])
 def test_fp6_sliced_gemm_exact(qd, O, M, N, K):
     say(f"fp6 sliced gemm M={M} N={N} K={K}")
     a4, w4 = _int4((M, K), 7 * M + K), _int4((N, K), 11 * N + K)

@@ -33,7 +33,8 @@ def test_pack_int4(qd, O, R, K):
     assert np.array_equal(host(p), O.pack_int4(q))
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (256, 256, 64), (257, 300, 512), (300, 1000, 28672), (64, 8, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (256, 256, 64), (257, 300, 512), (300, 1000, 28672), (64, 8, 1024),
+                                   (300, 520, 256), (300, 520, 320), (300, 520, 384), (300, 520, 448)])
 def test_int4_gemm_i32_exact(qd, O, M, N, K):
     say(f"int4 gemm i32 M={M} N={N} K={K}")
     a = _codes((M, K), seed=M * 3 + K, lo=-7)
