@@ -323,8 +323,8 @@ class LinearRun:
 
     def kernel_name(self) -> str:
         qd = self.qd
-        name = ("gemm_f6_w8_kernel<MODE_BF16> (K-sliced operands)" if self.sliced6 else
-                "gemm_f6_w8_kernel<MODE_BF16>" if self.fp6 else
+        name = ("gemm_f6_w4_kernel<MODE_BF16> (K-sliced operands)" if self.sliced6 else
+                "gemm_f6_w4_kernel<MODE_BF16>" if self.fp6 else
                 "gemm_i8_w8_kernel<MODE_BF16, 5, WF_I4>" if self.int4 else
                 "gemm_i8_w12_kernel<MODE_BF16> (256x384 tiles)"
                 if qd.int8_gemm_tiles(self.M, self.N, self.K) == qd.GEMM_TILES_256x384 else

@@ -334,8 +334,13 @@ __device__ __forceinline__ i32x4 unpack_int4x16(const u32x2& p) {
     return r;
 }
 
-__device__ __forceinline__ void dma16(uint32_t lds, const int8_t* src) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src) : "memory");
+// 16-byte global -> LDS copy per lane.  The source is split into a wave-uniform
+// base in SGPRs (the tile's first row plus the slice offset: one scalar add per
+// slice) and a fixed per-lane 32-bit offset (row within the tile x row pitch +
+// chunk; below 2^32 because tiles have at most 384 rows and K <= QD_MAX_K_GEMM),
+// so the K loop spends no vector instructions on copy addresses.
+__device__ __forceinline__ void dma16s(uint32_t lds, uint32_t voff, const int8_t* sbase) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -414,30 +419,32 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     // copies: activation instruction i (0, 1) of this wave covers rows
     // 16 * (wave + 8 i) + lane / 4; INT8 weights likewise; packed INT4 weights
     // take one instruction per wave for rows 32 * wave + lane / 2
-    const int8_t* ga[2];
-    const int8_t* gw[2];
+    // (sources: a uniform tile base advanced per slice plus a fixed per-lane offset)
+    uint32_t va[2], vw[2];
     uint32_t lrow[2], lwrow[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int rt = 16 * (wave + 8 * i) + (lane >> 2);
         const int c = (lane & 3) ^ swz(rt);
-        ga[i] = A + (int64_t)min(m0 + rt, M - 1) * lda + c * 16;
+        va[i] = (uint32_t)((int64_t)(min(m0 + rt, M - 1) - m0) * lda + c * 16);
         lrow[i] = (uint32_t)(16 * (wave + 8 * i) * BK);
         if (WF == WF_I8) {
-            gw[i] = W + (int64_t)min(n0 + rt, N - 1) * ldw + c * 16;
+            vw[i] = (uint32_t)((int64_t)(min(n0 + rt, N - 1) - n0) * ldw + c * 16);
             lwrow[i] = lrow[i];
         } else {
             const int rw = 32 * wave + (lane >> 1);
             const int cw = (lane & 1) ^ swz4(rw);
-            gw[i] = W + (int64_t)min(n0 + rw, N - 1) * ldw + cw * 16;
+            vw[i] = (uint32_t)((int64_t)(min(n0 + rw, N - 1) - n0) * ldw + cw * 16);
             lwrow[i] = (uint32_t)(32 * wave * WROW);
         }
     }
+    const int8_t* a_base = A + (int64_t)m0 * lda;
+    const int8_t* w_base = W + (int64_t)n0 * ldw;
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
         const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
-        if (part == 0) dma16(sb + lrow[i], ga[i] + (int64_t)u * a_ss);
-        else if (WF == WF_I8 || i == 0) dma16(sb + BM * BK + lwrow[i], gw[i] + (int64_t)u * w_ss);
+        if (part == 0) dma16s(sb + lrow[i], va[i], a_base + (int64_t)u * a_ss);
+        else if (WF == WF_I8 || i == 0) dma16s(sb + BM * BK + lwrow[i], vw[i], w_base + (int64_t)u * w_ss);
     };
     auto issue = [&](int u) {
         copy_part(u, 0, 0);
@@ -688,20 +695,22 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
 
     // copy instruction i of this wave covers rows 16 * (wave + 8 i) + lane / 4
     // of the activation tile (i < 2) and of the weight tile (i < 3)
-    const int8_t* ga[2];
-    const int8_t* gw[3];
+    // copy sources: tile base + slice offset (uniform) and a fixed per-lane offset
+    uint32_t va[2], vw[3];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
         const int rt = 16 * (wave + 8 * i) + (lane >> 2);
         const int c = (lane & 3) ^ swz(rt);
-        if (i < 2) ga[i] = A + (int64_t)min(m0 + rt, M - 1) * lda + c * 16;
-        gw[i] = W + (int64_t)min(n0 + rt, N - 1) * ldw + c * 16;
+        if (i < 2) va[i] = (uint32_t)((int64_t)(min(m0 + rt, M - 1) - m0) * lda + c * 16);
+        vw[i] = (uint32_t)((int64_t)(min(n0 + rt, N - 1) - n0) * ldw + c * 16);
     }
+    const int8_t* a_base = A + (int64_t)m0 * lda;
+    const int8_t* w_base = W + (int64_t)n0 * ldw;
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
         const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG) + (uint32_t)(16 * (wave + 8 * i) * BK);
-        if (part == 0) dma16(sb, ga[i] + (int64_t)u * a_ss);
-        else dma16(sb + BM * BK, gw[i] + (int64_t)u * w_ss);
+        if (part == 0) dma16s(sb, va[i], a_base + (int64_t)u * a_ss);
+        else dma16s(sb + BM * BK, vw[i], w_base + (int64_t)u * w_ss);
     };
 
     // fragment b of a wave: rows base + 32 b + lane % 32, 16-byte chunk 2 kk + lane / 32;
@@ -923,8 +932,6 @@ constexpr int F6_BK = 128;                 // values per slice
 constexpr int F6_RB = 96;                  // bytes per row per slice
 constexpr int F6_STG = (BM + BN) * F6_RB;  // 48 KB per stage
 constexpr int F6_NS = 3;
-constexpr int F6_PER = 6;                  // copies per slice per thread (3 activation + 3 weight)
-
 __device__ __forceinline__ int f6_rot(int r) { return 3 * (((r >> 2) ^ (r >> 3)) & 1); }   // slots
 __device__ __forceinline__ int f6_swp(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
 
@@ -1004,24 +1011,25 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
     }
 
     // copies: instruction i (0..5) of wave w fills the 16-byte LDS slots
-    // (6w + i) * 64 + lane of an operand's 24 KB stage part (layout as in
-    // gemm_f6_w8_kernel)
-    const uint8_t* ga[6];
-    const uint8_t* gw[6];
+    // (6w + i) * 64 + lane of an operand's 24 KB stage part (slot layout
+    // above: six slots per row slice, rotated by f6_rot(row))
+    uint32_t va[6], vw[6];
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
         const int q = (6 * wave + i) * 64 + lane;
         const int row = q / 6;
         const int phys = q - 6 * row;
         const int logical = (phys + f6_rot(row)) % 6;
-        ga[i] = A + (int64_t)min(m0 + row, M - 1) * lda + 16 * logical;
-        gw[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + 16 * logical;
+        va[i] = (uint32_t)((int64_t)(min(m0 + row, M - 1) - m0) * lda + 16 * logical);
+        vw[i] = (uint32_t)((int64_t)(min(n0 + row, N - 1) - n0) * ldw + 16 * logical);
     }
+    const int8_t* a_base = reinterpret_cast<const int8_t*>(A) + (int64_t)m0 * lda;
+    const int8_t* w_base = reinterpret_cast<const int8_t*>(W) + (int64_t)n0 * ldw;
     const uint32_t lds0 = lds_addr(smem);
     auto copy_part = [&](int u, int part, int i) {
         const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG) + (uint32_t)((6 * wave + i) * 1024);
-        if (part == 0) dma16(sb, reinterpret_cast<const int8_t*>(ga[i] + (int64_t)u * a_ss));
-        else dma16(sb + BM * F6_RB, reinterpret_cast<const int8_t*>(gw[i] + (int64_t)u * w_ss));
+        if (part == 0) dma16s(sb, va[i], a_base + (int64_t)u * a_ss);
+        else dma16s(sb + BM * F6_RB, vw[i], w_base + (int64_t)u * w_ss);
     };
 
     const int fr = lane & 31;
