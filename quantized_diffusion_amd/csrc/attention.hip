@@ -40,6 +40,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// max(x, x of lane ^ 32): the two half-waves exchange through
+// v_permlane32_swap (a VALU lane swap, no LDS round trip); the s_nop pads
+// cover the VALU write -> swap -> VALU read hazards
+__device__ __forceinline__ float max_xor32(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1" : "+v"(a), "+v"(b));
+    return a;
+}
+
 constexpr int AW = 12;               // waves per workgroup, 32 queries each
 constexpr int AQ = 32 * AW;          // queries per workgroup
 constexpr int AK = 64;               // keys per block
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
                 }
             }
         }
-        bm = __builtin_fmaxf(bm, __shfl_xor(bm, 32));
+        bm = max_xor32(bm);
         // The reference maximum only moves when the block's maximum exceeds it
         // by more than 2^8 in the exponent (the probabilities stay <= 256, far
         // inside FP32 and BF16 range, and out = sum p v / sum p does not depend

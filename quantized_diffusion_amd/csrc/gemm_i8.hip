@@ -932,6 +932,7 @@ constexpr int F6_BK = 128;                 // values per slice
 constexpr int F6_RB = 96;                  // bytes per row per slice
 constexpr int F6_STG = (BM + BN) * F6_RB;  // 48 KB per stage
 constexpr int F6_NS = 3;
+
 __device__ __forceinline__ int f6_rot(int r) { return 3 * (((r >> 2) ^ (r >> 3)) & 1); }   // slots
 __device__ __forceinline__ int f6_swp(int r) { return ((r >> 3) ^ (r >> 4)) & 1; }
 
