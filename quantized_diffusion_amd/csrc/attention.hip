@@ -11,9 +11,12 @@
 //
 // attn_i8_kernel: a workgroup of 12 waves (three per SIMD) takes 384 queries of
 // one (batch, head), each wave 32 queries, and walks the keys in blocks of 64
-// through two LDS stages (flash-attention style: running reference maximum
+// through four LDS stages (flash-attention style: running reference maximum
 // and sum, the output accumulators rescaled only when some query's maximum
-// outgrew its reference by more than 2^8).
+// outgrew its reference by more than 2^8).  Block kb + 2 is staged during
+// block kb, so one workgroup barrier per two blocks keeps every stage
+// written before it is read and read before it is rewritten; between
+// barriers the waves of a SIMD drift apart and overlap their phases.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_i32_32x32x32_i8 (K from LDS as the "A" operand, the wave's Q
 //    codes in registers as "B"), so a lane holds 16 keys of ONE query: the
@@ -79,7 +82,8 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
     // rows r and r + 256 / D share banks; XOR the chunk with the row's next bits
     // to put the 16 rows read by 16 lanes on 16 distinct 16-byte bank groups
     auto kswz = [](int row) { return (row / (256 / D)) & (CPR - 1); };
-    __shared__ AttnStage<D> st[2];
+    constexpr int NST = 4, PB = 2;   // LDS stages; blocks per barrier (= staging distance in blocks)
+    __shared__ AttnStage<D> st[NST];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
     const float sqc = sq[qbase + qr] * c;   // >= 0: applied inside the exponent
 
     // staging of key block kb: registers first (loads in flight during the
-    // previous block's math), then LDS.  Value group vg: keys 4 (vg % 16) + 0..3,
+    // math of block kb - PB), then LDS.  Value group vg: keys 4 (vg % 16) + 0..3,
     // dims 4 (vg / 16) + 0..3.
     constexpr int VGI = (VG + ATT_THREADS - 1) / ATT_THREADS;   // value groups staged per thread
     u32x4 kreg[KCH];
@@ -175,15 +179,18 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
     float l_run = 0.0f;
 
     const int nkb = (Lk + AK - 1) / AK;
-    gload(0);
-    sstore(st[0]);
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+        gload(j);
+        sstore(st[j]);
+    }
     __syncthreads();
     // key blocks: the full ones, then the partial last one (keys past Lk
     // masked) as a separate instance so that the full blocks carry no masking
     auto block = [&](int kb, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
-        const AttnStage<D>& S = st[kb & 1];
-        gload(kb + 1);   // rows clamped to Lk - 1 past the last block
+        const AttnStage<D>& S = st[kb % NST];
+        gload(kb + PB);   // rows clamped to Lk - 1 past the last block
 
         // S^T tiles: keys kt*32 + 8g + 4h + e (element 4g + e), query fr; the
         // two tiles' MFMAs alternate (independent accumulators)
@@ -277,9 +284,9 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
             }
         }
         l_run += ls;
-        // staging of the next block (for the last block it reloads clamped rows
-        // into the stage nobody reads any more: no branch, one scheduling region)
-        sstore(st[(kb + 1) & 1]);
+        // staging of block kb + PB (past the last block it reloads clamped rows
+        // into stages nobody reads any more: no branch, one scheduling region)
+        sstore(st[(kb + PB) % NST]);
         // schedule: value-tile reads first, the first tile's probabilities, then
         // each of its MFMAs followed by a share of the remaining VALU work
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * 4 * NS, 0);
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * NS, 0);
 
 
-        __syncthreads();
+        if (kb % PB == PB - 1) __syncthreads();
     };
     const int nfull = Lk / AK;
     for (int kb = 0; kb < nfull; ++kb) block(kb, std::false_type{});
