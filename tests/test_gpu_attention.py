@@ -76,8 +76,12 @@ def _check(qd, O, dev, host_in, dtype, scale=0.0, what=""):
         f"median bound / |exact| = {float(np.median(bound / np.maximum(np.abs(want), 1e-300))):.3f}")
 
 
+# Lk spans: a tail block alone, whole blocks only (1, 3 and 5 of them: the
+# kernel stages two blocks ahead and synchronises after every second block),
+# whole blocks plus a tail for both parities of the block count
 @pytest.mark.parametrize("BH,Lq,Lk,D", [(1, 1, 1, 64), (2, 130, 200, 64), (3, 257, 64, 128), (1, 128, 1000, 128),
-                                        (2, 64, 63, 128), (1, 300, 4097, 128), (4, 129, 129, 64)])
+                                        (2, 64, 63, 128), (1, 300, 4097, 128), (4, 129, 129, 64),
+                                        (1, 70, 192, 128), (2, 40, 320, 64)])
 def test_attention_bf16(qd, O, BH, Lq, Lk, D):
     say(f"int8_attention bf16 BH={BH} Lq={Lq} Lk={Lk} D={D}")
     dev, h = _inputs((BH, Lq, D), (BH, Lk, D), seed=BH * 1000 + Lq + Lk + D)
