@@ -193,7 +193,9 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
         gload(kb + PB);   // rows clamped to Lk - 1 past the last block
 
         // S^T tiles: keys kt*32 + 8g + 4h + e (element 4g + e), query fr; the
-        // two tiles' MFMAs alternate (independent accumulators)
+        // two tiles' MFMAs alternate (independent accumulators).  The wave
+        // issues them at raised priority: the block's softmax waits on them.
+        __builtin_amdgcn_s_setprio(1);
         i32x16 sacc[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -210,6 +212,7 @@ __global__ __launch_bounds__(ATT_THREADS, 3) void attn_i8_kernel(const int8_t* _
             }
         }
 
+        __builtin_amdgcn_s_setprio(0);
         float t[2][16];
         float bm = -__builtin_inff();
 #pragma unroll
