@@ -71,6 +71,8 @@ qd_status_t check_gemm(const char* fn, const int8_t* aq, int64_t M, int64_t K, i
         return fail(QD_EINVAL, fn, "need M >= 0, N >= 0, K > 0 (M=%lld, N=%lld, K=%lld)", (long long)M, (long long)N, (long long)K);
     if (M > 0 && N > 0 && (!aq || !wq || !out)) return fail(QD_EINVAL, fn, "null pointer argument");
     if (lda < K || ldw < K) return fail(QD_EINVAL, fn, "lda/ldw must be >= K");
+    if (lda > QD_MAX_LD_GEMM || ldw > QD_MAX_LD_GEMM)
+        return fail(QD_EUNSUPPORTED, fn, "lda/ldw (%lld, %lld) exceed %d", (long long)lda, (long long)ldw, QD_MAX_LD_GEMM);
     if (ldo < N) return fail(QD_EINVAL, fn, "output leading dimension (%lld) < N (%lld)", (long long)ldo, (long long)N);
     if (K % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 16", (long long)K);
     if (K > QD_MAX_K_GEMM) return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds %d", (long long)K, QD_MAX_K_GEMM);
@@ -496,6 +498,7 @@ namespace {
 qd_status_t check_w4(const char* fn, int64_t K, int64_t ldw, int64_t N) {
     if (K % 64 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 64 for packed INT4 weights", (long long)K);
     if (ldw < K / 2) return fail(QD_EINVAL, fn, "ldw (%lld bytes) < K/2", (long long)ldw);
+    if (ldw > QD_MAX_LD_GEMM) return fail(QD_EUNSUPPORTED, fn, "ldw (%lld) exceeds %d", (long long)ldw, QD_MAX_LD_GEMM);
     if (ldw % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "ldw must be a multiple of 16 bytes");
     (void)N;
     return QD_OK;
@@ -576,6 +579,8 @@ qd_status_t check_f6(const char* fn, const uint8_t* a6, int64_t M, int64_t K, in
     if (K % 128 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 128 for FP6 operands", (long long)K);
     if (K > QD_MAX_K_GEMM) return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds %d", (long long)K, QD_MAX_K_GEMM);
     if (lda < K / 4 * 3 || ldw < K / 4 * 3) return fail(QD_EINVAL, fn, "lda/ldw must be >= 3K/4 bytes");
+    if (lda > QD_MAX_LD_GEMM || ldw > QD_MAX_LD_GEMM)
+        return fail(QD_EUNSUPPORTED, fn, "lda/ldw (%lld, %lld) exceed %d", (long long)lda, (long long)ldw, QD_MAX_LD_GEMM);
     if (ldo < N) return fail(QD_EINVAL, fn, "output leading dimension (%lld) < N (%lld)", (long long)ldo, (long long)N);
     if (M > INT32_MAX - 256 || N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "M or N too large");
     if ((M + 255) / 256 * ((N + 255) / 256) > INT32_MAX) return fail(QD_EUNSUPPORTED, fn, "too many output tiles");

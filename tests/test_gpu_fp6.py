@@ -36,6 +36,27 @@ def test_pack_fp6(qd, O, R, K):
     assert_fp6_codes(host(p), q, "pack_fp6")
 
 
+def test_fp6_gemm_largest_stride(qd, O):
+    """Row-major FP6 operands whose rows lie QD_MAX_LD_GEMM bytes apart (the
+    largest stride accepted): exact sums bit for bit."""
+    import os
+    import re
+    import torch
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdiff.h")
+    ld = int(re.search(r"#define QD_MAX_LD_GEMM (\d+)", open(hdr).read()).group(1))
+    M, N, K = 300, 280, 256
+    say(f"fp6 gemm i32 row stride {ld} M={M} N={N} K={K}")
+    a = _codes((M, K), 820)
+    w = _codes((N, K), 821)
+    ab = torch.zeros((M, ld), dtype=torch.uint8, device="cuda")
+    wb = torch.zeros((N, ld), dtype=torch.uint8, device="cuda")
+    ab[:, :3 * K // 4] = qd.pack_fp6(to_dev(a))
+    wb[:, :3 * K // 4] = qd.pack_fp6(to_dev(w))
+    acc = qd.fp6_gemm_i32(ab[:, :3 * K // 4], wb[:, :3 * K // 4], K)
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+    del ab, wb
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (256, 256, 128), (257, 300, 512), (64, 8, 1024),
                                    (300, 520, 256), (300, 520, 384), (300, 520, 640), (257, 264, 768),
                                    (513, 264, 256), (300, 1000, 28672)])

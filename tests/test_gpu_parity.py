@@ -163,6 +163,28 @@ def test_gemm_i32_ring_boundaries(qd, O, tiles, K):
     assert np.array_equal(host(qd.int8_gemm_i32(to_dev(a), to_dev(w))), O.gemm_i32(a, w))
 
 
+def test_gemm_i32_largest_stride(qd, O, tiles):
+    """Operand rows QD_MAX_LD_GEMM bytes apart (the largest stride accepted:
+    a tile's copy offsets reach 383 rows x the stride): INT32 bit for bit."""
+    import os
+    import re
+    import torch
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdiff.h")
+    ld = int(re.search(r"#define QD_MAX_LD_GEMM (\d+)", open(hdr).read()).group(1))
+    M, N, K = 300, 520, 256
+    say(f"gemm i32 row stride {ld} M={M} N={N} K={K} tiles={tiles}")
+    g = np.random.Generator(np.random.PCG64(71 + tiles))
+    a = g.integers(-128, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-128, 128, (N, K), dtype=np.int64).astype(np.int8)
+    ab = torch.zeros((M, ld), dtype=torch.int8, device="cuda")
+    wb = torch.zeros((N, ld), dtype=torch.int8, device="cuda")
+    ab[:, :K] = to_dev(a)
+    wb[:, :K] = to_dev(w)
+    acc = qd.int8_gemm_i32(ab[:, :K], wb[:, :K])
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+    del ab, wb
+
+
 def test_gemm_i32_extremes(qd, O, tiles):
     say(f"gemm i32 extremes tiles={tiles}")
     K = 5376

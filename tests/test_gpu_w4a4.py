@@ -44,6 +44,27 @@ def test_int4_gemm_i32_exact(qd, O, M, N, K):
     assert np.array_equal(host(acc), O.gemm_i32(a, w))
 
 
+def test_int4_gemm_largest_stride(qd, O):
+    """Activation codes and packed INT4 weights whose rows lie QD_MAX_LD_GEMM
+    bytes apart (the largest stride accepted): INT32 bit for bit."""
+    import os
+    import re
+    import torch
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdiff.h")
+    ld = int(re.search(r"#define QD_MAX_LD_GEMM (\d+)", open(hdr).read()).group(1))
+    M, N, K = 300, 280, 256
+    say(f"int4 gemm i32 row stride {ld} M={M} N={N} K={K}")
+    a = _codes((M, K), seed=830, lo=-7)
+    w = _codes((N, K), seed=831)
+    ab = torch.zeros((M, ld), dtype=torch.int8, device="cuda")
+    wb = torch.zeros((N, ld), dtype=torch.uint8, device="cuda")
+    ab[:, :K] = to_dev(a)
+    wb[:, :K // 2] = to_dev(O.pack_int4(w))
+    acc = qd.int4_gemm_i32(ab[:, :K], wb[:, :K // 2])
+    assert np.array_equal(host(acc), O.gemm_i32(a, w))
+    del ab, wb
+
+
 def test_int4_scaled_mm(qd, O):
     say("int4 scaled_mm")
     from synth import random_bf16
