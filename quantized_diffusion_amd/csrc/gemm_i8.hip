@@ -32,6 +32,11 @@
 // so they read row-major operands or the K-sliced layout (each 64-byte K
 // slice of all rows stored contiguously: a copy instruction then reads 1 KB
 // of consecutive bytes, whole 128-byte lines, at lower power per byte).
+// Copy sources are a wave-uniform base in SGPRs (advanced by a scalar add
+// per slice) plus a fixed 32-bit offset per lane, so the loops spend no
+// vector instructions on addresses; the boundary keeps operand row strides
+// at most QD_MAX_LD_GEMM so that a tile's offsets fit 32 bits.
+// The FP6 kernel (W4A4 codes as FP6 E2M3) is described before its code.
 //
 // MFMA roles.  The weight tile is the MFMA "A" operand (its rows index n)
 // and the activation tile is "B" (its columns index m), so each lane ends up
@@ -52,7 +57,6 @@
 #include <stdint.h>
 
 #include <type_traits>
-
 
 #include "qd_device.h"
 #include "qd_launch.h"
