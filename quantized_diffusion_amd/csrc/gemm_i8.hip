@@ -294,8 +294,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_i8_kernel(const int8_t* __restrict
     }
 }
 
-constexpr int STAGE = (BM + BN) * BK;   // 32 KB per stage
-
 typedef __attribute__((address_space(3))) int8_t lds_i8;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -968,8 +966,12 @@ __device__ __forceinline__ u32x2 epi_bf16x4_f(const float* a4, float sx, const f
 // MFMA operands are 6-register FP6 tuples (the intrinsic's 6-dword form),
 // two registers fewer per fragment than the 8-dword builtin.
 typedef int32_t i32x6 __attribute__((ext_vector_type(6)));
+}  // namespace
+// (declared outside the unnamed namespace: the asm label binds it to the
+// compiler's intrinsic, so it has no definition of its own)
 __device__ f32x16 mfma_f6x6(i32x6 a, i32x6 b, f32x16 c, int cbsz, int blgp, int opsel_a, int scale_a, int opsel_b,
                             int scale_b) __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
+namespace {
 
 constexpr int NT4 = 256;
 constexpr int F6W4_PER = 12;   // copies per slice per thread (6 activation + 6 weight)
