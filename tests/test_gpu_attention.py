@@ -165,3 +165,35 @@ def test_attention_large_sampled(qd, O):
     err = np.abs(got - want)
     assert np.all(err <= bound), f"{int((err > bound).sum())} sampled outputs outside the bound"
     say(f"  max |err| / bound = {float((err / bound).max()):.3f}")
+
+
+def test_attention_full_size_sampled(qd, O):
+    """The benchmark's workload, 40 heads x 16384 tokens x 128 (BF16 N(0, 1)
+    inputs drawn as the benchmark draws them), in its launch configuration:
+    rows of three heads (first, middle, last; the first and last query, both
+    sides of a workgroup's 384-query boundary and random ones) against the
+    oracle within the bound."""
+    import torch
+    BH, L, D = 40, 16384, 128
+    say(f"int8_attention {BH}x{L}x{L}x{D}, sampled rows of three heads")
+    gen = torch.Generator(device="cuda").manual_seed(1234)
+    q, k, v = (torch.randn((BH, L, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(3))
+    ws = torch.empty(qd.attention_workspace_size(BH, L, L, D), dtype=torch.uint8, device="cuda")
+    out = qd.int8_attention(q, k, v, workspace=ws)
+    g = np.random.Generator(np.random.PCG64(46))
+    rows = np.unique(np.concatenate([g.integers(0, L, 18), [0, 383, 384, L - 1]]))
+    worst = 0.0
+    for hd in (0, 17, BH - 1):
+        hq, hk, hv = (_bits_of(t[hd:hd + 1]) for t in (q, k, v))
+        qc, sq = O.quantize_tokens(hq, "bf16")
+        kc, sk = O.quantize_tokens(hk, "bf16")
+        vc, sv = O.quantize_tokens(hv, "bf16")
+        want = O.attention_codes(qc[:, rows], sq[:, rows], kc, sk, vc, sv)
+        P = O.attention_probs(qc[:, rows], sq[:, rows], kc, sk)
+        sel = out[hd:hd + 1, torch.from_numpy(rows).cuda()]
+        got = (_bits_of(sel).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bound = attention_bound(want, P, qc[:, rows], sq[:, rows], kc, sk, vc, sv, 1.0 / np.sqrt(D))
+        err = np.abs(got - want)
+        assert np.all(err <= bound), f"head {hd}: {int((err > bound).sum())} sampled outputs outside the bound"
+        worst = max(worst, float((err / bound).max()))
+    say(f"  max |err| / bound = {worst:.3f}")
