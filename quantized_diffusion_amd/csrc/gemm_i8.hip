@@ -1033,8 +1033,9 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
     const int8_t* a_base = reinterpret_cast<const int8_t*>(A) + (int64_t)m0 * lda;
     const int8_t* w_base = reinterpret_cast<const int8_t*>(W) + (int64_t)n0 * ldw;
     const uint32_t lds0 = lds_addr(smem);
-    auto copy_part = [&](int u, int part, int i) {
-        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG) + (uint32_t)((6 * wave + i) * 1024);
+    // slice u into LDS stage sg (= u % NS, a constant in the unrolled steady loop)
+    auto copy_part = [&](int u, int sg, int part, int i) {
+        const uint32_t sb = lds0 + (uint32_t)(sg * STG) + (uint32_t)((6 * wave + i) * 1024);
         if (part == 0) dma16s(sb, va[i], a_base + (int64_t)u * a_ss);
         else dma16s(sb + BM * F6_RB, vw[i], w_base + (int64_t)u * w_ss);
     };
@@ -1052,8 +1053,8 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
         w_h[kk] = BM * F6_RB + rw * F6_RB + 16 * ((3 * kk + fk + f6_rot(rw)) % 6);
         w_t[kk] = BM * F6_RB + rw * F6_RB + 16 * ((3 * kk + 2 + f6_rot(rw)) % 6) + 8 * (fk ^ f6_swp(rw));
     }
-    auto rd = [&](int u, int head, int tail, int b) {
-        const int8_t* base = smem + (u % NS) * STG + b * 32 * F6_RB;
+    auto rd = [&](int sg, int head, int tail, int b) {
+        const int8_t* base = smem + sg * STG + b * 32 * F6_RB;
         const i32x4 h = *reinterpret_cast<const i32x4*>(base + head);
         const u32x2 t = *reinterpret_cast<const u32x2*>(base + tail);
         return i32x6{h[0], h[1], h[2], h[3], (int32_t)t[0], (int32_t)t[1]};
@@ -1072,15 +1073,15 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
     for (int u = 0; u < NS - 1; ++u)
         if (u < nk) {
 #pragma unroll
-            for (int i = 0; i < 6; ++i) copy_part(u, 0, i);
+            for (int i = 0; i < 6; ++i) copy_part(u, u, 0, i);
 #pragma unroll
-            for (int i = 0; i < 6; ++i) copy_part(u, 1, i);
+            for (int i = 0; i < 6; ++i) copy_part(u, u, 1, i);
         }
     wait_groups<PER>(min(nk, NS - 1) - 1);
     __syncthreads();
     if (NS - 1 < nk) {
 #pragma unroll
-        for (int i = 0; i < 6; ++i) copy_part(NS - 1, 0, i);
+        for (int i = 0; i < 6; ++i) copy_part(NS - 1, NS - 1, 0, i);
     }
 
     i32x6 a0[4], w0[4], a1[4], w1[4];
@@ -1090,14 +1091,18 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
         w0[b] = rd(0, w_h[0], w_t[0], b);
     }
     // STEADY: a slice with NS more after it (every copy issued, one slice in flight)
-    auto slice = [&](int t, auto steady_tag) {
+    auto slice = [&](int t, auto steady_tag, auto stage_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr int ST = decltype(stage_tag)::value;   // t % NS when known, else -1
+        const int sc = ST >= 0 ? ST : t % NS;
+        const int sn = ST >= 0 ? (ST + 1) % NS : (sc + 1 == NS ? 0 : sc + 1);
+        const int sp = ST >= 0 ? (ST + NS - 1) % NS : (sc == 0 ? NS - 1 : sc - 1);
         const bool late = STEADY || t + NS - 1 < nk;
         // first K step of slice t; reads of its second step; weight copies of slice t+NS-1
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            w1[q] = rd(t, w_h[1], w_t[1], q);
-            a1[q] = rd(t, a_h[1], a_t[1], q);
+            w1[q] = rd(sc, w_h[1], w_t[1], q);
+            a1[q] = rd(sc, a_h[1], a_t[1], q);
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[q][j] = mfma_f6x6(w0[q], a0[j], acc[q][j], 2, 2, 0, 127, 0, 127);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1107,10 +1112,10 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (late) {
-                if (q == 0) { copy_part(t + NS - 1, 1, 0); copy_part(t + NS - 1, 1, 1); }
-                if (q == 1) copy_part(t + NS - 1, 1, 2);
-                if (q == 2) { copy_part(t + NS - 1, 1, 3); copy_part(t + NS - 1, 1, 4); }
-                if (q == 3) copy_part(t + NS - 1, 1, 5);
+                if (q == 0) { copy_part(t + NS - 1, sp, 1, 0); copy_part(t + NS - 1, sp, 1, 1); }
+                if (q == 1) copy_part(t + NS - 1, sp, 1, 2);
+                if (q == 2) { copy_part(t + NS - 1, sp, 1, 3); copy_part(t + NS - 1, sp, 1, 4); }
+                if (q == 3) copy_part(t + NS - 1, sp, 1, 5);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1124,8 +1129,8 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
         // second K step of slice t; reads of slice t+1's first step; activation copies of slice t+NS
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            w0[q] = rd(t + 1, w_h[0], w_t[0], q);
-            a0[q] = rd(t + 1, a_h[0], a_t[0], q);
+            w0[q] = rd(sn, w_h[0], w_t[0], q);
+            a0[q] = rd(sn, a_h[0], a_t[0], q);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (q != 0 || j != 0) acc[q][j] = mfma_f6x6(w1[q], a1[j], acc[q][j], 2, 2, 0, 127, 0, 127);
@@ -1136,17 +1141,26 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if (early) {
-                if (q == 0) { copy_part(t + NS, 0, 0); copy_part(t + NS, 0, 1); }
-                if (q == 1) copy_part(t + NS, 0, 2);
-                if (q == 2) { copy_part(t + NS, 0, 3); copy_part(t + NS, 0, 4); }
-                if (q == 3) copy_part(t + NS, 0, 5);
+                if (q == 0) { copy_part(t + NS, sc, 0, 0); copy_part(t + NS, sc, 0, 1); }
+                if (q == 1) copy_part(t + NS, sc, 0, 2);
+                if (q == 2) { copy_part(t + NS, sc, 0, 3); copy_part(t + NS, sc, 0, 4); }
+                if (q == 3) copy_part(t + NS, sc, 0, 5);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // steady slices three at a time, so that each one's LDS stages are
+    // constants (with three stages, t % NS would otherwise cost a division
+    // and a dozen address adds per slice), then the rest
+    static_assert(NS == 3, "the unrolled steady loop assumes three stages");
     int t = 0;
-    for (; t + NS < nk; ++t) slice(t, std::true_type{});
-    for (; t < nk; ++t) slice(t, std::false_type{});
+    for (; t + NS + 2 < nk; t += 3) {
+        slice(t, std::true_type{}, std::integral_constant<int, 0>{});
+        slice(t + 1, std::true_type{}, std::integral_constant<int, 1>{});
+        slice(t + 2, std::true_type{}, std::integral_constant<int, 2>{});
+    }
+    for (; t + NS < nk; ++t) slice(t, std::true_type{}, std::integral_constant<int, -1>{});
+    for (; t < nk; ++t) slice(t, std::false_type{}, std::integral_constant<int, -1>{});
 
     if (MODE == MODE_BF16) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
