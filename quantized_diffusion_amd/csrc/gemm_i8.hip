@@ -443,16 +443,17 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     const int8_t* a_base = A + (int64_t)m0 * lda;
     const int8_t* w_base = W + (int64_t)n0 * ldw;
     const uint32_t lds0 = lds_addr(smem);
-    auto copy_part = [&](int u, int part, int i) {
-        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG);
+    // slice u into LDS stage sg (= u % NS; a constant in the unrolled steady loop)
+    auto copy_part = [&](int u, int sg, int part, int i) {
+        const uint32_t sb = lds0 + (uint32_t)(sg * STG);
         if (part == 0) dma16s(sb + lrow[i], va[i], a_base + (int64_t)u * a_ss);
         else if (WF == WF_I8 || i == 0) dma16s(sb + BM * BK + lwrow[i], vw[i], w_base + (int64_t)u * w_ss);
     };
     auto issue = [&](int u) {
-        copy_part(u, 0, 0);
-        copy_part(u, 0, 1);
-        copy_part(u, 1, 0);
-        copy_part(u, 1, 1);
+        copy_part(u, u, 0, 0);
+        copy_part(u, u, 0, 1);
+        copy_part(u, u, 1, 0);
+        copy_part(u, u, 1, 1);
     };
 
     const int fr = lane & 31;
@@ -475,12 +476,12 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
                 w_off[b][kk] = BM * BK + rw_row * WROW + ((kk ^ swz4(rw_row)) << 4) + (fk << 3);
         }
     }
-    auto rd_a = [&](int u, int kk, int b, i32x4* fa) {
-        fa[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STG + a_off[b][kk]);
+    auto rd_a = [&](int sg, int kk, int b, i32x4* fa) {
+        fa[b] = *reinterpret_cast<const i32x4*>(smem + sg * STG + a_off[b][kk]);
     };
-    auto rd_w = [&](int u, int kk, int b, i32x4* fw) {
-        if (WF == WF_I8) fw[b] = *reinterpret_cast<const i32x4*>(smem + (u % NS) * STG + w_off[b][kk]);
-        else fw[b] = unpack_int4x16(*reinterpret_cast<const u32x2*>(smem + (u % NS) * STG + w_off[b][kk]));
+    auto rd_w = [&](int sg, int kk, int b, i32x4* fw) {
+        if (WF == WF_I8) fw[b] = *reinterpret_cast<const i32x4*>(smem + sg * STG + w_off[b][kk]);
+        else fw[b] = unpack_int4x16(*reinterpret_cast<const u32x2*>(smem + sg * STG + w_off[b][kk]));
     };
 
     i32x16 acc[2][4];
@@ -499,8 +500,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     wait_groups<PER>(min(nk, NS - 1) - 1);
     __syncthreads();   // slice 0 and the epilogue operands are visible
     if (NS - 1 < nk) {
-        copy_part(NS - 1, 0, 0);
-        copy_part(NS - 1, 0, 1);
+        copy_part(NS - 1, NS - 1, 0, 0);
+        copy_part(NS - 1, NS - 1, 0, 1);
     }
 
     // The loop runs from barrier to barrier (second half of slice t, then
@@ -508,15 +509,19 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
     i32x4 a0[4], w0[2], a1[4], w1[2];
     // STEADY: a slice with NS more after it, where every copy is issued and
     // NS - 2 slices stay in flight (no run-time conditions in the loop body)
-    auto first_half = [&](int t, auto steady_tag) {
+    // stage_tag: t % NS when the caller knows it at compile time, else -1
+    auto first_half = [&](int t, auto steady_tag, auto stage_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr int ST = decltype(stage_tag)::value;
+        const int sc = ST >= 0 ? ST : t % NS;                          // slice t
+        const int sp = ST >= 0 ? (ST + NS - 1) % NS : (t + NS - 1) % NS;   // slice t + NS - 1
         // first half of slice t; reads of its second half; weight-row copies of slice t+NS-1
         const bool late = STEADY || t + NS - 1 < nk;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            rd_w(t, 1, q, w1);
-            rd_a(t, 1, 2 * q, a1);
-            rd_a(t, 1, 2 * q + 1, a1);
+            rd_w(sc, 1, q, w1);
+            rd_a(sc, 1, 2 * q, a1);
+            rd_a(sc, 1, 2 * q + 1, a1);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[q][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0[q], a0[j], acc[q][j], 0, 0, 0);
@@ -527,7 +532,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (late) copy_part(t + NS - 1, 1, q);
+            if (late) copy_part(t + NS - 1, sp, 1, q);
         }
         acc[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[0], a1[0], acc[0][0], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -536,16 +541,19 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
         else wait_groups<PER>(min(nk - 1, t + NS - 1) - (t + 1));
         __builtin_amdgcn_s_barrier();
     };
-    auto second_half = [&](int t, bool next, auto steady_tag) {
+    auto second_half = [&](int t, bool next, auto steady_tag, auto stage_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr int ST = decltype(stage_tag)::value;
+        const int sc = ST >= 0 ? ST : t % NS;                   // slice t (and t + NS)
+        const int sn = ST >= 0 ? (ST + 1) % NS : (t + 1) % NS;  // slice t + 1
         // second half of slice t; reads of slice t+1's first half; activation-row copies of slice t+NS
         const bool early = STEADY || t + NS < nk;
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             if (next) {
-                rd_w(t + 1, 0, q, w0);
-                rd_a(t + 1, 0, 2 * q, a0);
-                rd_a(t + 1, 0, 2 * q + 1, a0);
+                rd_w(sn, 0, q, w0);
+                rd_a(sn, 0, 2 * q, a0);
+                rd_a(sn, 0, 2 * q + 1, a0);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -558,24 +566,40 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if (early) copy_part(t + NS, 0, q);
+            if (early) copy_part(t + NS, sc, 0, q);
         }
     };
 #pragma unroll
     for (int b = 0; b < 4; ++b) rd_a(0, 0, b, a0);
 #pragma unroll
     for (int b = 0; b < 2; ++b) rd_w(0, 0, b, w0);
-    first_half(0, std::false_type{});
+    using rt = std::integral_constant<int, -1>;
+    first_half(0, std::false_type{}, std::integral_constant<int, 0>{});
+    // steady slices NS at a time, so that each one's LDS stages are constants
+    // (no per-slice stage arithmetic or address adds), then the rest
+    static_assert(NS == 4 || NS == 5, "the unrolled steady loop covers four or five stages");
+    auto steady = [&](int t0, auto jt) {
+        constexpr int J = decltype(jt)::value;
+        second_half(t0 + J, true, std::true_type{}, std::integral_constant<int, J>{});
+        first_half(t0 + J + 1, std::true_type{}, std::integral_constant<int, (J + 1) % NS>{});
+    };
     int t = 0;
+    for (; t + 2 * NS - 1 < nk; t += NS) {
+        steady(t, std::integral_constant<int, 0>{});
+        steady(t, std::integral_constant<int, 1>{});
+        steady(t, std::integral_constant<int, 2>{});
+        steady(t, std::integral_constant<int, 3>{});
+        if constexpr (NS == 5) steady(t, std::integral_constant<int, 4 % NS>{});
+    }
     for (; t + NS < nk; ++t) {
-        second_half(t, true, std::true_type{});
-        first_half(t + 1, std::true_type{});
+        second_half(t, true, std::true_type{}, rt{});
+        first_half(t + 1, std::true_type{}, rt{});
     }
     for (; t + 1 < nk; ++t) {
-        second_half(t, true, std::false_type{});
-        first_half(t + 1, std::false_type{});
+        second_half(t, true, std::false_type{}, rt{});
+        first_half(t + 1, std::false_type{}, rt{});
     }
-    second_half(nk - 1, false, std::false_type{});
+    second_half(nk - 1, false, std::false_type{}, rt{});
 
     if (MODE == MODE_BF16) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
