@@ -733,8 +733,9 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     const int8_t* a_base = A + (int64_t)m0 * lda;
     const int8_t* w_base = W + (int64_t)n0 * ldw;
     const uint32_t lds0 = lds_addr(smem);
-    auto copy_part = [&](int u, int part, int i) {
-        const uint32_t sb = lds0 + (uint32_t)((u % NS) * STG) + (uint32_t)(16 * (wave + 8 * i) * BK);
+    // slice u into LDS stage sg (= u % NS; a constant in the unrolled steady loop)
+    auto copy_part = [&](int u, int sg, int part, int i) {
+        const uint32_t sb = lds0 + (uint32_t)(sg * STG) + (uint32_t)(16 * (wave + 8 * i) * BK);
         if (part == 0) dma16s(sb, va[i], a_base + (int64_t)u * a_ss);
         else dma16s(sb + BM * BK, vw[i], w_base + (int64_t)u * w_ss);
     };
@@ -749,11 +750,11 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         a_off[kk] = (wm * 128 + fr) * BK + (((2 * kk + fk) ^ swz(fr)) << 4);
         w_off[kk] = BM * BK + (wn * 96 + fr) * BK + (((2 * kk + fk) ^ swz(fr)) << 4);
     }
-    auto rd_a = [&](int u, int kk, int b) {
-        return *reinterpret_cast<const i32x4*>(smem + (u % NS) * STG + a_off[kk] + b * 32 * BK);
+    auto rd_a = [&](int sg, int kk, int b) {
+        return *reinterpret_cast<const i32x4*>(smem + sg * STG + a_off[kk] + b * 32 * BK);
     };
-    auto rd_w = [&](int u, int kk, int b) {
-        return *reinterpret_cast<const i32x4*>(smem + (u % NS) * STG + w_off[kk] + b * 32 * BK);
+    auto rd_w = [&](int sg, int kk, int b) {
+        return *reinterpret_cast<const i32x4*>(smem + sg * STG + w_off[kk] + b * 32 * BK);
     };
 
     i32x16 acc[3][4];
@@ -768,17 +769,17 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
 #pragma unroll
     for (int u = 0; u < NS - 1; ++u)
         if (u < nk) {
-            copy_part(u, 0, 0);
-            copy_part(u, 0, 1);
-            copy_part(u, 1, 0);
-            copy_part(u, 1, 1);
-            copy_part(u, 1, 2);
+            copy_part(u, u, 0, 0);
+            copy_part(u, u, 0, 1);
+            copy_part(u, u, 1, 0);
+            copy_part(u, u, 1, 1);
+            copy_part(u, u, 1, 2);
         }
     wait_groups<PER>(min(nk, NS - 1) - 1);
     __syncthreads();   // slice 0 and the epilogue operands are visible
     if (NS - 1 < nk) {
-        copy_part(NS - 1, 0, 0);
-        copy_part(NS - 1, 0, 1);
+        copy_part(NS - 1, NS - 1, 0, 0);
+        copy_part(NS - 1, NS - 1, 0, 1);
     }
 
     // The loop runs from barrier to barrier (second half of slice t, then
@@ -786,8 +787,12 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     i32x4 a[4], w0[3], w1[3];
     // STEADY: a slice with NS more after it, where every copy is issued and
     // two slices stay in flight (no run-time conditions in the loop body)
-    auto first_half = [&](int t, auto steady_tag) {
+    // stage_tag: t % NS when the caller knows it at compile time, else -1
+    auto first_half = [&](int t, auto steady_tag, auto stage_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr int ST = decltype(stage_tag)::value;
+        const int sc = ST >= 0 ? ST : t % NS;                              // slice t
+        const int sp = ST >= 0 ? (ST + NS - 1) % NS : (t + NS - 1) % NS;   // slice t + NS - 1
         // first K half of slice t; its second half's fragments; weight copies of slice t+NS-1
         const bool late = STEADY || t + NS - 1 < nk;
         // raised priority while this half's MFMAs issue, normal again for the
@@ -795,17 +800,17 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (j < 3) w1[j] = rd_w(t, 1, j);
+            if (j < 3) w1[j] = rd_w(sc, 1, j);
 #pragma unroll
             for (int i = 0; i < 3; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0[i], a[j], acc[i][j], 0, 0, 0);
-            a[j] = rd_a(t, 1, j);
+            a[j] = rd_a(sc, 1, j);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            if (late && j < 3) copy_part(t + NS - 1, 1, j);
+            if (late && j < 3) copy_part(t + NS - 1, sp, 1, j);
             __builtin_amdgcn_sched_barrier(0);
         }
         acc[0][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[0], a[0], acc[0][0], 0, 0, 0);
@@ -816,18 +821,21 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         else wait_groups<PER>(min(nk - 1, t + NS - 1) - (t + 1));
         __builtin_amdgcn_s_barrier();
     };
-    auto second_half = [&](int t, bool next, auto steady_tag) {
+    auto second_half = [&](int t, bool next, auto steady_tag, auto stage_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr int ST = decltype(stage_tag)::value;
+        const int sc = ST >= 0 ? ST : t % NS;                   // slice t (and t + NS)
+        const int sn = ST >= 0 ? (ST + 1) % NS : (t + 1) % NS;  // slice t + 1
         // second K half of slice t; slice t+1's first-half fragments; activation copies of slice t+NS
         const bool early = STEADY || t + NS < nk;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (next && j < 3) w0[j] = rd_w(t + 1, 0, j);
+            if (next && j < 3) w0[j] = rd_w(sn, 0, j);
 #pragma unroll
             for (int i = 0; i < 3; ++i)
                 if (i != 0 || j != 0)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[i], a[j], acc[i][j], 0, 0, 0);
-            if (next) a[j] = rd_a(t + 1, 0, j);
+            if (next) a[j] = rd_a(sn, 0, j);
             if (j == 0) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -840,7 +848,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            if (early && j < 2) copy_part(t + NS, 0, j);
+            if (early && j < 2) copy_part(t + NS, sc, 0, j);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -848,17 +856,31 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     for (int b = 0; b < 4; ++b) a[b] = rd_a(0, 0, b);
 #pragma unroll
     for (int b = 0; b < 3; ++b) w0[b] = rd_w(0, 0, b);
-    first_half(0, std::false_type{});
+    using rt = std::integral_constant<int, -1>;
+    first_half(0, std::false_type{}, std::integral_constant<int, 0>{});
+    // steady slices NS at a time, so that each one's LDS stages are constants
+    static_assert(NS == 4, "the unrolled steady loop covers four stages");
+    auto steady = [&](int t0, auto jt) {
+        constexpr int J = decltype(jt)::value;
+        second_half(t0 + J, true, std::true_type{}, std::integral_constant<int, J>{});
+        first_half(t0 + J + 1, std::true_type{}, std::integral_constant<int, (J + 1) % NS>{});
+    };
     int t = 0;
+    for (; t + 2 * NS - 1 < nk; t += NS) {
+        steady(t, std::integral_constant<int, 0>{});
+        steady(t, std::integral_constant<int, 1>{});
+        steady(t, std::integral_constant<int, 2>{});
+        steady(t, std::integral_constant<int, 3>{});
+    }
     for (; t + NS < nk; ++t) {
-        second_half(t, true, std::true_type{});
-        first_half(t + 1, std::true_type{});
+        second_half(t, true, std::true_type{}, rt{});
+        first_half(t + 1, std::true_type{}, rt{});
     }
     for (; t + 1 < nk; ++t) {
-        second_half(t, true, std::false_type{});
-        first_half(t + 1, std::false_type{});
+        second_half(t, true, std::false_type{}, rt{});
+        first_half(t + 1, std::false_type{}, rt{});
     }
-    second_half(nk - 1, false, std::false_type{});
+    second_half(nk - 1, false, std::false_type{}, rt{});
 
     if (MODE == MODE_BF16) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
