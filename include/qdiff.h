@@ -91,9 +91,11 @@ typedef enum { QD_ACT_NONE = 0, QD_ACT_GELU_TANH = 1, QD_ACT_GELU_ERF = 2, QD_AC
  * GEMM entry points) can never overflow the INT32 accumulators. */
 #define QD_MAX_K_GEMM 131056
 
-/* Largest row stride (lda, ldw: bytes of INT8 codes, packed INT4 or FP6
- * operands) the GEMMs accept: a tile's copy offsets, up to 384 rows x the
- * stride, must fit 32 bits.  Larger strides return QD_EUNSUPPORTED. */
+/* Largest row stride the GEMMs accept, for the operands (lda, ldw: bytes of
+ * INT8 codes, packed INT4 or FP6 operands) and for the output (ldy:
+ * elements): a tile's copy offsets (up to 384 rows x the operand stride) and
+ * its store offsets (up to 160 rows x the output stride in bytes) must fit
+ * 32 bits.  Larger strides return QD_EUNSUPPORTED. */
 #define QD_MAX_LD_GEMM 8388608
 
 /* Message for the last non-OK status returned on the calling thread
@@ -145,7 +147,8 @@ qd_status_t qd_quantize_int8_rowwise(const void* x, qd_dtype_t x_dtype, int64_t 
  *   wq [N, K] INT8 (row stride ldw bytes), w_scale [N] FP32,
  *   bias [N] BF16 or NULL, y [M, N] BF16 (row stride ldy elements).
  * Requires K % 16 == 0, K <= QD_MAX_K_GEMM, aq/wq/y 16-byte aligned,
- * lda and ldw multiples of 16 and at most QD_MAX_LD_GEMM, ldy a multiple of 8.
+ * lda and ldw multiples of 16, ldy a multiple of 8, all three at most
+ * QD_MAX_LD_GEMM.
  */
 qd_status_t qd_int8_scaled_mm(const int8_t* aq, int64_t M, int64_t K, int64_t lda,
                               const float* a_scale, const int8_t* wq, int64_t N, int64_t ldw,

@@ -74,6 +74,8 @@ qd_status_t check_gemm(const char* fn, const int8_t* aq, int64_t M, int64_t K, i
     if (lda > QD_MAX_LD_GEMM || ldw > QD_MAX_LD_GEMM)
         return fail(QD_EUNSUPPORTED, fn, "lda/ldw (%lld, %lld) exceed %d", (long long)lda, (long long)ldw, QD_MAX_LD_GEMM);
     if (ldo < N) return fail(QD_EINVAL, fn, "output leading dimension (%lld) < N (%lld)", (long long)ldo, (long long)N);
+    if (ldo > QD_MAX_LD_GEMM)
+        return fail(QD_EUNSUPPORTED, fn, "output leading dimension (%lld) exceeds %d", (long long)ldo, QD_MAX_LD_GEMM);
     if (K % 16 != 0) return fail(QD_EUNSUPPORTED, fn, "K (%lld) must be a multiple of 16", (long long)K);
     if (K > QD_MAX_K_GEMM) return fail(QD_EUNSUPPORTED, fn, "K (%lld) exceeds %d", (long long)K, QD_MAX_K_GEMM);
     if (M > INT32_MAX - 256 || N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "M or N too large");
@@ -582,6 +584,8 @@ qd_status_t check_f6(const char* fn, const uint8_t* a6, int64_t M, int64_t K, in
     if (lda > QD_MAX_LD_GEMM || ldw > QD_MAX_LD_GEMM)
         return fail(QD_EUNSUPPORTED, fn, "lda/ldw (%lld, %lld) exceed %d", (long long)lda, (long long)ldw, QD_MAX_LD_GEMM);
     if (ldo < N) return fail(QD_EINVAL, fn, "output leading dimension (%lld) < N (%lld)", (long long)ldo, (long long)N);
+    if (ldo > QD_MAX_LD_GEMM)
+        return fail(QD_EUNSUPPORTED, fn, "output leading dimension (%lld) exceeds %d", (long long)ldo, QD_MAX_LD_GEMM);
     if (M > INT32_MAX - 256 || N > INT32_MAX - 256) return fail(QD_EUNSUPPORTED, fn, "M or N too large");
     if ((M + 255) / 256 * ((N + 255) / 256) > INT32_MAX) return fail(QD_EUNSUPPORTED, fn, "too many output tiles");
     if (M > 0 && N > 0 && (!aligned16(a6) || !aligned16(w6) || !aligned16(out)))

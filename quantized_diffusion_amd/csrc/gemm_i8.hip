@@ -319,6 +319,18 @@ __device__ __forceinline__ void wait_groups(int groups) {
     }
 }
 
+// the same with EXTRA further loads issued after the last copy (still in flight)
+template <int PER, int EXTRA>
+__device__ __forceinline__ void wait_groups_x(int groups) {
+    switch (groups) {
+        case 0:
+        case -1: wait_vmcnt<EXTRA>(); break;
+        case 1: wait_vmcnt<PER + EXTRA>(); break;
+        case 2: wait_vmcnt<2 * PER + EXTRA>(); break;
+        default: wait_vmcnt<3 * PER + EXTRA>(); break;
+    }
+}
+
 // 16 signed INT4 codes packed two per byte (code 2i in the low nibble of
 // byte i) -> 16 INT8 bytes in code order.  Byte-wise sign extension of a
 // nibble v: ((v ^ 8) + 0x78) ^ 0x80, which never carries across bytes.
@@ -670,13 +682,17 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
 // and latency).  Same slice protocol as gemm_i8_w8_kernel with four 40 KB
 // stages filling all 160 KB of LDS (activation copies of slice t+4 go into
 // stage t after slice t's barrier, weight copies of slice t+3 at the start
-// of slice t); the epilogue's scales and bias are copied into LDS only after
-// the K loop, above the staged output rows.  There is no room for a second set of
-// activation fragments, so each activation fragment is reloaded with the
-// next K half's data as soon as its three MFMAs are issued; the weight
-// fragments are double-buffered.  The output tile is staged through the ring
-// in two halves of 128 rows (768 bytes each, 16-byte chunks XOR-swizzled by
-// the row within groups of 16).
+// of slice t).  There is no room for a second set of activation fragments,
+// so each activation fragment is reloaded with the next K half's data as soon
+// as its three MFMAs are issued; the weight fragments are double-buffered.
+// Epilogue: the scales and bias are loaded into registers once the last copy
+// is issued (their latency hides under the last slices) and go to LDS above
+// the staged rows after the K loop; the output tile is staged through the
+// ring in four phases of 64 rows (768 bytes each, 16-byte chunks XOR-swizzled
+// by the row within groups of 16) over two alternating 48 KB buffers, one
+// barrier per phase, so one phase's stores overlap the next one's
+// conversion; whole tiles store through a wave-uniform row base plus fixed
+// 32-bit lane offsets, with no per-store bounds checks or 64-bit addressing.
 constexpr int BNW = 384;                        // weight rows per wide tile
 constexpr int W12_NS = 4;
 constexpr int W12_STG = (BM + BNW) * BK;        // 40 KB per stage
@@ -788,9 +804,10 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     // STEADY: a slice with NS more after it, where every copy is issued and
     // two slices stay in flight (no run-time conditions in the loop body)
     // stage_tag: t % NS when the caller knows it at compile time, else -1
-    auto first_half = [&](int t, auto steady_tag, auto stage_tag) {
+    auto first_half = [&](int t, auto steady_tag, auto stage_tag, auto extra_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
         constexpr int ST = decltype(stage_tag)::value;
+        constexpr int XL = decltype(extra_tag)::value;   // loads issued after the last copy
         const int sc = ST >= 0 ? ST : t % NS;                              // slice t
         const int sp = ST >= 0 ? (ST + NS - 1) % NS : (t + NS - 1) % NS;   // slice t + NS - 1
         // first K half of slice t; its second half's fragments; weight copies of slice t+NS-1
@@ -818,7 +835,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         if (STEADY) wait_vmcnt<(NS - 2) * PER>();
-        else wait_groups<PER>(min(nk - 1, t + NS - 1) - (t + 1));
+        else wait_groups_x<PER, XL>(min(nk - 1, t + NS - 1) - (t + 1));
         __builtin_amdgcn_s_barrier();
     };
     auto second_half = [&](int t, bool next, auto steady_tag, auto stage_tag) {
@@ -857,13 +874,14 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
 #pragma unroll
     for (int b = 0; b < 3; ++b) w0[b] = rd_w(0, 0, b);
     using rt = std::integral_constant<int, -1>;
-    first_half(0, std::false_type{}, std::integral_constant<int, 0>{});
+    using x0 = std::integral_constant<int, 0>;
+    first_half(0, std::false_type{}, std::integral_constant<int, 0>{}, x0{});
     // steady slices NS at a time, so that each one's LDS stages are constants
     static_assert(NS == 4, "the unrolled steady loop covers four stages");
     auto steady = [&](int t0, auto jt) {
         constexpr int J = decltype(jt)::value;
         second_half(t0 + J, true, std::true_type{}, std::integral_constant<int, J>{});
-        first_half(t0 + J + 1, std::true_type{}, std::integral_constant<int, (J + 1) % NS>{});
+        first_half(t0 + J + 1, std::true_type{}, std::integral_constant<int, (J + 1) % NS>{}, x0{});
     };
     int t = 0;
     for (; t + 2 * NS - 1 < nk; t += NS) {
@@ -874,67 +892,101 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     }
     for (; t + NS < nk; ++t) {
         second_half(t, true, std::true_type{}, rt{});
-        first_half(t + 1, std::true_type{}, rt{});
+        first_half(t + 1, std::true_type{}, rt{}, x0{});
+    }
+    // Every copy is issued now.  The epilogue's scales and bias are loaded here,
+    // three loads in every lane, so that the last slices hide their latency; the
+    // waits below allow those three loads to remain in flight.
+    constexpr int XL = MODE == MODE_BF16 ? 3 : 0;
+    float e_sx = 0.0f, e_sw = 0.0f;
+    uint16_t e_b = 0;
+    if constexpr (MODE == MODE_BF16) {
+        // the thread index rebuilt from the lane count (the compiler keeps
+        // threadIdx spilled across the K loop, and its reload would make it wait
+        // for the copies still in flight)
+        const int lt = wave * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int n = min(n0 + lt % BNW, N - 1);
+        e_sx = ep.a_scale[min(m0 + (lt & (BM - 1)), M - 1) * ep.a_step];
+        e_sw = ep.w_scale[n * ep.w_step];
+        e_b = *(ep.bias ? ep.bias + n : reinterpret_cast<const uint16_t*>(ep.w_scale));
     }
     for (; t + 1 < nk; ++t) {
         second_half(t, true, std::false_type{}, rt{});
-        first_half(t + 1, std::false_type{}, rt{});
+        first_half(t + 1, std::false_type{}, rt{}, std::integral_constant<int, XL>{});
     }
     second_half(nk - 1, false, std::false_type{}, rt{});
 
     if (MODE == MODE_BF16) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();   // the ring is free
-        if (tid < BM) l_sx[tid] = ep.a_scale[min(m0 + tid, M - 1) * ep.a_step];
+        if (tid < BM) l_sx[tid] = e_sx;
         if (tid < BNW) {
-            const int n = min(n0 + tid, N - 1);
-            l_sw[tid] = ep.w_scale[n * ep.w_step];
-            l_b[tid] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
+            l_sw[tid] = e_sw;
+            l_b[tid] = ep.bias ? bf16_to_f32(e_b) : 0.0f;
         }
+        // Four phases, one 32-row fragment j = ph of every wave each: tile rows
+        // wm * 128 + 32 ph + lane % 32 -> staged row wm * 32 + lane % 32 of a
+        // 64-row (48 KB) buffer; the two buffers alternate, so one barrier per
+        // phase keeps every buffer written before it is read and read before it
+        // is rewritten, and a phase's stores overlap the next phase's conversion.
+        // Thread chunk it of a phase: staged row q / 48, 16-byte chunk q % 48
+        // (q = it * 512 + tid); its offsets are the same in every phase.
+        uint32_t o_off[6], l_off[6];
+#pragma unroll
+        for (int it = 0; it < 6; ++it) {
+            const int q = it * NT8 + tid;
+            const int sr = q / 48, ch = q - 48 * (q / 48);
+            const int tr = (sr >> 5) * 128 + (sr & 31);   // tile row in phase 0
+            o_off[it] = (uint32_t)(tr * ep.ldo + ch * 8) * 2u;
+            l_off[it] = (uint32_t)(sr * 768 + (w12_chunk(ch, sr) << 4));
+        }
+        const bool full = m0 + BM <= M && n0 + BNW <= N;
         __syncthreads();
-        uint16_t* out = static_cast<uint16_t*>(ep.out);
-        // phase ph stages fragments j = 2 ph, 2 ph + 1 of every wave: tile rows
-        // wm * 128 + 64 ph + 32 jj + lane % 32 -> staged row wm * 64 + 32 jj + lane % 32
+        char* out = static_cast<char*>(ep.out);
 #pragma unroll
-        for (int ph = 0; ph < 2; ++ph) {
+        for (int ph = 0; ph < 4; ++ph) {
+            int8_t* buf = smem + (ph & 1) * (64 * 768);
+            const float sx = l_sx[wm * 128 + 32 * ph + fr];
+            const int sr = wm * 32 + fr;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                const int j = 2 * ph + jj;
-                const float sx = l_sx[wm * 128 + 32 * j + fr];
-                const int sr = wm * 64 + 32 * jj + fr;
+            for (int i = 0; i < 3; ++i) {
 #pragma unroll
-                for (int i = 0; i < 3; ++i) {
-#pragma unroll
-                    for (int g4 = 0; g4 < 4; ++g4) {
-                        const int c = wn * 96 + 32 * i + 8 * g4 + 4 * fk;
-                        const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
-                        const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
-                        const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
-                                               acc[i][j][4 * g4 + 3]};
-                        const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
-                        *reinterpret_cast<u32x2*>(smem + sr * 768 + (w12_chunk(c >> 3, sr) << 4) + ((c & 7) << 1)) =
-                            pk;
-                    }
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int c = wn * 96 + 32 * i + 8 * g4 + 4 * fk;
+                    const f32x4 sw = *reinterpret_cast<const f32x4*>(l_sw + c);
+                    const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
+                    const int32_t a4[4] = {acc[i][ph][4 * g4], acc[i][ph][4 * g4 + 1], acc[i][ph][4 * g4 + 2],
+                                           acc[i][ph][4 * g4 + 3]};
+                    const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
+                    *reinterpret_cast<u32x2*>(buf + sr * 768 + (w12_chunk(c >> 3, sr) << 4) + ((c & 7) << 1)) = pk;
                 }
             }
             __syncthreads();
-#pragma unroll 4
-            for (int it = 0; it < 12; ++it) {
-                const int q = it * NT8 + tid;
-                const int sr = q / 48, ch = q - 48 * (q / 48);
-                const int m = m0 + (sr >> 6) * 128 + 64 * ph + (sr & 63);
-                const int n = n0 + ch * 8;
-                if (m >= M || n >= N) continue;
-                const u32x4 v = *reinterpret_cast<const u32x4*>(smem + sr * 768 + (w12_chunk(ch, sr) << 4));
-                uint16_t* dst = out + (int64_t)m * ep.ldo + n;
-                if (n + 7 < N) {
-                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
-                } else {
-                    for (int e = 0; e < 8 && n + e < N; ++e)
-                        dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            char* obase = out + ((int64_t)(m0 + 32 * ph) * ep.ldo + n0) * 2;   // the phase's first output row
+            if (full) {
+#pragma unroll
+                for (int it = 0; it < 6; ++it) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(buf + l_off[it]);
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + o_off[it]));
+                }
+            } else {
+#pragma unroll
+                for (int it = 0; it < 6; ++it) {
+                    const int q = it * NT8 + tid;
+                    const int sr2 = q / 48, ch = q - 48 * (q / 48);
+                    const int m = m0 + (sr2 >> 5) * 128 + 32 * ph + (sr2 & 31);
+                    const int n = n0 + ch * 8;
+                    if (m >= M || n >= N) continue;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(buf + l_off[it]);
+                    uint16_t* dst = reinterpret_cast<uint16_t*>(obase + o_off[it]);
+                    if (n + 7 < N) {
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+                    } else {
+                        for (int e = 0; e < 8 && n + e < N; ++e)
+                            dst[e] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+                    }
                 }
             }
-            if (ph == 0) __syncthreads();
         }
     } else {
 #pragma unroll

@@ -128,7 +128,9 @@ def test_gemm_k_limit():
 
 def test_gemm_stride_limit():
     """Operand row strides above QD_MAX_LD_GEMM are refused (a tile's copy
-    offsets, 384 rows x the stride, must fit 32 bits); the limit passes."""
+    offsets, 384 rows x the stride, must fit 32 bits), and so are output row
+    strides above it (store offsets, 160 rows x the stride in bytes); the
+    limit passes."""
     L = qd.lib()
     ldmax = int(re.search(r"#define QD_MAX_LD_GEMM (\d+)", open(HEADER).read()).group(1))
     assert ldmax % 16 == 0 and 384 * ldmax < 2 ** 32
@@ -143,6 +145,9 @@ def test_gemm_stride_limit():
         (L.qd_fp6_gemm_i32, (FAKE, 4, K, big, FAKE, 8, K // 4 * 3, FAKE, 8, STREAM)),
         (L.qd_fp6_gemm_i32, (FAKE, 4, K, K // 4 * 3, FAKE, 8, big, FAKE, 8, STREAM)),
         (L.qd_int8_linear, (FAKE, Q, 4, K, K, FAKE, 8, big, FAKE, NULL, 256, FAKE, 1 << 20, FAKE, 8, STREAM)),
+        (L.qd_int8_scaled_mm, (FAKE, 4, K, K, FAKE, FAKE, 8, K, FAKE, NULL, FAKE, big, STREAM)),
+        (L.qd_int8_gemm_i32, (FAKE, 4, K, K, FAKE, 8, K, FAKE, big, STREAM)),
+        (L.qd_fp6_gemm_i32, (FAKE, 4, K, K // 4 * 3, FAKE, 8, K // 4 * 3, FAKE, big, STREAM)),
     ]
     for fn, args in cases:
         st, msg = _status(fn, *args)
@@ -151,6 +156,7 @@ def test_gemm_stride_limit():
     assert L.qd_int8_gemm_i32(FAKE, 0, K, ldmax, FAKE, 8, ldmax, FAKE, 8, STREAM) == qd.QD_OK
     assert L.qd_fp6_gemm_i32(FAKE, 0, K, ldmax, FAKE, 8, ldmax, FAKE, 8, STREAM) == qd.QD_OK
     assert L.qd_int4_gemm_i32(FAKE, 0, K, K, FAKE, 8, ldmax, FAKE, 8, STREAM) == qd.QD_OK
+    assert L.qd_int8_scaled_mm(FAKE, 0, K, K, FAKE, FAKE, 8, K, FAKE, NULL, FAKE, ldmax, STREAM) == qd.QD_OK
 
 
 def test_linear_validation_and_workspace():

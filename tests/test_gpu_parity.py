@@ -185,6 +185,35 @@ def test_gemm_i32_largest_stride(qd, O, tiles):
     del ab, wb
 
 
+def test_scaled_mm_largest_output_stride(qd, O, tiles):
+    """BF16 output rows QD_MAX_LD_GEMM elements apart (the largest output
+    stride accepted: the store offsets reach 159 rows x 2 x the stride bytes),
+    with whole tiles (first tile row) and a partial one (second tile row):
+    within 1 ulp of the oracle, and nothing written between the rows."""
+    import os
+    import re
+    import torch
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qdiff.h")
+    ld = int(re.search(r"#define QD_MAX_LD_GEMM (\d+)", open(hdr).read()).group(1))
+    M, N, K = 300, 768, 512
+    say(f"scaled_mm output row stride {ld} M={M} N={N} K={K} tiles={tiles}")
+    g = np.random.Generator(np.random.PCG64(73 + tiles))
+    a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    sx = (g.uniform(0.5, 2.0, M) * 2.0 ** -7).astype(np.float32)
+    sw = (g.uniform(0.5, 2.0, N) * 2.0 ** -12).astype(np.float32)
+    from synth import random_bf16
+    b = random_bf16(N, seed=74, scale=0.1)
+    yb = torch.full((M, ld), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    y = yb[:, :N]
+    qd.int8_scaled_mm(to_dev(a), to_dev(sx), to_dev(w), to_dev(sw), to_dev_bf16(b), out=y)
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, b)
+    assert_bf16_within_1ulp(bf16_bits(y), yo, "scaled_mm largest output stride")
+    gap = yb[:, N:N + 4096].view(torch.int16)
+    assert bool((gap == -1).all()), "writes outside the output rows"
+    del yb, y
+
+
 def test_gemm_i32_extremes(qd, O, tiles):
     say(f"gemm i32 extremes tiles={tiles}")
     K = 5376
