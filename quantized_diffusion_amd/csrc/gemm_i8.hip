@@ -688,17 +688,20 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
 // Epilogue: the scales and bias are loaded into registers once the last copy
 // is issued (their latency hides under the last slices) and go to LDS above
 // the staged rows after the K loop; the output tile is staged through the
-// ring in four phases of 64 rows (768 bytes each, 16-byte chunks XOR-swizzled
-// by the row within groups of 16) over two alternating 48 KB buffers, one
-// barrier per phase, so one phase's stores overlap the next one's
-// conversion; whole tiles store through a wave-uniform row base plus fixed
+// ring in four phases of 64 rows (768 bytes each, padded to 784) over two
+// alternating 49 KB buffers, one barrier per phase, so one phase's stores
+// overlap the next one's conversion; without bias it adds -0 (which changes
+// no value) rather than selecting per output; whole tiles store through a wave-uniform row base plus fixed
 // 32-bit lane offsets, with no per-store bounds checks or 64-bit addressing.
 constexpr int BNW = 384;                        // weight rows per wide tile
 constexpr int W12_NS = 4;
 constexpr int W12_STG = (BM + BNW) * BK;        // 40 KB per stage
 constexpr int W12_PER = 5;                      // copies per slice per thread (2 activation + 3 weight)
 
-__device__ __forceinline__ int w12_chunk(int ch, int sr) { return (ch & ~15) | ((ch ^ sr) & 15); }
+// staged output row: 768 bytes of BF16 plus 16 of padding, so that the 32
+// rows written by a wave's lanes at one column start on 8 different 16-byte
+// bank groups (rows 784 bytes apart) while every chunk stays 16-byte aligned
+constexpr int W12_ROW = 784;
 
 template <int MODE>
 __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __restrict__ A, int64_t lda, int64_t a_ss,
@@ -708,9 +711,9 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
     constexpr int STG = W12_STG;
     constexpr int PER = W12_PER;
     constexpr int RING = NS * STG;                 // >= 128 rows x 768 bytes of staged output
-    static_assert(RING >= 128 * 768, "output staging");
+    static_assert(RING >= 2 * 64 * W12_ROW + (BM + 2 * BNW) * 4, "output staging and epilogue operands");
     __shared__ __attribute__((aligned(1024))) int8_t smem[RING];
-    float* l_sx = reinterpret_cast<float*>(smem + 128 * 768);   // after the K loop, above the staged rows
+    float* l_sx = reinterpret_cast<float*>(smem + 2 * 64 * W12_ROW);   // after the K loop, above the staged rows
     float* l_sw = l_sx + 256;
     float* l_b = l_sw + BNW;
 
@@ -922,7 +925,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
         if (tid < BM) l_sx[tid] = e_sx;
         if (tid < BNW) {
             l_sw[tid] = e_sw;
-            l_b[tid] = ep.bias ? bf16_to_f32(e_b) : 0.0f;
+            // without bias, -0: adding it changes no value (unlike +0, which turns -0 into +0)
+            l_b[tid] = ep.bias ? bf16_to_f32(e_b) : -0.0f;
         }
         // Four phases, one 32-row fragment j = ph of every wave each: tile rows
         // wm * 128 + 32 ph + lane % 32 -> staged row wm * 32 + lane % 32 of a
@@ -938,14 +942,14 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
             const int sr = q / 48, ch = q - 48 * (q / 48);
             const int tr = (sr >> 5) * 128 + (sr & 31);   // tile row in phase 0
             o_off[it] = (uint32_t)(tr * ep.ldo + ch * 8) * 2u;
-            l_off[it] = (uint32_t)(sr * 768 + (w12_chunk(ch, sr) << 4));
+            l_off[it] = (uint32_t)(sr * W12_ROW + ch * 16);
         }
         const bool full = m0 + BM <= M && n0 + BNW <= N;
         __syncthreads();
         char* out = static_cast<char*>(ep.out);
 #pragma unroll
         for (int ph = 0; ph < 4; ++ph) {
-            int8_t* buf = smem + (ph & 1) * (64 * 768);
+            int8_t* buf = smem + (ph & 1) * (64 * W12_ROW);
             const float sx = l_sx[wm * 128 + 32 * ph + fr];
             const int sr = wm * 32 + fr;
 #pragma unroll
@@ -957,8 +961,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w12_kernel(const int8_t* __res
                     const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                     const int32_t a4[4] = {acc[i][ph][4 * g4], acc[i][ph][4 * g4 + 1], acc[i][ph][4 * g4 + 2],
                                            acc[i][ph][4 * g4 + 3]};
-                    const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
-                    *reinterpret_cast<u32x2*>(buf + sr * 768 + (w12_chunk(c >> 3, sr) << 4) + ((c & 7) << 1)) = pk;
+                    const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, true);
+                    *reinterpret_cast<u32x2*>(buf + sr * W12_ROW + 2 * c) = pk;
                 }
             }
             __syncthreads();

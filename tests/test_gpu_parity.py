@@ -214,6 +214,32 @@ def test_scaled_mm_largest_output_stride(qd, O, tiles):
     del yb, y
 
 
+def test_scaled_mm_no_bias_tiny_scales(qd, O, tiles):
+    """Without bias, scales so small that the products are FP32 subnormals or
+    round to zero: every output bit for bit as the oracle's, the sign of zero
+    included (a kernel that added +0 for the missing bias would turn every -0
+    into +0)."""
+    say(f"scaled_mm no bias, subnormal products tiles={tiles}")
+    M, N, K = 300, 776, 512
+    g = np.random.Generator(np.random.PCG64(75 + tiles))
+    a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    a[::7] = 0        # zero rows: +0 outputs
+    a[1::5, ::2] = 1  # small sums of either sign
+    # row scales 2^-60, 2^-70, 2^-80 in turn: products from normal through
+    # subnormal (FP32 and BF16) to zero
+    sx = (g.uniform(0.5, 2.0, M) * 2.0 ** (-60.0 - 10.0 * (np.arange(M) % 3))).astype(np.float32)
+    sw = (g.uniform(0.5, 2.0, N) * 2.0 ** -66).astype(np.float32)
+    y = qd.int8_scaled_mm(to_dev(a), to_dev(sx), to_dev(w), to_dev(sw), None)
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, None)
+    got = bf16_bits(y).reshape(-1)
+    want = yo.reshape(-1)
+    assert int((want == 0x8000).sum()) > 1000 and int((want == 0).sum()) > 1000
+    assert int((((want & 0x7F80) == 0) & ((want & 0x7F) != 0)).sum()) > 1000   # BF16 subnormals
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} outputs differ, first at {bad[0]}: {got[bad[0]]:#06x} vs {want[bad[0]]:#06x}"
+
+
 def test_gemm_i32_extremes(qd, O, tiles):
     say(f"gemm i32 extremes tiles={tiles}")
     K = 5376
