@@ -17,7 +17,11 @@
 // with global_load_lds_dwordx4 (no staging registers) through a ring of
 // four 64-byte K slices; copies run three slices ahead and are spread over
 // the slice so that the copy queue never stalls a wave for long.  The output
-// tile is staged through the ring so that every store writes whole rows.
+// tile is staged through the ring so that every store writes whole rows; a
+// whole tile stores through a wave-uniform row base plus fixed 32-bit lane
+// offsets (no per-store bounds checks or 64-bit address arithmetic), and
+// without bias the epilogue adds -0, which changes no value, instead of
+// selecting per output.
 // A wide variant owns 256 x 384 output tiles (twelve accumulators per wave,
 // four 40 KB stages), moving 17 % fewer bytes from L2 into LDS per MAC; the
 // launcher picks the tile by shape (rounds of one workgroup per CU).
@@ -426,7 +430,8 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
             const int c = tid - 256;
             const int n = min(n0 + c, N - 1);
             l_sw[c] = ep.w_scale[n * ep.w_step];
-            l_b[c] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
+            // without bias, -0: adding it changes no value (unlike +0, which turns -0 into +0)
+            l_b[c] = ep.bias ? bf16_to_f32(ep.bias[n]) : -0.0f;
         }
     }
 
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
                     const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                     const int32_t a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                                            acc[i][j][4 * g4 + 3]};
-                    const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, ep.bias != nullptr);
+                    const u32x2 pk = epi_bf16x4(a4, sx, sw, bb, true);
                     const int off = r * 512 + (((c >> 3) ^ (r & 31)) << 4) + ((c & 7) << 1);
                     *reinterpret_cast<u32x2*>(smem + off) = pk;
                 }
@@ -638,6 +643,19 @@ __global__ __launch_bounds__(NT8, 1) void gemm_i8_w8_kernel(const int8_t* __rest
         }
         __syncthreads();
         uint16_t* out = static_cast<uint16_t*>(ep.out);
+        if (m0 + BM <= M && n0 + BN <= N) {
+            // a whole tile: sixteen rows per instruction, a wave-uniform row base
+            // plus a fixed 32-bit lane offset, no bounds checks
+            const int c = tid & 31, rw = tid >> 5;
+            const uint32_t o_lane = (uint32_t)(rw * ep.ldo + c * 8) * 2u;
+            char* obase = reinterpret_cast<char*>(out + (int64_t)m0 * ep.ldo + n0);
+#pragma unroll 4
+            for (int it = 0; it < 16; ++it) {
+                const int r = it * 16 + rw;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)it * 32 * ep.ldo + o_lane));
+            }
+        } else
 #pragma unroll 4
         for (int it = 0; it < 16; ++it) {
             const int q = it * NT8 + tid;
@@ -1116,7 +1134,8 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
         l_sx[tid] = ep.a_scale[min(m0 + tid, M - 1) * ep.a_step];
         const int n = min(n0 + tid, N - 1);
         l_sw[tid] = ep.w_scale[n * ep.w_step];
-        l_b[tid] = ep.bias ? bf16_to_f32(ep.bias[n]) : 0.0f;
+        // without bias, -0: adding it changes no value (unlike +0, which turns -0 into +0)
+        l_b[tid] = ep.bias ? bf16_to_f32(ep.bias[n]) : -0.0f;
     }
 
     // copies: instruction i (0..5) of wave w fills the 16-byte LDS slots
@@ -1281,7 +1300,7 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
                     const f32x4 bb = *reinterpret_cast<const f32x4*>(l_b + c);
                     const float a4[4] = {acc[i][j][4 * g4], acc[i][j][4 * g4 + 1], acc[i][j][4 * g4 + 2],
                                          acc[i][j][4 * g4 + 3]};
-                    const u32x2 pk = epi_bf16x4_f(a4, sx, sw, bb, ep.bias != nullptr);
+                    const u32x2 pk = epi_bf16x4_f(a4, sx, sw, bb, true);
                     const int off = r * 512 + (((c >> 3) ^ (r & 31)) << 4) + ((c & 7) << 1);
                     *reinterpret_cast<u32x2*>(smem + off) = pk;
                 }
@@ -1289,6 +1308,19 @@ __global__ __launch_bounds__(NT4, 1) void gemm_f6_w4_kernel(const uint8_t* __res
         }
         __syncthreads();
         uint16_t* out = static_cast<uint16_t*>(ep.out);
+        if (m0 + BM <= M && n0 + BN <= N) {
+            // a whole tile: eight rows per instruction, a wave-uniform row base
+            // plus a fixed 32-bit lane offset, no bounds checks
+            const int c = tid & 31, rw = tid >> 5;
+            const uint32_t o_lane = (uint32_t)(rw * ep.ldo + c * 8) * 2u;
+            char* obase = reinterpret_cast<char*>(out + (int64_t)m0 * ep.ldo + n0);
+#pragma unroll 4
+            for (int it = 0; it < 32; ++it) {
+                const int r = it * 8 + rw;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * 512 + ((c ^ (r & 31)) << 4));
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + (int64_t)it * 16 * ep.ldo + o_lane));
+            }
+        } else
 #pragma unroll 4
         for (int it = 0; it < 32; ++it) {
             const int q = it * NT4 + tid;
