@@ -20,12 +20,15 @@ Prints ONE JSON line.  Besides the headline it carries:
                   bandwidth (read, copy, and the quantizer's 2:1 mix);
   kernels         both kernels' average durations, TOP/s or GB/s and fractions;
   per_config      the other large workloads (odd M, wide MLP, W4A4 on the FP6
-                  path) measured in the same run: ms, TOP/s, fractions and a
-                  sampled comparison with the oracle;
+                  path) measured in the same run: ms, TOP/s, fractions, and
+                  in their own cpu_baseline leg a sampled comparison with the
+                  oracle;
   cpu_baseline    the plain C oracle timed on the host cores over a bounded
                   sample of the same workload (the leading rows), rotate+quant
                   and GEMM+epilogue timed separately, and the GPU output of
                   those rows compared with it.
+The oracle is used only by the cpu_baseline legs (outside every timed
+region; --no-cpu-baseline skips them all).
 
 Usage: python bench.py [--gpus 1] [--steps 30] [--warmup 30] [--workload 3]
 """
@@ -449,9 +452,10 @@ def measure_config(cid: int, args, torch, O):
            "separate_launch_output_identical": same, "clock": clk}
     if w.cid in PAGE_MS:
         out["context_page_ms"] = PAGE_MS[w.cid]
-    if O is not None:
-        log(f"[bench] {w.name}: sampled outputs against the oracle")
-        out["sampled_parity"] = run.sampled_parity(O)
+    if O is not None:   # the cpu_baseline leg of this line: its oracle checks sampled outputs
+        log(f"[bench] {w.name}: cpu baseline leg, sampled outputs against the oracle")
+        out["cpu_baseline"] = {"kind": "oracle", "sample": "4000 random outputs and the whole last row",
+                               "sampled_parity": run.sampled_parity(O)}
     del run
     torch.cuda.empty_cache()
     return out
