@@ -147,3 +147,48 @@ def test_w4a4_full_size(qd, O):
     aq = ws[: M * K].view(M, K).view(torch.int8)
     acc = qd.int4_gemm_i32(aq, wp)
     assert np.array_equal(host(acc[ri, ci]), acco)
+
+
+def _tiny_case(seed):
+    """INT4 codes with row scales 2^-60, 2^-70, 2^-80 in turn and column
+    scales near 2^-66: products from normal through subnormal to zero, both
+    signs (zero rows and rows of small sums included), no bias."""
+    M, N, K = 300, 512, 512
+    g = np.random.Generator(np.random.PCG64(seed))
+    a = g.integers(-7, 8, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-7, 8, (N, K), dtype=np.int64).astype(np.int8)
+    a[::7] = 0
+    a[1::5, ::2] = 1
+    sx = (g.uniform(0.5, 2.0, M) * 2.0 ** (-60.0 - 10.0 * (np.arange(M) % 3))).astype(np.float32)
+    sw = (g.uniform(0.5, 2.0, N) * 2.0 ** -66).astype(np.float32)
+    return a, w, sx, sw
+
+
+def _strided_out(M, N, pad):
+    import torch
+    buf = torch.full((M, N + pad), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    return buf, buf[:, :N]
+
+
+def _check_exact(y, buf, N, want, what):
+    import torch
+    got = bf16_bits(y).reshape(-1)
+    want = want.reshape(-1)
+    assert int((want == 0x8000).sum()) > 1000 and int((want == 0).sum()) > 1000
+    assert int((((want & 0x7F80) == 0) & ((want & 0x7F) != 0)).sum()) > 1000
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{what}: {bad.size} outputs differ, first at {bad[0]}: {got[bad[0]]:#06x} vs {want[bad[0]]:#06x}"
+    assert bool((buf[:, N:].view(torch.int16) == -1).all()), f"{what}: writes outside the output rows"
+
+
+def test_int4_scaled_mm_strided_out_no_bias_tiny_scales(qd, O):
+    """Output rows 776 elements apart (whole tiles in the first tile row, a
+    partial one after), no bias, subnormal and signed-zero products: every
+    output bit for bit as the oracle's, nothing written between the rows."""
+    say("int4 scaled_mm strided output, no bias, subnormal products")
+    a, w, sx, sw = _tiny_case(90)
+    M, K = a.shape
+    N = w.shape[0]
+    buf, y = _strided_out(M, N, 264)
+    qd.int4_scaled_mm(to_dev(a), to_dev(sx), to_dev(O.pack_int4(w)), to_dev(sw), None, out=y)
+    _check_exact(y, buf, N, O.epilogue(O.gemm_i32(a, w), sx, sw, None), "int4 scaled_mm")
