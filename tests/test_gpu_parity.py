@@ -240,6 +240,27 @@ def test_scaled_mm_no_bias_tiny_scales(qd, O, tiles):
     assert bad.size == 0, f"{bad.size} outputs differ, first at {bad[0]}: {got[bad[0]]:#06x} vs {want[bad[0]]:#06x}"
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320])
+def test_scaled_mm_short_k(qd, O, tiles, K):
+    """One to five 64-byte K slices (fewer than the LDS ring holds, so the
+    eight-wave kernels never reach their steady loop and the epilogue operand
+    loads are issued right after the prologue's copies): BF16 outputs of
+    whole and partial tiles within 1 ulp of the oracle."""
+    say(f"scaled_mm short K={K} tiles={tiles}")
+    from synth import random_bf16
+    M, N = 300, 776
+    g = np.random.Generator(np.random.PCG64(76 + K + tiles))
+    a = g.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    w = g.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    sx = (g.uniform(0.5, 2.0, M) * 2.0 ** -7).astype(np.float32)
+    sw = (g.uniform(0.5, 2.0, N) * 2.0 ** -12).astype(np.float32)
+    b = random_bf16(N, seed=77 + K, scale=0.1)
+    y = qd.int8_scaled_mm(to_dev(a), to_dev(sx), to_dev(w), to_dev(sw), to_dev_bf16(b))
+    yo = O.epilogue(O.gemm_i32(a, w), sx, sw, b)
+    n = assert_bf16_within_1ulp(bf16_bits(y), yo, f"scaled_mm K={K}")
+    say(f"  {n} of {yo.size} outputs differ from the oracle (allowed: 1 ulp)")
+
+
 def test_gemm_i32_extremes(qd, O, tiles):
     say(f"gemm i32 extremes tiles={tiles}")
     K = 5376
