@@ -171,6 +171,7 @@ size_t qd_int8_linear_workspace_size(int64_t M, int64_t K);
  *              bytes, 256-byte aligned; holds the activation codes and row
  *              scales between the two launches.
  *   y          [M, N] BF16, stride ldy.
+ * ldw and ldy at most QD_MAX_LD_GEMM (QD_EUNSUPPORTED above).
  * Exactly two kernels are enqueued: the (rotating) quantizer, then the INT8
  * GEMM with the fused dequantizing epilogue.
  */
