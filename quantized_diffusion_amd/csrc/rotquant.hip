@@ -62,6 +62,8 @@
 #include "qd_act.h"
 
 namespace qd {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace {
 
 template <class In> struct In16 { static constexpr int value = 0; };
@@ -189,7 +191,9 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
 // fields straight into the FP6 operand format (q is then the FP6 matrix,
 // ldq its row stride in bytes, 3K/4 bytes per row): each 8-code chunk is
 // 48 bits, three 2-byte pieces placed in the block's 192-byte image at their
-// head / tail positions.
+// head / tail positions.  The fields of four chunks come from one gfx950
+// FP32 -> FP6 conversion (v_cvt_scalef32_2xpk16_fp6_f32, unit scale) of the
+// codes as floats, which are exact integers of [-7, 7].
 template <class In, bool ROT, int QMAX, bool STAGE, int ACT, bool F6 = false, bool SL = false>
 __global__ __launch_bounds__((kMaxThreads<ACT, In16<In>::value>::value)) void rotquant_kernel(const uint8_t* __restrict__ x,
                                                         int64_t ldx_bytes, int M, int K, int nb,
@@ -400,6 +404,11 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
     const float r = 1.0f / s;
     const float trs = tau * (ROT ? r * 0.0625f : r);
     int8_t* dst = q + (int64_t)row * ldq + (int64_t)blk * 256;
+    // F6: the codes of four chunks as floats (exact integers of [-7, 7], +0
+    // for zero), converted to E2M3 fields together by the matrix-format
+    // conversion; its two 16-value operands interleave (field 2j from the
+    // first, 2j + 1 from the second), so code k of the 32 goes to operand k % 2
+    f32x16 f6a, f6b;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int c = i * 4 + ql;
@@ -407,6 +416,7 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
         // Fast codes for the chunk; one test of the largest |d| decides
         // whether any element of the chunk needs the exact path.
         uint32_t code[E];
+        float fcode[E];   // the same codes as floats (F6 only; n is t - kMagic exactly, +0 for zero)
         float dmax = 0.0f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -416,6 +426,7 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
             const float d = __builtin_fmaf(w, trs, -n);
             dmax = __builtin_fmaxf(dmax, __builtin_fabsf(d));
             code[e] = f_bits(t);
+            fcode[e] = n;
         }
         if (__builtin_expect(mode != 1 || dmax >= kFastMargin, 0)) {
 #pragma unroll
@@ -424,25 +435,39 @@ __device__ __forceinline__ void quantize_store(const float* v, uint32_t amax_bit
                 const float t = __builtin_fmaf(w, trs, kMagic);
                 const float n = t - kMagic;
                 const float d = __builtin_fmaf(w, trs, -n);
-                if (mode != 1 || __builtin_fabsf(d) >= kFastMargin)
+                if (mode != 1 || __builtin_fabsf(d) >= kFastMargin) {
                     code[e] = mode == 0 ? 0u : exact_code<ROT, QMAX>(w, tau, s);
+                    fcode[e] = (float)(int)(int8_t)(uint8_t)code[e];
+                }
             }
         }
         if (F6 && E == 8) {
-            // 8 codes -> 48 bits of E2M3 fields; piece p = (c % 8) / 4 of K block
-            // c / 8, piece bytes 6 (c % 4) .. +5, each 2-byte part at its head
-            // (bytes < 16) or tail position
-            const uint32_t g0 = pack6x4(e2m3x4(pack4(code[0], code[1], code[2], code[3])));
-            const uint32_t g1 = pack6x4(e2m3x4(pack4(code[4 % E], code[5 % E], code[6 % E], code[7 % E])));
-            const uint32_t lo = g0 | (g1 << 24), hi = g1 >> 8;
-            const uint32_t part[3] = {lo & 0xFFFFu, lo >> 16, hi & 0xFFFFu};
-            const int kb = c >> 3, p = (c >> 2) & 1, o = 6 * (c & 3);
+            static_assert(!F6 || (ROT && QMAX == 7), "FP6 codes are rotated INT4 codes");
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float fc = fcode[e];
+                const int k = 8 * (i & 3) + e;
+                if (k % 2 == 0) f6a[k / 2] = fc;
+                else f6b[k / 2] = fc;
+            }
+            if ((i & 3) != 3) continue;
+            const auto f6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(f6a, f6b, 1.0f);
             const int swp = ((row >> 3) ^ (row >> 4)) & 1;
 #pragma unroll
-            for (int h = 0; h < 3; ++h) {
-                const int x = o + 2 * h;
-                const int pos = kb * 48 + (x < 16 ? 16 * p + x : 32 + 8 * (p ^ swp) + (x - 16));
-                *reinterpret_cast<uint16_t*>(img + pos) = (uint16_t)part[h];
+            for (int j = 0; j < 4; ++j) {
+                // chunk i - 3 + j: 48 bits at bit 48 j of the conversion; piece
+                // p = (c % 8) / 4 of K block c / 8, piece bytes 6 (c % 4) .. +5,
+                // each 2-byte part at its head (bytes < 16) or tail position
+                const int cj = (i - 3 + j) * 4 + ql;
+                const int kb = cj >> 3, p = (cj >> 2) & 1, o = 6 * (cj & 3);
+#pragma unroll
+                for (int h = 0; h < 3; ++h) {
+                    const int bit = 48 * j + 16 * h;
+                    const uint16_t part = (uint16_t)((uint32_t)f6[bit / 32] >> (bit % 32));
+                    const int x = o + 2 * h;
+                    const int pos = kb * 48 + (x < 16 ? 16 * p + x : 32 + 8 * (p ^ swp) + (x - 16));
+                    *reinterpret_cast<uint16_t*>(img + pos) = part;
+                }
             }
             continue;
         }
@@ -497,12 +522,13 @@ hipError_t launch_typed(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t
     if (best_threads == 0) { R = 1; best_threads = (4 * nb + 63) / 64 * 64; }
     if (R > M) { R = (int)M; best_threads = (4 * R * nb + 63) / 64 * 64; }
     if (best_threads > MAXT) return hipErrorInvalidValue;   // rows longer than the caller's checks allow
-    if (F6)
+    if constexpr (F6)
         return launch_staged<In, ROT, QMAX, true, ACT, true, SL>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
-    if (ROT)
+    else if constexpr (ROT)
         return launch_staged<In, ROT, QMAX, true, ACT, false, SL>(x, M, K, ldx, q, ldq, scale, stream, R,
                                                                  best_threads);
-    return launch_staged<In, ROT, QMAX, false, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
+    else
+        return launch_staged<In, ROT, QMAX, false, ACT>(x, M, K, ldx, q, ldq, scale, stream, R, best_threads);
 }
 
 }  // namespace
