@@ -167,6 +167,30 @@ def test_attention_large_sampled(qd, O):
     say(f"  max |err| / bound = {float((err / bound).max()):.3f}")
 
 
+def test_attention_d64_long_sampled(qd, O):
+    """D = 64 over long sequences (4 heads x 8192 queries x 8192 keys): rows
+    of every head (first and last query, both sides of a workgroup's
+    384-query boundary, random ones) against the oracle within the bound."""
+    import torch
+    BH, L, D = 4, 8192, 64
+    say(f"int8_attention {BH}x{L}x{L}x{D}, sampled rows")
+    dev, h = _inputs((BH, L, D), (BH, L, D), seed=47)
+    q, k, v = dev
+    out = qd.int8_attention(q, k, v)
+    g = np.random.Generator(np.random.PCG64(48))
+    rows = np.unique(np.concatenate([g.integers(0, L, 24), [0, 383, 384, L - 1]]))
+    qc, sq = O.quantize_tokens(h[0], "bf16")
+    kc, sk = O.quantize_tokens(h[1], "bf16")
+    vc, sv = O.quantize_tokens(h[2], "bf16")
+    want = O.attention_codes(qc[:, rows], sq[:, rows], kc, sk, vc, sv)
+    P = O.attention_probs(qc[:, rows], sq[:, rows], kc, sk)
+    got = (_bits_of(out[:, torch.from_numpy(rows).cuda()]).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = attention_bound(want, P, qc[:, rows], sq[:, rows], kc, sk, vc, sv, 1.0 / np.sqrt(D))
+    err = np.abs(got - want)
+    assert np.all(err <= bound), f"{int((err > bound).sum())} sampled outputs outside the bound"
+    say(f"  max |err| / bound = {float((err / bound).max()):.3f}")
+
+
 def test_attention_full_size_sampled(qd, O):
     """The benchmark's workload, 40 heads x 16384 tokens x 128 (BF16 N(0, 1)
     inputs drawn as the benchmark draws them), in its launch configuration:
